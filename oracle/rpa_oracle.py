@@ -1,0 +1,180 @@
+"""Plain fp64 CPU oracle for ragged paged attention (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The GPU library never calls it, and it
+shares no code with the GPU library: it is the plain definition written out,
+slow on purpose, so that a reader can check it against the pages by eye.
+
+What it computes (the pages' method, read plainly):
+
+* The step's query tokens of all sequences sit in one flattened array; each
+  sequence's slice is given by cumulative query lengths, and its true KV length
+  by per-sequence metadata ("TPU Deep Dive", chapter 8, "Continuous batching
+  with static shapes": flattened token batch + per-sequence metadata; true
+  lengths handled inside the kernel).
+* A sequence's keys and values live in fixed-size pages found through its page
+  table ("Pallas Kernel: vLLM on TPU ...", environment section and S3: KV held
+  in 128-token blocks).  Un-paging is a pure gather: key t of sequence s is slot
+  t mod B of page ``page_table[s][t div B]``.
+* Query tokens are the *last* q_len positions of the sequence: row r sits at
+  absolute position p = kv_len - q_len + r (chunked prefill on top of earlier
+  context, same page, environment section).
+* Several query heads share one KV head ("TPU Deep Dive", chapter 4, "Shape
+  on TPU": KV heads; "Pallas Kernel ...", S3: 8 query heads share 1 KV head).
+  Reading: contiguous groups, query head h uses KV head h // G, G = Hq / Hkv.
+* Causal attention, optionally through a sliding window: in a sliding-window
+  layer a key is wanted by the W queries that follow it ("Chasing speed of
+  light on TPU v6e", section Attention).  Reading: with W > 0, query position p
+  sees keys j with p - W + 1 <= j <= p (W keys counting itself); W = 0 means
+  full causal, j <= p.
+* Each (query, key) pair costs a q.k dot product and a p.v product per query
+  head -- two matmuls per head -- and the normalised scores never leave the
+  chip ("Chasing speed of light on TPU v6e", footnote 5 of section Attention).
+  Written out: out = softmax(scale * Q K^T + mask) V per sequence and head, with
+  mask = 0 on visible pairs and -inf elsewhere.
+
+Everything is done in float64 on values converted exactly from the bf16 inputs.
+Nothing here is blocked, fused or reordered: rows are processed in groups of at
+most ``ROW_BLOCK`` only to bound memory, which is exact because rows of a
+softmax are independent.
+
+Every function below is pinned by ``tests/test_oracle.py`` (brute force, a
+library routine, closed forms and invariants); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+ROW_BLOCK = 1024
+
+
+def as_f64(x) -> np.ndarray:
+    """Exact conversion of a torch tensor (any float dtype incl. bf16) or array to float64."""
+    if hasattr(x, "detach"):
+        import torch  # CPU only; plain dtype conversion
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def as_i64(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        return x.detach().to("cpu").numpy().astype(np.int64)
+    return np.asarray(x, dtype=np.int64)
+
+
+def unpage(pages: np.ndarray, table_row: np.ndarray, kv_len: int, page_size: int) -> np.ndarray:
+    """Gather the first ``kv_len`` token rows of one sequence from the page pool.
+
+    pages: [P, B, Hkv, D]; table_row: the sequence's page-table row.
+    Returns [kv_len, Hkv, D]: row t = pages[table_row[t // B], t % B].
+    """
+    out = np.empty((kv_len,) + pages.shape[2:], dtype=np.float64)
+    for t in range(kv_len):
+        out[t] = pages[int(table_row[t // page_size]), t % page_size]
+    return out
+
+
+def visible(q_len: int, kv_len: int, window: int, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Boolean [len(rows), kv_len]: True where query row r may attend to key j.
+
+    Row r is at position p = kv_len - q_len + r; key j is visible iff j <= p and,
+    for a window W > 0, j >= p - W + 1.
+    """
+    if rows is None:
+        rows = np.arange(q_len)
+    p = (kv_len - q_len + np.asarray(rows, dtype=np.int64))[:, None]
+    j = np.arange(kv_len, dtype=np.int64)[None, :]
+    ok = j <= p
+    if window > 0:
+        ok &= j >= p - window + 1
+    return ok
+
+
+def softmax_rows(scores: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """Row softmax of ``scores`` where masked entries count as -inf."""
+    s = np.where(mask, scores, -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _check_metadata(cu: np.ndarray, kv: np.ndarray, num_q_heads: int, num_kv_heads: int,
+                    window: int) -> None:
+    if num_q_heads % num_kv_heads:
+        raise ValueError("query heads must be a multiple of KV heads")
+    if window < 0:
+        raise ValueError("window must be >= 0")
+    if cu[0] != 0 or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_q_lens must start at 0 and be non-decreasing")
+    if np.any(np.diff(cu) > kv):
+        raise ValueError("q_len may not exceed kv_len")
+
+
+def sequence_probs(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, window: int,
+                   scale: float, seq: int, head: int) -> np.ndarray:
+    """Debug hook: the [q_len, kv_len] probability matrix P of one sequence and query head."""
+    qf, kf = as_f64(q), as_f64(k_pages)
+    pt, cu, kv = as_i64(page_table), as_i64(cu_q_lens), as_i64(kv_lens)
+    hq, hkv = qf.shape[1], kf.shape[2]
+    g = head // (hq // hkv)
+    q_len, kv_len = int(cu[seq + 1] - cu[seq]), int(kv[seq])
+    k_s = unpage(kf, pt[seq], kv_len, kf.shape[1])
+    q_h = qf[cu[seq]:cu[seq + 1], head, :]
+    s = scale * (q_h @ k_s[:, g, :].T)
+    return softmax_rows(s, visible(q_len, kv_len, window))
+
+
+def forward_rows(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, window: int,
+                 scale: float, token_rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Oracle output for the selected flattened token rows (all of them if None).
+
+    Returns float64 [len(token_rows), Hq, D] in the order of ``token_rows``.
+    """
+    qf = as_f64(q)
+    kf = as_f64(k_pages)
+    vf = as_f64(v_pages)
+    pt = as_i64(page_table)
+    cu = as_i64(cu_q_lens)
+    kv = as_i64(kv_lens)
+    t_total, hq, d = qf.shape
+    hkv, b = kf.shape[2], kf.shape[1]
+    _check_metadata(cu, kv, hq, hkv, window)
+    group = hq // hkv
+    if token_rows is None:
+        token_rows = np.arange(t_total)
+    token_rows = np.asarray(list(token_rows), dtype=np.int64)
+    out = np.full((len(token_rows), hq, d), np.nan, dtype=np.float64)
+    # which sequence owns each requested row
+    owner = np.searchsorted(cu, token_rows, side="right") - 1
+    for s in np.unique(owner):
+        s = int(s)
+        sel = np.nonzero(owner == s)[0]
+        local = token_rows[sel] - cu[s]
+        q_len, kv_len = int(cu[s + 1] - cu[s]), int(kv[s])
+        k_s = unpage(kf, pt[s], kv_len, b)
+        v_s = unpage(vf, pt[s], kv_len, b)
+        for lo in range(0, len(sel), ROW_BLOCK):
+            blk = slice(lo, lo + ROW_BLOCK)
+            rows = local[blk]
+            mask = visible(q_len, kv_len, window, rows)
+            for h in range(hq):
+                g = h // group
+                q_h = qf[token_rows[sel[blk]], h, :]
+                scores = scale * (q_h @ k_s[:, g, :].T)
+                p = softmax_rows(scores, mask)
+                out[sel[blk], h, :] = p @ v_s[:, g, :]
+    return out
+
+
+def forward(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, window: int,
+            scale: float) -> np.ndarray:
+    """Full oracle output, float64 [T, Hq, D]."""
+    return forward_rows(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, window, scale)
+
+
+def forward_inputs(inp, token_rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Convenience wrapper over an ``rpa_workloads.Inputs`` bundle."""
+    return forward_rows(inp.q, inp.k_pages, inp.v_pages, inp.page_table, inp.cu_q_lens,
+                        inp.kv_lens, inp.window, inp.scale, token_rows)

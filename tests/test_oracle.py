@@ -1,0 +1,452 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+* brute force: scalar Python loops with ``math.exp`` on tiny inputs;
+* a library routine: ``torch.nn.functional.scaled_dot_product_attention`` in
+  float64 on CPU after an independent un-paging;
+* a hand-worked example with exact rational answers (``tests/golden``);
+* closed forms (window 1 returns the own value, constant values, zero keys);
+* invariants (rows sum to 1, paging is a pure gather, window >= kv_len is full
+  causal, decode equals the last prefill row, a chunk equals the tail of the
+  full prefill, GQA equals MHA with repeated KV heads, batch order).
+
+The mutation tests at the bottom plant plausible mistakes *in the oracle* (on
+the CPU) and check that at least one pin catches each of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.rpa_oracle as ora
+import rpa_workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# independent helpers (no oracle code)
+# ---------------------------------------------------------------------------
+
+def brute_force(q, kp, vp, pt, cu, kv, window, scale):
+    """Scalar loops, straight from the definition, one output element at a time."""
+    hq, d = q.shape[1], q.shape[2]
+    b, hkv = kp.shape[1], kp.shape[2]
+    q = q.to(torch.float64).tolist()
+    kp = kp.to(torch.float64).tolist()
+    vp = vp.to(torch.float64).tolist()
+    pt = pt.tolist()
+    cu = [int(x) for x in cu]
+    kv = [int(x) for x in kv]
+    group = hq // hkv
+    out = [[[0.0] * d for _ in range(hq)] for _ in range(cu[-1])]
+    for s in range(len(kv)):
+        q_len = cu[s + 1] - cu[s]
+        for r in range(q_len):
+            pos = kv[s] - q_len + r
+            for h in range(hq):
+                g = h // group
+                keys = []
+                for j in range(kv[s]):
+                    if j > pos:
+                        continue
+                    if window > 0 and j < pos - window + 1:
+                        continue
+                    page, slot = pt[s][j // b], j % b
+                    dot = 0.0
+                    for e in range(d):
+                        dot += q[cu[s] + r][h][e] * kp[page][slot][g][e]
+                    keys.append((j, scale * dot))
+                mx = max(sc for _, sc in keys)
+                den = sum(math.exp(sc - mx) for _, sc in keys)
+                for e in range(d):
+                    acc = 0.0
+                    for j, sc in keys:
+                        page, slot = pt[s][j // b], j % b
+                        acc += math.exp(sc - mx) / den * vp[page][slot][g][e]
+                    out[cu[s] + r][h][e] = acc
+    return np.array(out, dtype=np.float64).reshape(cu[-1], hq, d)
+
+
+def sdpa_reference(inp):
+    """torch SDPA (float64, CPU) on K/V gathered with flat index arithmetic."""
+    q = inp.q.to(torch.float64)
+    kp = inp.k_pages.to(torch.float64)
+    vp = inp.v_pages.to(torch.float64)
+    n_pages, b, hkv, d = kp.shape
+    flat_k = kp.reshape(n_pages * b, hkv, d)
+    flat_v = vp.reshape(n_pages * b, hkv, d)
+    hq = q.shape[1]
+    group = hq // hkv
+    out = torch.zeros(q.shape, dtype=torch.float64)
+    cu = inp.cu_q_lens.tolist()
+    kvl = inp.kv_lens.tolist()
+    for s in range(len(kvl)):
+        q_len, kv_len = cu[s + 1] - cu[s], kvl[s]
+        if q_len == 0:
+            continue
+        t = torch.arange(kv_len)
+        idx = inp.page_table[s].long()[t // b] * b + t % b
+        k = flat_k[idx].repeat_interleave(group, dim=1).permute(1, 0, 2).contiguous()
+        v = flat_v[idx].repeat_interleave(group, dim=1).permute(1, 0, 2).contiguous()
+        qs = q[cu[s]:cu[s + 1]].permute(1, 0, 2).contiguous()
+        pos = torch.arange(q_len)[:, None] + (kv_len - q_len)
+        j = torch.arange(kv_len)[None, :]
+        allow = j <= pos
+        if inp.window > 0:
+            allow = allow & (j > pos - inp.window)
+        o = torch.nn.functional.scaled_dot_product_attention(qs, k, v, attn_mask=allow,
+                                                             scale=inp.scale)
+        out[cu[s]:cu[s + 1]] = o.permute(1, 0, 2)
+    return out.numpy()
+
+
+def run_oracle(inp, window=None, scale=None):
+    return ora.forward(inp.q, inp.k_pages, inp.v_pages, inp.page_table, inp.cu_q_lens,
+                       inp.kv_lens, inp.window if window is None else window,
+                       inp.scale if scale is None else scale)
+
+
+def small_cases():
+    cases = []
+    rng = np.random.default_rng(5)
+    for hkv in (1, 2, 4):
+        for b in (1, 2, 3):
+            for window in (0, 1, 2, 3, 100):
+                n = int(rng.integers(1, 4))
+                seqs = []
+                for _ in range(n):
+                    kv = int(rng.integers(1, 10))
+                    q = int(rng.integers(0, min(kv, 5) + 1))
+                    seqs.append((q, kv))
+                cases.append(wl.custom(seqs, 4, hkv, 4, b, window, seed=int(rng.integers(1 << 30))))
+    return cases
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", small_cases(), ids=lambda w: f"hkv{w.num_kv_heads}_b{w.page_size}_w{w.window}_{len(w.seqs)}seq")
+def test_brute_force(w):
+    inp = wl.make_inputs(w, poison=True)
+    got = run_oracle(inp)
+    ref = brute_force(inp.q, inp.k_pages, inp.v_pages, inp.page_table, inp.cu_q_lens,
+                      inp.kv_lens, inp.window, inp.scale)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("w", [
+    wl.tiny(),
+    wl.custom([(5, 40), (0, 7), (33, 33), (1, 90)], 8, 2, 32, 16, 0, seed=11),
+    wl.custom([(5, 40), (0, 7), (33, 33), (1, 90)], 8, 2, 32, 16, 17, seed=12),
+    wl.custom([(64, 200)], 4, 4, 16, 8, 50, seed=13),
+], ids=["tiny", "gqa4_causal", "gqa4_window17", "mha_window50"])
+def test_library_sdpa(w):
+    inp = wl.make_inputs(w, poison=True)
+    got = run_oracle(inp)
+    ref = sdpa_reference(inp)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def _golden_inputs(fix):
+    b, hkv, d = fix["page_size"], fix["num_kv_heads"], fix["head_dim"]
+    pt = np.array(fix["page_table"], dtype=np.int64)
+    n_pages = int(pt.max()) + 1
+    kp = np.full((n_pages, b, hkv, d), np.nan)
+    vp = np.full((n_pages, b, hkv, d), np.nan)
+    for s, (weights, values) in enumerate(zip(fix["key_weights"], fix["values"])):
+        for t, (a, v) in enumerate(zip(weights, values)):
+            kp[pt[s][t // b], t % b, 0] = [math.log(a), 0.0]
+            vp[pt[s][t // b], t % b, 0] = v
+    return (np.array(fix["q"], dtype=np.float64), kp, vp, pt,
+            np.array(fix["cu_q_lens"]), np.array(fix["kv_lens"]))
+
+
+def test_golden_hand_worked():
+    with open(os.path.join(GOLDEN, "hand_worked.json")) as f:
+        fix = json.load(f)
+    q, kp, vp, pt, cu, kv = _golden_inputs(fix)
+    for window, expect in fix["expected"].items():
+        got = ora.forward(q, kp, vp, pt, cu, kv, int(window), fix["scale"])
+        want = np.array([[[float(Fraction(x)) for x in row] for row in tok] for tok in expect])
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-14)
+
+
+def test_window_one_returns_own_value():
+    w = wl.custom([(7, 20), (1, 5), (3, 3)], 4, 2, 8, 4, 1, seed=3)
+    inp = wl.make_inputs(w, poison=True)
+    got = run_oracle(inp)
+    cu, kv = inp.cu_q_lens.tolist(), inp.kv_lens.tolist()
+    vf = inp.v_pages.to(torch.float64).numpy()
+    for s in range(len(kv)):
+        for r in range(cu[s + 1] - cu[s]):
+            pos = kv[s] - (cu[s + 1] - cu[s]) + r
+            page, slot = int(inp.page_table[s, pos // 4]), pos % 4
+            for h in range(4):
+                assert np.array_equal(got[cu[s] + r, h], vf[page, slot, h // 2])
+
+
+def test_single_token_sequence_returns_v0():
+    w = wl.custom([(1, 1)] * 3, 8, 1, 16, 16, 0, seed=4)
+    inp = wl.make_inputs(w, poison=True)
+    got = run_oracle(inp)
+    vf = inp.v_pages.to(torch.float64).numpy()
+    for s in range(3):
+        page = int(inp.page_table[s, 0])
+        for h in range(8):
+            assert np.array_equal(got[s, h], vf[page, 0, 0])
+
+
+@pytest.mark.parametrize("window", [0, 5])
+def test_zero_scores_give_mean_of_visible_values(window):
+    w = wl.custom([(6, 15), (1, 9)], 4, 1, 8, 4, window, seed=5)
+    inp = wl.make_inputs(w, poison=True)
+    zero_k = wl.Inputs(w, inp.q, torch.zeros_like(inp.k_pages), inp.v_pages, inp.page_table,
+                       inp.cu_q_lens, inp.kv_lens, inp.trap_page, window, inp.scale)
+    got_k0 = run_oracle(zero_k)
+    got_s0 = run_oracle(inp, scale=0.0)
+    cu, kv = inp.cu_q_lens.tolist(), inp.kv_lens.tolist()
+    vf = inp.v_pages.to(torch.float64).numpy()
+    for s in range(2):
+        q_len = cu[s + 1] - cu[s]
+        for r in range(q_len):
+            pos = kv[s] - q_len + r
+            lo = max(0, pos - window + 1) if window else 0
+            vals = [vf[int(inp.page_table[s, j // 4]), j % 4, 0] for j in range(lo, pos + 1)]
+            mean = np.mean(vals, axis=0)
+            for h in range(4):
+                np.testing.assert_allclose(got_k0[cu[s] + r, h], mean, rtol=0, atol=1e-13)
+                np.testing.assert_allclose(got_s0[cu[s] + r, h], mean, rtol=0, atol=1e-13)
+
+
+def test_constant_values_give_constant():
+    w = wl.custom([(9, 30), (2, 2)], 4, 2, 8, 8, 0, seed=6)
+    inp = wl.make_inputs(w)
+    v = torch.full_like(inp.v_pages, 0.375)
+    c = wl.Inputs(w, inp.q, inp.k_pages, v, inp.page_table, inp.cu_q_lens, inp.kv_lens,
+                  inp.trap_page, 0, inp.scale)
+    got = run_oracle(c)
+    np.testing.assert_allclose(got, 0.375, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [0, 4])
+def test_probability_rows_sum_to_one(window):
+    w = wl.custom([(12, 40)], 4, 2, 16, 8, window, seed=7)
+    inp = wl.make_inputs(w, poison=True)
+    for h in range(4):
+        p = ora.sequence_probs(inp.q, inp.k_pages, inp.v_pages, inp.page_table,
+                               inp.cu_q_lens, inp.kv_lens, window, inp.scale, 0, h)
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        vis = ora.visible(12, 40, window)
+        assert np.all(p[~vis] == 0.0)
+        assert np.all(p[vis] > 0.0)
+
+
+def test_paging_is_a_pure_gather():
+    """Same logical K/V under a contiguous table, a shuffled table and another page size."""
+    w = wl.custom([(10, 37), (1, 12), (20, 20)], 4, 2, 8, 4, 0, seed=8)
+    base = wl.make_inputs(w, shuffle=False)
+    ref = run_oracle(base)
+    rng = np.random.default_rng(1)
+    n_pages = base.k_pages.shape[0]
+    perm = torch.from_numpy(rng.permutation(n_pages))
+    kp = torch.empty_like(base.k_pages)
+    vp = torch.empty_like(base.v_pages)
+    kp[perm] = base.k_pages
+    vp[perm] = base.v_pages
+    shuf = wl.Inputs(w, base.q, kp, vp, perm[base.page_table.long()].to(torch.int32),
+                     base.cu_q_lens, base.kv_lens, int(perm[base.trap_page]), 0, base.scale)
+    assert np.array_equal(run_oracle(shuf), ref)
+    # repack into pages of size 3 (contiguous, sequence-major)
+    for new_b in (3, 64):
+        kv = base.kv_lens.tolist()
+        need = [(k + new_b - 1) // new_b for k in kv]
+        total = sum(need)
+        kp2 = torch.zeros((total + 1, new_b, 2, 8), dtype=torch.bfloat16)
+        vp2 = torch.zeros_like(kp2)
+        pt2 = torch.full((len(kv), max(need)), total, dtype=torch.int32)
+        cur = 0
+        for s, k in enumerate(kv):
+            for t in range(k):
+                src_page, src_slot = int(base.page_table[s, t // 4]), t % 4
+                kp2[cur + t // new_b, t % new_b] = base.k_pages[src_page, src_slot]
+                vp2[cur + t // new_b, t % new_b] = base.v_pages[src_page, src_slot]
+            pt2[s, :need[s]] = torch.arange(cur, cur + need[s])
+            cur += need[s]
+        re = wl.Inputs(w, base.q, kp2, vp2, pt2, base.cu_q_lens, base.kv_lens, total, 0,
+                       base.scale)
+        assert np.array_equal(run_oracle(re), ref)
+
+
+def test_window_covering_everything_is_full_causal():
+    w = wl.custom([(10, 37), (1, 12), (20, 20)], 4, 1, 8, 4, 0, seed=9)
+    inp = wl.make_inputs(w, poison=True)
+    full = run_oracle(inp, window=0)
+    for window in (37, 38, 1000):
+        assert np.array_equal(run_oracle(inp, window=window), full)
+    assert not np.allclose(run_oracle(inp, window=5), full)
+
+
+def test_decode_equals_last_prefill_row_and_chunk_equals_tail():
+    n, prior, chunk = 45, 30, 15
+    w_full = wl.custom([(n, n)], 8, 2, 16, 8, 0, seed=10)
+    full_in = wl.make_inputs(w_full, shuffle=False)
+    full = run_oracle(full_in)
+    # decode: one query token (the last one) on the same cache
+    dec = wl.Inputs(wl.custom([(1, n)], 8, 2, 16, 8), full_in.q[n - 1:n], full_in.k_pages,
+                    full_in.v_pages, full_in.page_table, torch.tensor([0, 1], dtype=torch.int32),
+                    full_in.kv_lens, full_in.trap_page, 0, full_in.scale)
+    np.testing.assert_allclose(run_oracle(dec)[0], full[n - 1], rtol=0, atol=1e-12)
+    # chunk: the last `chunk` tokens with `prior` earlier tokens already cached
+    ch = wl.Inputs(wl.custom([(chunk, n)], 8, 2, 16, 8), full_in.q[prior:], full_in.k_pages,
+                   full_in.v_pages, full_in.page_table,
+                   torch.tensor([0, chunk], dtype=torch.int32), full_in.kv_lens,
+                   full_in.trap_page, 0, full_in.scale)
+    np.testing.assert_allclose(run_oracle(ch), full[prior:], rtol=0, atol=1e-12)
+    # with a window too
+    for window in (7,):
+        fw = run_oracle(full_in, window=window)
+        np.testing.assert_allclose(run_oracle(ch, window=window), fw[prior:], rtol=0, atol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    w = wl.custom([(9, 21), (1, 14)], 8, 2, 8, 4, 6, seed=11)
+    inp = wl.make_inputs(w, poison=True)
+    got = run_oracle(inp)
+    rep = wl.Inputs(wl.custom(w.seqs, 8, 8, 8, 4, 6), inp.q,
+                    inp.k_pages.repeat_interleave(4, dim=2), inp.v_pages.repeat_interleave(4, dim=2),
+                    inp.page_table, inp.cu_q_lens, inp.kv_lens, inp.trap_page, 6, inp.scale)
+    np.testing.assert_allclose(run_oracle(rep), got, rtol=0, atol=1e-13)
+
+
+def test_batch_order_permutes_rows_only():
+    w = wl.custom([(9, 21), (1, 14), (4, 4), (0, 3)], 4, 1, 8, 4, 0, seed=12)
+    inp = wl.make_inputs(w, poison=True)
+    got = run_oracle(inp)
+    order = [2, 0, 3, 1]
+    cu = inp.cu_q_lens.tolist()
+    q_parts = [inp.q[cu[s]:cu[s + 1]] for s in order]
+    qlens = [cu[s + 1] - cu[s] for s in order]
+    cu2 = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32)
+    perm_in = wl.Inputs(w, torch.cat(q_parts), inp.k_pages, inp.v_pages,
+                        inp.page_table[order], cu2, inp.kv_lens[order], inp.trap_page, 0, inp.scale)
+    got2 = run_oracle(perm_in)
+    expect = np.concatenate([got[cu[s]:cu[s + 1]] for s in order])
+    assert np.array_equal(got2, expect)
+
+
+def test_row_blocks_and_row_subsets_are_exact(monkeypatch):
+    w = wl.custom([(40, 70), (3, 9)], 4, 2, 8, 8, 11, seed=13)
+    inp = wl.make_inputs(w, poison=True)
+    full = run_oracle(inp)
+    monkeypatch.setattr(ora, "ROW_BLOCK", 7)
+    np.testing.assert_allclose(run_oracle(inp), full, rtol=0, atol=1e-13)
+    rows = [42, 0, 39, 17]
+    sub = ora.forward_rows(inp.q, inp.k_pages, inp.v_pages, inp.page_table, inp.cu_q_lens,
+                           inp.kv_lens, 11, inp.scale, rows)
+    np.testing.assert_allclose(sub, full[rows], rtol=0, atol=1e-13)
+
+
+def test_metadata_errors():
+    w = wl.custom([(2, 4)], 4, 2, 8, 4, 0, seed=14)
+    inp = wl.make_inputs(w)
+    with pytest.raises(ValueError):
+        ora.forward(inp.q, inp.k_pages, inp.v_pages, inp.page_table, inp.cu_q_lens,
+                    torch.tensor([1], dtype=torch.int32), 0, 1.0)
+    with pytest.raises(ValueError):
+        ora.forward(inp.q, inp.k_pages, inp.v_pages, inp.page_table, inp.cu_q_lens,
+                    inp.kv_lens, -1, 1.0)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must be caught by at least one pin
+# ---------------------------------------------------------------------------
+
+def _pins_pass() -> bool:
+    """Run a compact set of the pins above; False if any of them fails."""
+    checks = [
+        lambda: test_brute_force(small_cases()[7]),
+        lambda: test_brute_force(small_cases()[30]),
+        lambda: test_library_sdpa(wl.custom([(5, 40), (0, 7), (33, 33), (1, 90)], 8, 2, 32, 16, 17, seed=12)),
+        test_golden_hand_worked,
+        test_window_one_returns_own_value,
+        test_gqa_equals_mha_with_repeated_kv,
+    ]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+def _mut_window_off_by_one(q_len, kv_len, window, rows=None):
+    if rows is None:
+        rows = np.arange(q_len)
+    p = (kv_len - q_len + np.asarray(rows))[:, None]
+    j = np.arange(kv_len)[None, :]
+    ok = j <= p
+    if window > 0:
+        ok &= j >= p - window          # W + 1 keys
+    return ok
+
+
+def _mut_query_at_front(q_len, kv_len, window, rows=None):
+    if rows is None:
+        rows = np.arange(q_len)
+    p = np.asarray(rows)[:, None]      # forgets the prior context
+    j = np.arange(kv_len)[None, :]
+    ok = j <= p
+    if window > 0:
+        ok &= j >= p - window + 1
+    return ok
+
+
+def _mut_unpage_slot(pages, table_row, kv_len, page_size):
+    out = np.empty((kv_len,) + pages.shape[2:], dtype=np.float64)
+    for t in range(kv_len):
+        out[t] = pages[int(table_row[t // page_size]), (t + 1) % page_size]
+    return out
+
+
+def _mut_softmax_no_normalise(scores, mask):
+    s = np.where(mask, scores, -np.inf)
+    return np.exp(s - s.max(axis=-1, keepdims=True))
+
+
+def test_pins_pass_on_the_real_oracle():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("name,attr,fn", [
+    ("window W+1 keys", "visible", _mut_window_off_by_one),
+    ("queries placed at the front", "visible", _mut_query_at_front),
+    ("wrong page slot", "unpage", _mut_unpage_slot),
+    ("softmax not normalised", "softmax_rows", _mut_softmax_no_normalise),
+])
+def test_planted_mistake_is_caught(monkeypatch, name, attr, fn):
+    monkeypatch.setattr(ora, attr, fn)
+    assert not _pins_pass(), f"planted mistake not caught: {name}"
+
+
+def test_planted_gqa_mapping_is_caught(monkeypatch):
+    real = ora.forward_rows
+
+    def swapped(q, k_pages, v_pages, *a, **k):
+        # query head h reads KV head h % Hkv instead of h // G
+        qf = ora.as_f64(q)
+        hq, hkv = qf.shape[1], k_pages.shape[2]
+        g = hq // hkv
+        order = [(h % hkv) * g + h // hkv for h in range(hq)]
+        inv = np.argsort(order)
+        out = real(qf[:, order, :], k_pages, v_pages, *a, **k)
+        return out[:, inv, :]
+    monkeypatch.setattr(ora, "forward_rows", swapped)
+    assert not _pins_pass()
