@@ -1,0 +1,178 @@
+/*
+ * rpa.h -- ragged paged attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes, for every query token of a step, causal (optionally
+ * sliding-window) grouped-query attention over that token's sequence, whose
+ * keys and values live in fixed-size pages found through a per-sequence page
+ * table.  The step's query tokens of all sequences are flattened into one
+ * array, with per-sequence metadata giving their structure ("TPU Deep Dive",
+ * chapter 8, "Continuous batching with static shapes": flattened token batch,
+ * true lengths handled inside the kernel, decode / prefill / mixed steps).
+ *
+ * The operation (the pages' method, read plainly):
+ *   For sequence s with q_len = cu_q_lens[s+1] - cu_q_lens[s] and kv_len =
+ *   kv_lens[s], query row r sits at position p = kv_len - q_len + r (the step's
+ *   tokens are the last q_len of the sequence: chunked prefill on a cached
+ *   prefix, "Pallas Kernel: vLLM on TPU ...", environment section).  Key t of
+ *   the sequence is slot t % page_size of page page_table[s][t / page_size]
+ *   (same page, S3: KV in 128-token blocks).  Query head h reads KV head
+ *   h / G with G = num_q_heads / num_kv_heads ("TPU Deep Dive", chapter 4:
+ *   several query heads share a KV head).  Key j is visible from position p iff
+ *   j <= p and, when window W > 0, j >= p - W + 1 (a key is wanted by the W
+ *   queries that follow it, "Chasing speed of light on TPU v6e", section
+ *   Attention).  Then
+ *       out[row, h, :] = sum_j softmax_j(scale * q[row, h, :] . k_j) * v_j
+ *   over the visible keys: the two per-head products of footnote 5 of that
+ *   section, with fp32 softmax accumulators (its footnote 6).
+ *
+ * Data types are fixed: bf16 tensors, int32 metadata, fp32 accumulation,
+ * bf16 output rounded to nearest even.
+ *
+ * Threading: a context is not thread-safe; use one context per stream.
+ * Every call that takes a stream only enqueues work on it and returns.
+ */
+#ifndef RPA_H
+#define RPA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  No exception or abort crosses this interface. */
+enum {
+  RPA_OK = 0,
+  RPA_ERR_INVALID_ARG = -1, /* a pointer, size or metadata value is invalid   */
+  RPA_ERR_UNSUPPORTED = -2, /* head_dim / head ratio without a compiled kernel */
+  RPA_ERR_OOM = -3,         /* device or pinned host allocation failed         */
+  RPA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed      */
+};
+
+typedef struct rpa_ctx rpa_ctx;
+
+/* Shapes fixed for the lifetime of a context. */
+typedef struct rpa_config {
+  int32_t num_q_heads;       /* Hq >= 1                                         */
+  int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0                          */
+  int32_t head_dim;          /* D: 64, 128, 256 or 512                          */
+  int32_t page_size;         /* B: tokens per page, >= 1                        */
+  int32_t max_num_seqs;      /* most sequences of one call                      */
+  int32_t max_pages_per_seq; /* row stride of page_table, >= 1                  */
+  int64_t max_q_tokens;      /* most query tokens of one call                   */
+} rpa_config;
+
+/*
+ * rpa_create -- validate `cfg` and allocate a context (host memory only; the
+ * device work-list and split-KV workspace are allocated on first use, on the
+ * device that is current then, and grow as needed).
+ * Returns RPA_OK and *out_ctx, RPA_ERR_INVALID_ARG for a bad config or null
+ * pointer, RPA_ERR_UNSUPPORTED for a head_dim without a compiled kernel.
+ */
+int rpa_create(const rpa_config* cfg, rpa_ctx** out_ctx);
+
+/*
+ * rpa_forward -- one ragged paged attention call (the operation above).
+ *
+ *   q          device, bf16 [T, Hq, D] row-major, T = cu_q_lens[num_seqs]
+ *   k_pages    device, bf16 [P, page_size, Hkv, D] row-major (P pages)
+ *   v_pages    device, bf16 [P, page_size, Hkv, D] row-major
+ *   page_table device, int32 [num_seqs, max_pages_per_seq] row-major; entries
+ *              past ceil(kv_len / page_size) are never read
+ *   cu_q_lens  HOST, int32 [num_seqs + 1]; cu[0] = 0, non-decreasing
+ *   kv_lens    HOST, int32 [num_seqs]; q_len <= kv_len, ceil(kv_len / B) <=
+ *              max_pages_per_seq; kv_len includes this step's tokens, whose K/V
+ *              must already be in their pages
+ *   num_seqs   0 <= num_seqs <= max_num_seqs
+ *   window     0: full causal; W > 0: keys p - W + 1 .. p; negative is an error
+ *   scale      finite multiplier of q.k before the softmax (usually 1/sqrt(D))
+ *   out        device, bf16 [T, Hq, D]; must not overlap q
+ *   stream     a hipStream_t (NULL = the null stream)
+ *
+ * Host arrays are read before the call returns and may be freed afterwards.
+ * Device buffers are owned by the caller and must stay valid until the
+ * enqueued work has completed.  Page slots past kv_len and the pool's other
+ * pages may hold anything (even NaN): they never reach the result.
+ * Every argument check runs on the host before anything is enqueued: a call
+ * that returns an error has enqueued nothing.  Page-table *values* are device
+ * data and are not checked.  Returns RPA_OK, RPA_ERR_INVALID_ARG, RPA_ERR_OOM
+ * or RPA_ERR_HIP; rpa_last_error() then holds a message.
+ */
+int rpa_forward(rpa_ctx* ctx, const void* q, const void* k_pages, const void* v_pages,
+                const int32_t* page_table, const int32_t* cu_q_lens, const int32_t* kv_lens,
+                int32_t num_seqs, int32_t window, float scale, void* out, void* stream);
+
+/* rpa_destroy -- free a context (NULL-safe).  The caller must first make sure
+ * no work enqueued with it is still running. */
+void rpa_destroy(rpa_ctx* ctx);
+
+/* rpa_status_string -- static text of a status code. */
+const char* rpa_status_string(int status);
+
+/* rpa_last_error -- message of the context's last failing call ("" if none). */
+const char* rpa_last_error(const rpa_ctx* ctx);
+
+/*
+ * Tuning options (rpa_set_option).  Every option changes only how the work is
+ * scheduled, never what is computed: block sizes change scheduling, not
+ * arithmetic ("Chasing speed of light on TPU v6e", footnote 6 of section
+ * Attention; "Pallas Kernel: vLLM on TPU ...", S7).
+ */
+enum {
+  RPA_OPT_DECODE_SPLIT_KEYS = 1, /* keys per split of a decode item; 0 = automatic
+                                    (a positive value is rounded up to 32)      */
+  RPA_OPT_PATH = 2,              /* 0 automatic, 1 every sequence through the
+                                    prefill kernel, 2 decode kernel wherever the
+                                    rows of a sequence fit one decode item      */
+  RPA_OPT_MERGE = 3,             /* 0 automatic (fused), 1 fused: the last split
+                                    of a group merges, 2 separate merge kernel   */
+  RPA_OPT_DECODE_MAX_ROWS = 4    /* most q_len * G rows of a decode item (1..16)  */
+};
+/* Returns RPA_OK or RPA_ERR_INVALID_ARG (unknown option or bad value). */
+int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);
+
+/*
+ * Planner introspection (host only, no device call).  The host builds the
+ * work list that the kernels consume: one item per (sequence, KV head, query
+ * tile, key range), the GPU form of the per-sequence metadata the pages'
+ * kernel reads ("TPU Deep Dive", chapter 8).
+ */
+typedef struct rpa_work_item {
+  int32_t seq;          /* sequence index                                          */
+  int32_t kv_head;      /* KV head g; query heads g*G .. g*G+G-1                   */
+  int32_t q_start;      /* first flattened query token of the item                 */
+  int32_t q_count;      /* query tokens in the item                                */
+  int32_t q_pos0;       /* position of token q_start in its sequence               */
+  int32_t kv_begin;     /* first key of the item's range (inclusive)               */
+  int32_t kv_end;       /* end of the range (exclusive), <= kv_len                 */
+  int32_t split_group;  /* -1: writes the output; else index of its merge group    */
+  int32_t split_index;  /* 0 .. num_splits-1 within the group                      */
+  int32_t num_splits;   /* splits in the group (1 when split_group == -1)          */
+  int32_t partial_base; /* first partial-result slot of the group                  */
+  int32_t kind;         /* 0: prefill kernel item, 1: decode kernel item           */
+} rpa_work_item;
+
+typedef struct rpa_plan_info {
+  int32_t num_prefill_items;
+  int32_t num_decode_items;
+  int32_t num_split_groups;
+  int32_t num_partials;     /* partial-result slots used                            */
+  int32_t prefill_rows;     /* query rows (tokens x grouped heads) per prefill tile */
+  int32_t decode_split_keys;/* keys per decode split chosen                         */
+  int64_t visible_pairs;    /* visible (query, key) pairs per query head            */
+} rpa_plan_info;
+
+/*
+ * rpa_plan -- build the work list for the given metadata without launching.
+ * Writes *info and, when items != NULL, up to `capacity` items (prefill items
+ * first, then decode items, each in launch order).  Same checks as
+ * rpa_forward on the metadata.  Returns RPA_OK or RPA_ERR_INVALID_ARG.
+ */
+int rpa_plan(rpa_ctx* ctx, const int32_t* cu_q_lens, const int32_t* kv_lens, int32_t num_seqs,
+             int32_t window, rpa_plan_info* info, rpa_work_item* items, int32_t capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPA_H */

@@ -1,0 +1,160 @@
+"""Ragged paged attention forward for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``librpa.so`` (include/rpa.h): it only
+checks and marshals arguments.  Every step of the attention runs in the HIP
+kernels of the library; there is no fallback path.  PyTorch provides device
+memory and the current stream.
+
+    attn = RaggedPagedAttention(num_q_heads=8, num_kv_heads=1, head_dim=256,
+                                page_size=128, max_num_seqs=512,
+                                max_pages_per_seq=64, max_q_tokens=8192)
+    out = attn.forward(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens,
+                       window=0, scale=256 ** -0.5)
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (RPA_ERR_HIP, RPA_ERR_INVALID_ARG, RPA_ERR_OOM, RPA_ERR_UNSUPPORTED, RPA_OK,
+                   RPA_OPT_DECODE_MAX_ROWS, RPA_OPT_DECODE_SPLIT_KEYS, RPA_OPT_MERGE, RPA_OPT_PATH,
+                   PlanInfo, RpaError, WorkItem)
+
+__all__ = ["RaggedPagedAttention", "rpa_forward", "RpaError", "library_path", "RPA_OK",
+           "RPA_ERR_INVALID_ARG", "RPA_ERR_UNSUPPORTED", "RPA_ERR_OOM", "RPA_ERR_HIP",
+           "RPA_OPT_DECODE_SPLIT_KEYS", "RPA_OPT_PATH", "RPA_OPT_MERGE", "RPA_OPT_DECODE_MAX_ROWS"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _host_i32(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        x = x.detach().to("cpu")
+        x = x.numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class RaggedPagedAttention:
+    """One library context (fixed head counts, head size and page size)."""
+
+    def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+                 max_num_seqs: int, max_pages_per_seq: int, max_q_tokens: int):
+        self._lib = _lib.load()
+        cfg = _lib.Config(num_q_heads, num_kv_heads, head_dim, page_size, max_num_seqs,
+                          max_pages_per_seq, max_q_tokens)
+        ctx = ctypes.c_void_p()
+        st = self._lib.rpa_create(ctypes.byref(cfg), ctypes.byref(ctx))
+        if st != RPA_OK:
+            raise RpaError(st, f"rpa_create failed: {self._lib.rpa_status_string(st).decode()}")
+        self._ctx = ctx
+        self.num_q_heads = num_q_heads
+        self.num_kv_heads = num_kv_heads
+        self.head_dim = head_dim
+        self.page_size = page_size
+        self.max_pages_per_seq = max_pages_per_seq
+
+    # -- lifetime -------------------------------------------------------------
+    def close(self):
+        if getattr(self, "_ctx", None) is not None and self._ctx.value:
+            self._lib.rpa_destroy(self._ctx)
+        self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _error(self, st: int, what: str) -> RpaError:
+        msg = self._lib.rpa_last_error(self._ctx).decode(errors="replace")
+        return RpaError(st, f"{what}: {self._lib.rpa_status_string(st).decode()}: {msg}")
+
+    # -- options / planner ----------------------------------------------------
+    def set_option(self, option: int, value: int) -> None:
+        st = self._lib.rpa_set_option(self._ctx, int(option), int(value))
+        if st != RPA_OK:
+            raise self._error(st, "rpa_set_option")
+
+    def plan(self, cu_q_lens, kv_lens, window: int = 0) -> Tuple[dict, list]:
+        cu = _host_i32(cu_q_lens)
+        kv = _host_i32(kv_lens)
+        n = int(kv.shape[0])
+        info = PlanInfo()
+        st = self._lib.rpa_plan(self._ctx, _i32p(cu), _i32p(kv), n, int(window), ctypes.byref(info),
+                                None, 0)
+        if st != RPA_OK:
+            raise self._error(st, "rpa_plan")
+        total = info.num_prefill_items + info.num_decode_items
+        items = (WorkItem * max(total, 1))()
+        st = self._lib.rpa_plan(self._ctx, _i32p(cu), _i32p(kv), n, int(window), ctypes.byref(info),
+                                items, total)
+        if st != RPA_OK:
+            raise self._error(st, "rpa_plan")
+        return info.as_dict(), [items[i].as_dict() for i in range(total)]
+
+    # -- forward --------------------------------------------------------------
+    def forward(self, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                page_table: torch.Tensor, cu_q_lens, kv_lens, window: int = 0,
+                scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """Enqueue one attention call on ``stream`` (default: torch's current stream)."""
+        if scale is None:
+            scale = float(self.head_dim) ** -0.5
+        cu = _host_i32(cu_q_lens)
+        kv = _host_i32(kv_lens)
+        n = int(kv.shape[0])
+        if cu.shape[0] != n + 1:
+            raise ValueError("cu_q_lens must have num_seqs + 1 entries")
+        for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+        if page_table.dtype != torch.int32 or not page_table.is_cuda or not page_table.is_contiguous():
+            raise ValueError("page_table must be a contiguous int32 CUDA tensor")
+        if q.dim() != 3 or q.shape[1] != self.num_q_heads or q.shape[2] != self.head_dim:
+            raise ValueError(f"q must be [T, {self.num_q_heads}, {self.head_dim}]")
+        if n and int(cu[-1]) != q.shape[0]:
+            raise ValueError("q has a different token count than cu_q_lens[-1]")
+        pool = (self.page_size, self.num_kv_heads, self.head_dim)
+        if k_pages.dim() != 4 or tuple(k_pages.shape[1:]) != pool or k_pages.shape != v_pages.shape:
+            raise ValueError(f"k_pages / v_pages must both be [P, {pool[0]}, {pool[1]}, {pool[2]}]")
+        if page_table.dim() != 2 or page_table.shape[0] < n or page_table.shape[1] != self.max_pages_per_seq:
+            raise ValueError(f"page_table must be [num_seqs, {self.max_pages_per_seq}]")
+        if out is None:
+            out = torch.empty_like(q)
+        elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        with torch.cuda.device(q.device):
+            st = self._lib.rpa_forward(self._ctx, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                       page_table.data_ptr(), _i32p(cu), _i32p(kv), n, int(window),
+                                       float(scale), out.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        if st != RPA_OK:
+            raise self._error(st, "rpa_forward")
+        return out
+
+    __call__ = forward
+
+
+def rpa_forward(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, window: int = 0,
+                scale: Optional[float] = None, out=None):
+    """One-shot call with a temporary context sized to the arguments."""
+    kv = _host_i32(kv_lens)
+    attn = RaggedPagedAttention(q.shape[1], k_pages.shape[2], q.shape[2], k_pages.shape[1],
+                                max(1, kv.shape[0]), page_table.shape[1], max(1, q.shape[0]))
+    try:
+        res = attn.forward(q, k_pages, v_pages, page_table, cu_q_lens, kv, window, scale, out)
+        torch.cuda.current_stream(q.device).synchronize()
+        return res
+    finally:
+        attn.close()

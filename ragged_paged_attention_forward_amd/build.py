@@ -1,0 +1,72 @@
+"""Build step: compiles the HIP kernels and the host library into librpa.so (gfx950).
+
+Run ``python -m ragged_paged_attention_forward_amd.build`` (or call ``build()``).
+hipcc cross-compiles for gfx950, so this works on machines without a GPU.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "librpa.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+
+SOURCES = ["rpa_kernels.hip", "rpa_api.cpp", "rpa_plan.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def compile_flags():
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        # packed fp32 VALU forms stay off: the compiler would otherwise emit them
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
+    ]
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source and link librpa.so in the package directory."""
+    cc = hipcc()
+    out_dir = os.path.join(ROOT, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(out_dir, src + ".o")
+        cmd = [cc] + compile_flags() + list(extra_flags) + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd = [cc, "-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC,
+                   "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src), "-o", obj]
+        _run(cmd, verbose)
+        objs.append(obj)
+    tmp = LIB_PATH + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    text = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{text}")
+    if verbose and text.strip():
+        print(text)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

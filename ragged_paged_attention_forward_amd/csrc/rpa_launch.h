@@ -1,0 +1,40 @@
+// Interface between the host library (rpa_api.cpp) and the kernels (rpa_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "rpa.h"
+
+namespace rpa {
+
+struct LaunchArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  void* out;
+  const rpa_work_item* groups;  // device
+  float* partial_o;             // device [slots][16][D]
+  float* partial_lse;           // device [slots][16]
+  int32_t* counters;            // device, one per split group
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t window;
+  float scale_log2;
+  int32_t fused_merge;
+  void* stream;
+};
+
+// Rows (tokens x grouped heads) per prefill workgroup for a head size, 0 if none.
+int prefill_rows_for(int head_dim);
+bool head_dim_supported(int head_dim);
+
+hipError_t launch_prefill(const LaunchArgs& a, const rpa_work_item* items, int n_items);
+hipError_t launch_decode(const LaunchArgs& a, const rpa_work_item* items, int n_items);
+hipError_t launch_merge(const LaunchArgs& a, int n_groups);
+
+}  // namespace rpa

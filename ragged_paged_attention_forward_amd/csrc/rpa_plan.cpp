@@ -1,0 +1,207 @@
+// Host-side ragged metadata builder.
+//
+// The pages' kernel keeps a block of queries on chip and streams in every key
+// that block attends to, so each key is fetched once per query block that
+// wants it; larger query blocks mean fewer re-reads ("Chasing speed of light on
+// TPU v6e", section Attention, and footnote 6: the query block grows with the
+// query/KV head ratio).  Here a prefill tile packs `prefill_rows` rows of
+// (token, grouped query head) that share one KV head, and its key range is
+// exactly the union of what those rows can see: causal, clipped by the window.
+//
+// Decode sequences (one or a few query tokens) are memory-bound at any batch
+// ("TPU Deep Dive", chapter 4: decode attention intensity is about G; chapter
+// 7: decode is memory-bound), so their key ranges are cut into splits that
+// run in parallel and are merged by log-sum-exp afterwards; key ranges follow
+// the true lengths, never a padded block ("Pallas Kernel: vLLM on TPU ...", S7:
+// oversized KV blocks left most of a decode block as masked padding).
+#include "rpa_plan.h"
+
+#include <algorithm>
+#include <cstdio>
+
+namespace rpa {
+
+namespace {
+
+std::string fmt(const char* f, long long a, long long b = 0, long long c = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, f, a, b, c);
+  return buf;
+}
+
+int32_t range_begin(int64_t pos0, int32_t window) {
+  if (window <= 0) return 0;
+  int64_t lo = pos0 - window + 1;
+  return lo > 0 ? static_cast<int32_t>(lo) : 0;
+}
+
+}  // namespace
+
+int validate_metadata(const PlanParams& p, const int32_t* cu, const int32_t* kv,
+                      int32_t num_seqs, int32_t window, std::string* err) {
+  if (num_seqs < 0 || num_seqs > p.max_num_seqs) {
+    *err = fmt("num_seqs %lld outside [0, %lld]", num_seqs, p.max_num_seqs);
+    return RPA_ERR_INVALID_ARG;
+  }
+  if (window < 0) {
+    *err = fmt("window %lld is negative", window);
+    return RPA_ERR_INVALID_ARG;
+  }
+  if (cu == nullptr || (num_seqs > 0 && kv == nullptr)) {
+    *err = "cu_q_lens / kv_lens is NULL";
+    return RPA_ERR_INVALID_ARG;
+  }
+  if (cu[0] != 0) {
+    *err = fmt("cu_q_lens[0] = %lld, must be 0", cu[0]);
+    return RPA_ERR_INVALID_ARG;
+  }
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t q_len = static_cast<int64_t>(cu[s + 1]) - cu[s];
+    if (q_len < 0) {
+      *err = fmt("cu_q_lens decreases at sequence %lld", s);
+      return RPA_ERR_INVALID_ARG;
+    }
+    if (kv[s] < 0) {
+      *err = fmt("kv_lens[%lld] = %lld is negative", s, kv[s]);
+      return RPA_ERR_INVALID_ARG;
+    }
+    if (q_len > kv[s]) {
+      *err = fmt("sequence %lld: q_len %lld exceeds kv_len %lld", s, q_len, kv[s]);
+      return RPA_ERR_INVALID_ARG;
+    }
+    const int64_t pages = (static_cast<int64_t>(kv[s]) + p.page_size - 1) / p.page_size;
+    if (pages > p.max_pages_per_seq) {
+      *err = fmt("sequence %lld needs %lld pages, max_pages_per_seq is %lld", s, pages,
+                 p.max_pages_per_seq);
+      return RPA_ERR_INVALID_ARG;
+    }
+  }
+  if (cu[num_seqs] > p.max_q_tokens) {
+    *err = fmt("%lld query tokens exceed max_q_tokens %lld", cu[num_seqs], p.max_q_tokens);
+    return RPA_ERR_INVALID_ARG;
+  }
+  return RPA_OK;
+}
+
+void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32_t num_seqs,
+                int32_t window, Plan* out) {
+  out->prefill.clear();
+  out->decode.clear();
+  out->groups.clear();
+  out->num_partials = 0;
+  out->visible_pairs = 0;
+  out->total_q = num_seqs > 0 ? cu[num_seqs] : 0;
+
+  const int group = p.num_q_heads / p.num_kv_heads;
+  const int tile_tokens = std::max(1, p.prefill_rows / group);
+  const int dec_tokens = p.decode_max_rows / group;  // 0 when G exceeds a decode item
+
+  struct DecodeSeq {
+    int32_t seq, q_start, q_count, pos0, kv_begin, kv_end;
+  };
+  std::vector<DecodeSeq> dec;
+
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t q_len = cu[s + 1] - cu[s];
+    const int32_t kv_len = kv[s];
+    if (q_len == 0) continue;
+    const int32_t pos_first = kv_len - q_len;
+    for (int32_t r = 0; r < q_len; ++r) out->visible_pairs += visible_keys(pos_first + r, window);
+
+    const bool fits_decode = dec_tokens > 0 && q_len <= dec_tokens;
+    const bool use_decode = p.path_mode != 1 && fits_decode;
+    if (use_decode) {
+      dec.push_back({s, cu[s], q_len, pos_first, range_begin(pos_first, window), kv_len});
+      continue;
+    }
+    for (int32_t g = 0; g < p.num_kv_heads; ++g) {
+      for (int32_t t = 0; t < q_len; t += tile_tokens) {
+        const int32_t count = std::min(tile_tokens, q_len - t);
+        rpa_work_item it{};
+        it.seq = s;
+        it.kv_head = g;
+        it.q_start = cu[s] + t;
+        it.q_count = count;
+        it.q_pos0 = pos_first + t;
+        it.kv_begin = range_begin(it.q_pos0, window);
+        it.kv_end = it.q_pos0 + count;  // last position + 1
+        it.split_group = -1;
+        it.split_index = 0;
+        it.num_splits = 1;
+        it.partial_base = 0;
+        it.kind = 0;
+        out->prefill.push_back(it);
+      }
+    }
+  }
+
+  // Longest first: the most expensive tiles start first so the tail is short.
+  std::stable_sort(out->prefill.begin(), out->prefill.end(),
+                   [](const rpa_work_item& a, const rpa_work_item& b) {
+                     const int64_t ca = int64_t(a.kv_end - a.kv_begin) * a.q_count;
+                     const int64_t cb = int64_t(b.kv_end - b.kv_begin) * b.q_count;
+                     return ca > cb;
+                   });
+
+  // Decode split size: enough splits to give every compute unit a few
+  // workgroups, in whole multiples of what one workgroup takes per step.
+  const int64_t wg_keys = int64_t(p.decode_wave_keys) * p.decode_waves;
+  int64_t split = p.decode_split_keys;
+  if (split <= 0) {
+    int64_t total = 0;
+    for (const auto& d : dec) total += int64_t(d.kv_end - d.kv_begin) * p.num_kv_heads;
+    const int64_t target = int64_t(2) * p.num_cus;
+    split = (total + target - 1) / std::max<int64_t>(target, 1);
+    split = (split + wg_keys - 1) / wg_keys * wg_keys;
+    if (split < wg_keys) split = wg_keys;
+  } else {
+    split = (split + p.decode_wave_keys - 1) / p.decode_wave_keys * p.decode_wave_keys;
+  }
+  out->decode_split_keys = static_cast<int>(split);
+
+  for (const auto& d : dec) {
+    const int64_t keys = d.kv_end - d.kv_begin;
+    const int32_t n = static_cast<int32_t>(std::max<int64_t>(1, (keys + split - 1) / split));
+    for (int32_t g = 0; g < p.num_kv_heads; ++g) {
+      rpa_work_item base{};
+      base.seq = d.seq;
+      base.kv_head = g;
+      base.q_start = d.q_start;
+      base.q_count = d.q_count;
+      base.q_pos0 = d.pos0;
+      base.kind = 1;
+      base.num_splits = n;
+      if (n == 1) {
+        base.kv_begin = d.kv_begin;
+        base.kv_end = d.kv_end;
+        base.split_group = -1;
+        base.split_index = 0;
+        base.partial_base = 0;
+        out->decode.push_back(base);
+        continue;
+      }
+      base.split_group = static_cast<int32_t>(out->groups.size());
+      base.partial_base = out->num_partials;
+      out->num_partials += n;
+      for (int32_t i = 0; i < n; ++i) {
+        rpa_work_item it = base;
+        it.split_index = i;
+        it.kv_begin = static_cast<int32_t>(d.kv_begin + int64_t(i) * split);
+        it.kv_end = static_cast<int32_t>(std::min<int64_t>(d.kv_end, d.kv_begin + int64_t(i + 1) * split));
+        if (i == 0) {
+          rpa_work_item grp = it;
+          grp.kv_begin = d.kv_begin;
+          grp.kv_end = d.kv_end;
+          out->groups.push_back(grp);
+        }
+        out->decode.push_back(it);
+      }
+    }
+  }
+  std::stable_sort(out->decode.begin(), out->decode.end(),
+                   [](const rpa_work_item& a, const rpa_work_item& b) {
+                     return (a.kv_end - a.kv_begin) > (b.kv_end - b.kv_begin);
+                   });
+}
+
+}  // namespace rpa

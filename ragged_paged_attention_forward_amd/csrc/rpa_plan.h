@@ -1,0 +1,55 @@
+// Host-side ragged metadata builder: turns per-sequence query/KV lengths into
+// the work lists the attention kernels consume.  Pure C++ (no HIP), so it is
+// also exercised on machines without a GPU through rpa_plan().
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "rpa.h"
+
+namespace rpa {
+
+struct PlanParams {
+  int num_q_heads = 0;
+  int num_kv_heads = 0;
+  int head_dim = 0;
+  int page_size = 0;
+  int max_num_seqs = 0;
+  int max_pages_per_seq = 0;
+  int64_t max_q_tokens = 0;
+  int prefill_rows = 128;      // query rows (tokens x grouped heads) per prefill tile
+  int decode_max_rows = 16;    // most rows of one decode item
+  int decode_wave_keys = 32;   // keys one decode wave takes per step
+  int decode_waves = 4;        // waves of one decode workgroup
+  int64_t decode_split_keys = 0;  // 0: automatic
+  int path_mode = 0;           // 0 auto, 1 all prefill kernel, 2 decode where it fits
+  int num_cus = 256;           // compute units to fill
+};
+
+struct Plan {
+  std::vector<rpa_work_item> prefill;  // launch order
+  std::vector<rpa_work_item> decode;   // launch order
+  std::vector<rpa_work_item> groups;   // one entry per split group (its split 0)
+  int num_partials = 0;
+  int decode_split_keys = 0;
+  int64_t visible_pairs = 0;
+  int64_t total_q = 0;
+};
+
+// Checks the metadata of one call.  Returns RPA_OK or RPA_ERR_INVALID_ARG with *err set.
+int validate_metadata(const PlanParams& p, const int32_t* cu_q_lens, const int32_t* kv_lens,
+                      int32_t num_seqs, int32_t window, std::string* err);
+
+// Builds the work lists (metadata must have passed validate_metadata).
+void build_plan(const PlanParams& p, const int32_t* cu_q_lens, const int32_t* kv_lens,
+                int32_t num_seqs, int32_t window, Plan* out);
+
+// Number of visible keys of query position `pos` (keys 0..pos, clipped by the window).
+inline int64_t visible_keys(int64_t pos, int32_t window) {
+  if (window > 0 && pos + 1 > window) return window;
+  return pos + 1;
+}
+
+}  // namespace rpa

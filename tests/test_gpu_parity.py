@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: max-abs <= 2e-2 and mean-abs <= 2e-3 over every compared element, no NaN.
+Page slots past kv_len and the pool's trap page are filled with NaN, so any
+read of them shows up as a non-finite output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import rpa_workloads as wl
+from gpu_common import compare, gpu_available, make_attn, oracle_rows, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+if not gpu_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import ragged_paged_attention_forward_amd as R  # noqa: E402
+
+
+def mixed_small(window, seed=205):
+    rng = np.random.default_rng(seed)
+    kv = rng.integers(64, 1500, 64)
+    chunks = [(300, 300), (150, 230), (70, 400), (33, 80)]
+    return wl.Workload(f"mixed_small_w{window}", chunks + [(1, int(k)) for k in kv], 8, 1, 256, 128,
+                       window, seed, length_draw=(64, 1500, 64))
+
+
+SMALL = {
+    "tiny": lambda: wl.tiny(),
+    "decode": lambda: wl.decode(),
+    "swa_prefill_1100": lambda: wl.swa_prefill(tokens=1100),
+    "global_prefill_777": lambda: wl.global_prefill(tokens=777),
+    "mixed_small_w0": lambda: mixed_small(0),
+    "mixed_small_w1024": lambda: mixed_small(1024),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small(name):
+    w = SMALL[name]()
+    inp = wl.make_inputs(w, poison=True)
+    attn = make_attn(w)
+    got = run_gpu(attn, inp)
+    ref = oracle_rows(inp)
+    mx, mean = compare(got, ref, label=name)
+    print(f"{name}: max-abs {mx:.3e} mean-abs {mean:.3e}")
+
+
+FULL = {
+    "swa_prefill": wl.swa_prefill,
+    "global_prefill": wl.global_prefill,
+    "mixed": lambda: wl.mixed(window=0),
+    "mixed_swa": lambda: wl.mixed(window=1024),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_parity_full_size_sampled(name):
+    """Full-size workloads; the oracle computes a seeded sample of rows one by one."""
+    w = FULL[name]()
+    inp = wl.make_inputs(w, poison=True)
+    attn = make_attn(w)
+    got = run_gpu(attn, inp)
+    t = w.total_q
+    cu = inp.cu_q_lens.tolist()
+    must = [0, 1, t - 1]
+    for s in range(min(w.num_seqs, 4)):
+        must += [cu[s], cu[s + 1] - 1, cu[s] + 127, cu[s] + 128, cu[s] + 1023, cu[s] + 1024]
+    if w.num_seqs > 4:   # every decode row of the mixed step
+        must += list(range(cu[4], t))
+    rows = wl.sample_rows(t, 40, w.seed, must)
+    ref = oracle_rows(inp, rows)
+    mx, mean = compare(got, ref, rows=rows, label=name)
+    print(f"{name}: {len(rows)} rows, max-abs {mx:.3e} mean-abs {mean:.3e}")
+
+
+def test_parity_decode_full_size():
+    w = wl.decode()
+    inp = wl.make_inputs(w, poison=True)
+    got = run_gpu(make_attn(w), inp)
+    compare(got, oracle_rows(inp), label="decode")
+
+
+VARIANTS = [
+    ("all_prefill_kernel", {R.RPA_OPT_PATH: 1}),
+    ("split32", {R.RPA_OPT_DECODE_SPLIT_KEYS: 32}),
+    ("split64", {R.RPA_OPT_DECODE_SPLIT_KEYS: 64}),
+    ("split96", {R.RPA_OPT_DECODE_SPLIT_KEYS: 96}),
+    ("split_none", {R.RPA_OPT_DECODE_SPLIT_KEYS: 1 << 20}),
+    ("merge_kernel", {R.RPA_OPT_MERGE: 2}),
+    ("merge_kernel_split32", {R.RPA_OPT_MERGE: 2, R.RPA_OPT_DECODE_SPLIT_KEYS: 32}),
+    ("decode_rows8", {R.RPA_OPT_DECODE_MAX_ROWS: 8}),
+]
+
+
+@pytest.mark.parametrize("window", [0, 700])
+def test_scheduling_variants_agree(window):
+    """Tile/split/merge choices change scheduling, not the result."""
+    w = mixed_small(window, seed=300 + window)
+    inp = wl.make_inputs(w, poison=True)
+    ref = oracle_rows(inp)
+    base = run_gpu(make_attn(w), inp)
+    compare(base, ref, label="default")
+    for label, opts in VARIANTS:
+        attn = make_attn(w)
+        for k, v in opts.items():
+            attn.set_option(k, v)
+        got = run_gpu(attn, inp)
+        compare(got, ref, label=label)
+        d = (got.float() - base.float()).abs().max().item()
+        assert d <= 2e-2, f"{label} differs from default by {d}"
+
+
+def test_multi_token_decode_items_and_splits():
+    """q_len 2 with G 8 fits one decode item; splits then hold rows with no visible key."""
+    seqs = [(2, 300), (2, 2), (1, 129), (2, 1000), (1, 1)]
+    for window in (0, 5, 200):
+        w = wl.custom(seqs, 8, 1, 256, 128, window, seed=41)
+        inp = wl.make_inputs(w, poison=True)
+        ref = oracle_rows(inp)
+        for split in (0, 32):
+            attn = make_attn(w)
+            attn.set_option(R.RPA_OPT_DECODE_SPLIT_KEYS, split)
+            compare(run_gpu(attn, inp), ref, label=f"w{window}_split{split}")
+
+
+def test_deterministic_bitwise():
+    w = mixed_small(1024, seed=77)
+    inp = wl.make_inputs(w, poison=True)
+    attn = make_attn(w)
+    a = run_gpu(attn, inp).clone()
+    b = run_gpu(attn, inp).clone()
+    c = run_gpu(make_attn(w), inp)
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("hq,hkv,d,b", [
+    (4, 1, 64, 16), (16, 1, 128, 32), (8, 2, 256, 64), (16, 16, 64, 8), (32, 1, 128, 16),
+    (16, 2, 512, 128), (8, 8, 512, 256), (2, 1, 256, 1), (12, 4, 128, 128),
+])
+def test_shapes(hq, hkv, d, b):
+    seqs = [(0, 5), (1, 1), (9, 9), (1, 300), (40, 170), (3, 77), (130, 130), (2, 513), (0, 0)]
+    for window in (0, 1, 64):
+        w = wl.custom(seqs, hq, hkv, d, b, window, seed=hq * 1000 + d + b)
+        inp = wl.make_inputs(w, poison=True)
+        ref = oracle_rows(inp)
+        attn = make_attn(w)
+        compare(run_gpu(attn, inp), ref, label=f"hq{hq} hkv{hkv} d{d} b{b} w{window}")
+
+
+def test_window_one_returns_own_value_exactly():
+    w = wl.custom([(7, 20), (1, 300), (50, 50)], 8, 1, 256, 16, 1, seed=3)
+    inp = wl.make_inputs(w, poison=True)
+    got = run_gpu(make_attn(w), inp).cpu()
+    cu, kv = inp.cu_q_lens.tolist(), inp.kv_lens.tolist()
+    for s in range(3):
+        ql = cu[s + 1] - cu[s]
+        for r in range(ql):
+            pos = kv[s] - ql + r
+            page, slot = int(inp.page_table[s, pos // 16]), pos % 16
+            for h in range(8):
+                assert torch.equal(got[cu[s] + r, h], inp.v_pages[page, slot, 0])
+
+
+def test_window_covering_everything_equals_causal():
+    w = wl.custom([(100, 300), (1, 200), (64, 64)], 8, 2, 128, 32, 0, seed=5)
+    inp = wl.make_inputs(w, poison=True)
+    attn = make_attn(w)
+    full = run_gpu(attn, inp).clone()
+    wide = run_gpu(attn, inp, window=300).clone()
+    assert torch.equal(full, wide)
+
+
+def test_empty_batch_and_empty_sequences():
+    w = wl.custom([(0, 10), (0, 0)], 8, 1, 256, 128, 0, seed=6)
+    inp = wl.make_inputs(w)
+    attn = make_attn(w)
+    d = inp.to("cuda")
+    out = torch.full((0, 8, 256), 1.0, dtype=torch.bfloat16, device="cuda")
+    attn.forward(d.q, d.k_pages, d.v_pages, d.page_table, inp.cu_q_lens, inp.kv_lens, 0, 0.1, out=out)
+    torch.cuda.synchronize()
+    # zero sequences
+    attn.forward(d.q, d.k_pages, d.v_pages, d.page_table[:0], [0], [], 0, 0.1, out=out)
+    torch.cuda.synchronize()
+
+
+def test_plan_cache_reuse_and_change():
+    """Same metadata reuses the uploaded plan; new metadata replaces it."""
+    attn = None
+    for seed, seqs in ((1, [(1, 100), (5, 300)]), (2, [(1, 700), (1, 64), (30, 30)]), (1, [(1, 100), (5, 300)])):
+        w = wl.custom(seqs, 8, 1, 256, 128, 0, seed=seed, extra_pages_per_seq=8 - (max(k for _, k in seqs) + 127) // 128)
+        inp = wl.make_inputs(w, poison=True)
+        if attn is None:
+            attn = make_attn(w, max_num_seqs=4, max_q_tokens=64)
+        for _ in range(2):
+            compare(run_gpu(attn, inp), oracle_rows(inp), label=f"seed{seed}")
