@@ -124,9 +124,8 @@ enum {
   RPA_OPT_PATH = 2,              /* 0 automatic, 1 every sequence through the
                                     prefill kernel, 2 decode kernel wherever the
                                     rows of a sequence fit one decode item      */
-  RPA_OPT_MERGE = 3,             /* 0 automatic (fused), 1 fused: the last split
-                                    of a group merges, 2 separate merge kernel   */
-  RPA_OPT_DECODE_MAX_ROWS = 4    /* most q_len * G rows of a decode item (1..16)  */
+  RPA_OPT_DECODE_MAX_ROWS = 4,   /* most q_len * G rows of a decode item (1..16)  */
+  RPA_OPT_DECODE_WAVES = 5       /* waves per decode workgroup: 0 automatic, 4, 8 */
 };
 /* Returns RPA_OK or RPA_ERR_INVALID_ARG (unknown option or bad value). */
 int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);

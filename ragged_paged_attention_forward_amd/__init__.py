@@ -21,12 +21,14 @@ import torch
 
 from . import _lib
 from ._lib import (RPA_ERR_HIP, RPA_ERR_INVALID_ARG, RPA_ERR_OOM, RPA_ERR_UNSUPPORTED, RPA_OK,
-                   RPA_OPT_DECODE_MAX_ROWS, RPA_OPT_DECODE_SPLIT_KEYS, RPA_OPT_MERGE, RPA_OPT_PATH,
+                   RPA_OPT_DECODE_MAX_ROWS, RPA_OPT_DECODE_SPLIT_KEYS, RPA_OPT_DECODE_WAVES,
+                   RPA_OPT_PATH,
                    PlanInfo, RpaError, WorkItem)
 
 __all__ = ["RaggedPagedAttention", "rpa_forward", "RpaError", "library_path", "RPA_OK",
            "RPA_ERR_INVALID_ARG", "RPA_ERR_UNSUPPORTED", "RPA_ERR_OOM", "RPA_ERR_HIP",
-           "RPA_OPT_DECODE_SPLIT_KEYS", "RPA_OPT_PATH", "RPA_OPT_MERGE", "RPA_OPT_DECODE_MAX_ROWS"]
+           "RPA_OPT_DECODE_SPLIT_KEYS", "RPA_OPT_PATH", "RPA_OPT_DECODE_MAX_ROWS",
+           "RPA_OPT_DECODE_WAVES"]
 
 
 def library_path() -> str:

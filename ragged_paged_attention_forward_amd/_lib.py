@@ -15,8 +15,8 @@ RPA_ERR_HIP = -4
 
 RPA_OPT_DECODE_SPLIT_KEYS = 1
 RPA_OPT_PATH = 2
-RPA_OPT_MERGE = 3
 RPA_OPT_DECODE_MAX_ROWS = 4
+RPA_OPT_DECODE_WAVES = 5
 
 EXPORTED = ("rpa_create", "rpa_forward", "rpa_destroy", "rpa_status_string", "rpa_last_error",
             "rpa_set_option", "rpa_plan")

@@ -16,8 +16,7 @@
 //    batch size ("TPU Deep Dive", chapter 4 and 7), so the waves of a
 //    workgroup each stream a different 32-key chunk straight from HBM into
 //    MFMA operand registers, and splits of long sequences run in parallel and
-//    are merged by log-sum-exp (by the last split to finish, or by
-//    rpa_merge_kernel).
+//    are merged by log-sum-exp in rpa_merge_kernel.
 //
 // Both compute S^T = K * Q^T and O^T = V^T * P^T with the bf16 MFMA
 // v_mfma_f32_16x16x32_bf16, so that a query row is always the MFMA column
@@ -82,6 +81,13 @@ RPA_DEV void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
 
 RPA_DEV u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Wave-uniform load through the constant address space, so it becomes a
+// scalar load that does not wait behind the vector loads in flight.
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+RPA_DEV int32_t uniform_load(const int32_t* p, int idx) {
+  return ((const_i32_ptr)(p))[idx];
+}
+
 struct KernelArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -92,7 +98,6 @@ struct KernelArgs {
   const rpa_work_item* groups;
   float* partial_o;      // [slot][16 rows][D]
   float* partial_lse;    // [slot][16 rows], base-2 log-sum-exp
-  int32_t* counters;     // one per split group, zero between calls
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;         // G = Hq / Hkv
@@ -100,15 +105,7 @@ struct KernelArgs {
   int32_t max_pages;
   int32_t window;
   float scale_log2;      // scale * log2(e)
-  int32_t fused_merge;
 };
-
-// Element offset of key `t` of sequence row `pt_row` for KV head g.
-RPA_DEV int64_t kv_offset(const int32_t* pt_row, int t, int page_size, int hkv, int g, int D) {
-  const int page = pt_row[t / page_size];
-  const int slot = t - (t / page_size) * page_size;
-  return ((static_cast<int64_t>(page) * page_size + slot) * hkv + g) * D;
-}
 
 RPA_DEV bool key_visible(int key, int pos, int kv_begin, int kv_end, int window) {
   return key >= kv_begin && key < kv_end && key <= pos && (window <= 0 || key > pos - window);
@@ -142,7 +139,7 @@ RPA_DEV int vt_chunk(int r, int chunk) {
   return chunk ^ (sw & (NC - 1));
 }
 
-template <int D, int NB, int NW, int BN>
+template <int D, int NB, int NW, int BN, bool UNI>
 __global__ void __launch_bounds__(NW * 64)
 rpa_prefill_kernel(KernelArgs args) {
   using C = PrefillCfg<D, NB, NW, BN>;
@@ -153,7 +150,7 @@ rpa_prefill_kernel(KernelArgs args) {
   const rpa_work_item it = args.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 15;   // MFMA column: query row within a block; or key/d row
   const int lq = lane >> 4;   // lane quad 0..3
 
@@ -161,7 +158,11 @@ rpa_prefill_kernel(KernelArgs args) {
   const int hkv = args.num_kv_heads;
   const int G = args.group;
   const int g = it.kv_head;
-  const int32_t* pt_row = args.page_table + static_cast<int64_t>(it.seq) * args.max_pages;
+  const int32_t* __restrict__ pt_row = args.page_table + static_cast<int64_t>(it.seq) * args.max_pages;
+  const uint16_t* __restrict__ kbase = args.k;
+  const uint16_t* __restrict__ vbase = args.v;
+  const int page_size = args.page_size;
+  const int64_t row_stride = static_cast<int64_t>(hkv) * D;  // elements between slots of a page
 
   // ---- per-lane rows, Q fragments (B operand of S^T = K Q^T) ----
   int row_pos[NB];
@@ -196,7 +197,8 @@ rpa_prefill_kernel(KernelArgs args) {
 
   const int kv_begin = it.kv_begin;
   const int kv_end = it.kv_end;
-  const int n_tiles = (kv_end - kv_begin + BN - 1) / BN;
+  const int tile0 = (kv_begin / BN) * BN;  // tiles are aligned to BN keys
+  const int n_tiles = (kv_end - tile0 + BN - 1) / BN;
   const int pos_min = it.q_pos0;
   const int pos_max = it.q_pos0 + it.q_count - 1;
   const int window = args.window;
@@ -206,7 +208,50 @@ rpa_prefill_kernel(KernelArgs args) {
   u32x4 kreg[C::K_PER_T];
   u32x4 vreg[C::V_PER_T][8];
 
+  // Element offset of key `key` (KV head g).  With UNI every page holds a whole
+  // number of tiles, so one wave-uniform page lookup serves the tile.
   auto load_tile = [&](int k0) {
+    int64_t ubase = 0;
+    if constexpr (UNI) {
+      const int pidx = k0 / page_size;
+      const int64_t page = uniform_load(pt_row, pidx);
+      ubase = ((page * page_size + (k0 - pidx * page_size)) * hkv + g) * D;
+    }
+    auto kv_row = [&](int key, int pid) -> int64_t {
+      if constexpr (UNI) {
+        return ubase + static_cast<int64_t>(key - k0) * row_stride;
+      } else {
+        const int slot = key - (key / page_size) * page_size;
+        return ((static_cast<int64_t>(pid) * page_size + slot) * hkv + g) * D;
+      }
+    };
+    // page ids of every row this thread loads, fetched before any K/V load
+    int kpid[C::K_PER_T];
+    int vpid[C::V_PER_T][8];
+#pragma unroll
+    for (int i = 0; i < C::K_PER_T; ++i) {
+      kpid[i] = 0;
+      if constexpr (!UNI) {
+        const int u = i * C::NT + tid;
+        const int key = k0 + u / (D / 8);
+        if (u < C::K_UNITS && key >= kv_begin && key < kv_end) kpid[i] = pt_row[key / page_size];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::V_PER_T; ++i) {
+      const int u = i * C::NT + tid;
+      const int grp = u / (D / 8);
+      const int t = grp >> 2;
+      const int qd = grp & 3;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        vpid[i][j] = 0;
+        if constexpr (!UNI) {
+          const int key = k0 + t * 32 + ((j < 4) ? (qd * 4 + j) : (16 + qd * 4 + j - 4));
+          if (u < C::V_UNITS && key >= kv_begin && key < kv_end) vpid[i][j] = pt_row[key / page_size];
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::K_PER_T; ++i) {
       const int u = i * C::NT + tid;
@@ -214,7 +259,7 @@ rpa_prefill_kernel(KernelArgs args) {
       if (u < C::K_UNITS) {
         const int key = k0 + u / (D / 8);
         const int c = u % (D / 8);
-        if (key < kv_end) kreg[i] = load16(args.k + kv_offset(pt_row, key, args.page_size, hkv, g, D) + c * 8);
+        if (key >= kv_begin && key < kv_end) kreg[i] = load16(kbase + kv_row(key, kpid[i]) + c * 8);
       }
     }
 #pragma unroll
@@ -228,8 +273,8 @@ rpa_prefill_kernel(KernelArgs args) {
       for (int j = 0; j < 8; ++j) {
         vreg[i][j] = u32x4{0, 0, 0, 0};
         const int key = k0 + t * 32 + ((j < 4) ? (qd * 4 + j) : (16 + qd * 4 + j - 4));
-        if (u < C::V_UNITS && key < kv_end)
-          vreg[i][j] = load16(args.v + kv_offset(pt_row, key, args.page_size, hkv, g, D) + c * 8);
+        if (u < C::V_UNITS && key >= kv_begin && key < kv_end)
+          vreg[i][j] = load16(vbase + kv_row(key, vpid[i][j]) + c * 8);
       }
     }
   };
@@ -261,10 +306,10 @@ rpa_prefill_kernel(KernelArgs args) {
     }
   };
 
-  if (n_tiles > 0) load_tile(kv_begin);
+  if (n_tiles > 0) load_tile(tile0);
 
   for (int tile = 0; tile < n_tiles; ++tile) {
-    const int k0 = kv_begin + tile * BN;
+    const int k0 = tile0 + tile * BN;
     __syncthreads();
     store_tile();
     __syncthreads();
@@ -287,7 +332,7 @@ rpa_prefill_kernel(KernelArgs args) {
     }
 
     // ---- mask + online softmax (fp32, base 2) ----
-    const bool full = (k0 + BN <= kv_end) && (k0 + BN - 1 <= pos_min) &&
+    const bool full = (k0 >= kv_begin) && (k0 + BN <= kv_end) && (k0 + BN - 1 <= pos_min) &&
                       (window <= 0 || k0 > pos_max - window);
     u32x4 pf[BN / 32][NB];
 #pragma unroll
@@ -360,17 +405,18 @@ rpa_prefill_kernel(KernelArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// Split merge: out = sum_i 2^(lse_i - M) O_i / sum_i 2^(lse_i - M).
-// One call merges one group; `tid`/`nthreads` stride over rows x D.
+// Split merge: out = sum_i 2^(lse_i - M) O_i / sum_i 2^(lse_i - M), M = max_i lse_i.
+// One workgroup per group; each thread owns one 4-float column of one row.
 // ---------------------------------------------------------------------------
 template <int D>
-RPA_DEV void merge_group(const KernelArgs& args, const rpa_work_item& grp, int tid, int nthreads) {
+__global__ void __launch_bounds__(256) rpa_merge_kernel(KernelArgs args) {
+  const rpa_work_item grp = args.groups[blockIdx.x];
+  constexpr int C4 = D / 4;
   const int rows = grp.q_count * args.group;
   const int n = grp.num_splits;
   const float* lse = args.partial_lse + static_cast<int64_t>(grp.partial_base) * 16;
   const float* po = args.partial_o + static_cast<int64_t>(grp.partial_base) * 16 * D;
-  constexpr int C4 = D / 4;
-  for (int idx = tid; idx < rows * C4; idx += nthreads) {
+  for (int idx = threadIdx.x; idx < rows * C4; idx += blockDim.x) {
     const int r = idx / C4;
     const int c = idx - r * C4;
     float mx = kNegInf;
@@ -378,14 +424,14 @@ RPA_DEV void merge_group(const KernelArgs& args, const rpa_work_item& grp, int t
     const float base = (mx == kNegInf) ? 0.f : mx;
     float wsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int i = 0; i < n; ++i) {
       const float w = fast_exp2(lse[i * 16 + r] - base);
-      wsum += w;
       const f32x4 v = *reinterpret_cast<const f32x4*>(po + (static_cast<int64_t>(i) * 16 + r) * D + c * 4);
+      wsum += w;
       acc += w * v;
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    acc *= inv;
+    acc *= wsum > 0.f ? 1.f / wsum : 0.f;
     const int tk = r / args.group;
     const int hh = r - tk * args.group;
     uint16_t* dst = args.out + (static_cast<int64_t>(grp.q_start + tk) * args.num_q_heads +
@@ -394,39 +440,36 @@ RPA_DEV void merge_group(const KernelArgs& args, const rpa_work_item& grp, int t
   }
 }
 
-template <int D>
-__global__ void __launch_bounds__(256) rpa_merge_kernel(KernelArgs args) {
-  const rpa_work_item grp = args.groups[blockIdx.x];
-  merge_group<D>(args, grp, threadIdx.x, blockDim.x);
-}
-
 // ---------------------------------------------------------------------------
 // Decode: rows = q_count * G <= 16; NW waves take 32-key chunks round robin.
+// Every wave issues all loads of a chunk before touching any of them; the
+// waves are combined in a fixed order through LDS (bitwise reproducible).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NW>
 struct DecodeCfg {
-  static constexpr int NW = 4;
   static constexpr int NT = NW * 64;
   static constexpr int NCH = D / 8;                   // 16-byte chunks per key row
   static constexpr int NU = (NCH + 15) / 16;          // V chunk rounds per lane
-  static constexpr int LDS_O = NW * 16 * D;           // floats
+  static constexpr int OSTRIDE = D + 4;               // floats per LDS row (padded)
+  static constexpr int LDS_O = (NW / 2) * 16 * OSTRIDE; // tree-combine slots
   static constexpr int LDS_BYTES = LDS_O * 4 + NW * 16 * 2 * 4;
 };
 
-template <int D>
-__global__ void __launch_bounds__(256)
+// Second launch bound: waves per SIMD to fit (two, so a compute unit holds two
+// workgroups of 4 waves; one for D = 512 whose fragments need the full file).
+template <int D, int NW, bool UNI>
+__global__ void __launch_bounds__(NW * 64, D >= 512 ? 1 : 2)
 rpa_decode_kernel(KernelArgs args) {
-  using C = DecodeCfg<D>;
+  using C = DecodeCfg<D, NW>;
   extern __shared__ __attribute__((aligned(16))) float dsm[];
-  float* lds_o = dsm;                     // [NW][16][D]
+  float* lds_o = dsm;                     // [NW/2][16][OSTRIDE]
   float* lds_m = dsm + C::LDS_O;          // [NW][16]
-  float* lds_l = lds_m + C::NW * 16;      // [NW][16]
-  __shared__ int s_last;
+  float* lds_l = lds_m + NW * 16;         // [NW][16]
 
   const rpa_work_item it = args.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int ln = lane & 15;
   const int lq = lane >> 4;
   const int hq = args.num_q_heads;
@@ -434,23 +477,27 @@ rpa_decode_kernel(KernelArgs args) {
   const int G = args.group;
   const int g = it.kv_head;
   const int rows = it.q_count * G;
-  const int32_t* pt_row = args.page_table + static_cast<int64_t>(it.seq) * args.max_pages;
+  const int32_t* __restrict__ pt_row = args.page_table + static_cast<int64_t>(it.seq) * args.max_pages;
+  const uint16_t* __restrict__ kbase = args.k;
+  const uint16_t* __restrict__ vbase = args.v;
+  const int page_size = args.page_size;
+  const int64_t row_stride = static_cast<int64_t>(hkv) * D;
   const int kv_begin = it.kv_begin;
   const int kv_end = it.kv_end;
   const int window = args.window;
   const float sl2 = args.scale_log2;
 
-  // row n = ln: token ln / G, head ln % G
+  // query row n = ln: token ln / G, head ln % G
   const int tk = ln / G;
   const int hh = ln - tk * G;
   const bool row_ok = ln < rows;
   const int pos = it.q_pos0 + tk;
-  const int64_t row_off = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
+  const int64_t q_off = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
 
   u32x4 qf[D / 32];
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk)
-    qf[kk] = row_ok ? load16(args.q + row_off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
+    qf[kk] = row_ok ? load16(args.q + q_off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
 
   f32x4 o[C::NU][8];
 #pragma unroll
@@ -459,31 +506,60 @@ rpa_decode_kernel(KernelArgs args) {
     for (int e = 0; e < 8; ++e) o[u][e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  const int n_chunks = (kv_end - kv_begin + 31) / 32;
-  for (int ch = wave; ch < n_chunks; ch += C::NW) {
-    const int k0 = kv_begin + ch * 32;
-    // K rows k0 + 16*kb + ln, d = 32*kk + 8*lq (A operand of S^T = K Q^T)
+  // 32-key chunks aligned to 32 keys; with UNI a chunk never crosses a page.
+  const int chunk0 = (kv_begin / 32) * 32;
+  const int n_chunks = (kv_end - chunk0 + 31) / 32;
+  for (int ch = wave; ch < n_chunks; ch += NW) {
+    const int k0 = chunk0 + ch * 32;
+    int64_t ubase = 0;
+    if constexpr (UNI) {
+      const int pidx = k0 / page_size;
+      const int64_t page = uniform_load(pt_row, pidx);
+      ubase = ((page * page_size + (k0 - pidx * page_size)) * hkv + g) * D;
+    }
+    // keys of this lane: K rows k0 + 16*kb + ln; V rows k0 + 4*lq + j and k0 + 16 + 4*lq + j
+    int kkey[2], vkey[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) kkey[kb] = k0 + kb * 16 + ln;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vkey[j] = k0 + ((j < 4) ? (lq * 4 + j) : (16 + lq * 4 + j - 4));
+    int kpid[2] = {0, 0}, vpid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (!UNI) {   // every page id first, then the K/V loads
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kkey[kb] >= kv_begin && kkey[kb] < kv_end) kpid[kb] = pt_row[kkey[kb] / page_size];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (vkey[j] >= kv_begin && vkey[j] < kv_end) vpid[j] = pt_row[vkey[j] / page_size];
+    }
+    auto kv_row = [&](int key, int pid) -> int64_t {
+      if constexpr (UNI) {
+        return ubase + static_cast<int64_t>(key - k0) * row_stride;
+      } else {
+        const int slot = key - (key / page_size) * page_size;
+        return ((static_cast<int64_t>(pid) * page_size + slot) * hkv + g) * D;
+      }
+    };
+    // K rows (A operand of S^T = K Q^T): d = 32*kk + 8*lq
     u32x4 kf[2][D / 32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = k0 + kb * 16 + ln;
-      const bool ok = key < kv_end;
-      const int64_t off = ok ? kv_offset(pt_row, key, args.page_size, hkv, g, D) : 0;
+      const bool ok = kkey[kb] >= kv_begin && kkey[kb] < kv_end;
+      const int64_t off = kv_row(kkey[kb], kpid[kb]);
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk)
-        kf[kb][kk] = ok ? load16(args.k + off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
+        kf[kb][kk] = ok ? load16(kbase + off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
     }
-    // V rows: keys k0 + 4*lq + j and k0 + 16 + 4*lq + j at chunk 16*u + ln
+    // V rows at 16-byte chunk 16*u + ln
     u32x4 vf[C::NU][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int key = k0 + ((j < 4) ? (lq * 4 + j) : (16 + lq * 4 + j - 4));
-      const bool ok = key < kv_end;
-      const int64_t off = ok ? kv_offset(pt_row, key, args.page_size, hkv, g, D) : 0;
+      const bool ok = vkey[j] >= kv_begin && vkey[j] < kv_end;
+      const int64_t off = kv_row(vkey[j], vpid[j]);
 #pragma unroll
       for (int u = 0; u < C::NU; ++u) {
         const int c = u * 16 + ln;
-        vf[u][j] = (ok && c < C::NCH) ? load16(args.v + off + c * 8) : u32x4{0, 0, 0, 0};
+        vf[u][j] = (ok && c < C::NCH) ? load16(vbase + off + c * 8) : u32x4{0, 0, 0, 0};
       }
     }
 
@@ -533,103 +609,133 @@ rpa_decode_kernel(KernelArgs args) {
     }
   }
 
-  // ---- combine the waves through LDS ----
+  // ---- combine the waves: common max, per-wave weight, fixed-order tree ----
   const float l_wave = xor_sum(l_run);
   if (lq == 0) {
     lds_m[wave * 16 + ln] = m_run;
     lds_l[wave * 16 + ln] = l_wave;
   }
-  // lane (lq, ln) holds O[row ln][d = 8*(16u + 4lq + j) + e]
-#pragma unroll
-  for (int u = 0; u < C::NU; ++u) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = u * 16 + lq * 4 + j;
-      if (c < C::NCH) {
-        float* dst = lds_o + (wave * 16 + ln) * D + c * 8;
-        *reinterpret_cast<f32x4*>(dst) = f32x4{o[u][0][j], o[u][1][j], o[u][2][j], o[u][3][j]};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[u][4][j], o[u][5][j], o[u][6][j], o[u][7][j]};
-      }
-    }
-  }
   __syncthreads();
+  float mx = kNegInf;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_m[w * 16 + ln]);
+  const float base = (mx == kNegInf) ? 0.f : mx;
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) lsum += fast_exp2(lds_m[w * 16 + ln] - base) * lds_l[w * 16 + ln];
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const float wscale = fast_exp2(m_run - base) * inv;   // this wave's share, normalised
+#pragma unroll
+  for (int u = 0; u < C::NU; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[u][e] *= wscale;
+  // lane (lq, ln) holds O[row ln][d = 8*(16u + 4lq + j) + e]; slot rows are padded by 4 floats
+  auto slot_ptr = [&](int slot, int u, int j) {
+    return reinterpret_cast<f32x4*>(lds_o + (slot * 16 + ln) * C::OSTRIDE + (u * 16 + lq * 4 + j) * 8);
+  };
+#pragma unroll
+  for (int half = NW / 2; half >= 1; half /= 2) {
+    if (wave >= half && wave < 2 * half && row_ok) {
+#pragma unroll
+      for (int u = 0; u < C::NU; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (u * 16 + lq * 4 + j < C::NCH) {
+            f32x4* dst = slot_ptr(wave - half, u, j);
+            dst[0] = f32x4{o[u][0][j], o[u][1][j], o[u][2][j], o[u][3][j]};
+            dst[1] = f32x4{o[u][4][j], o[u][5][j], o[u][6][j], o[u][7][j]};
+          }
+    }
+    __syncthreads();
+    if (wave < half && row_ok) {
+#pragma unroll
+      for (int u = 0; u < C::NU; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (u * 16 + lq * 4 + j < C::NCH) {
+            const f32x4* src = slot_ptr(wave, u, j);
+            const f32x4 lo = src[0], hi = src[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              o[u][e][j] += lo[e];
+              o[u][4 + e][j] += hi[e];
+            }
+          }
+    }
+    if (half > 1) __syncthreads();
+  }
+  if (wave != 0 || !row_ok) return;
 
+  // ---- wave 0 writes the output row (or the split's partial) from registers ----
   const bool split = it.split_group >= 0;
-  const int64_t slot = static_cast<int64_t>(it.partial_base) + it.split_index;
-  constexpr int C4 = D / 4;
-  for (int idx = tid; idx < rows * C4; idx += C::NT) {
-    const int r = idx / C4;
-    const int c = idx - r * C4;
-    float mx = kNegInf;
+  if (!split) {
+    uint16_t* dst = args.out + q_off;
 #pragma unroll
-    for (int w = 0; w < C::NW; ++w) mx = fmaxf(mx, lds_m[w * 16 + r]);
-    const float base = (mx == kNegInf) ? 0.f : mx;
-    float lsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < C::NU; ++u)
 #pragma unroll
-    for (int w = 0; w < C::NW; ++w) {
-      const float wt = fast_exp2(lds_m[w * 16 + r] - base);
-      lsum += wt * lds_l[w * 16 + r];
-      acc += wt * *reinterpret_cast<const f32x4*>(lds_o + (w * 16 + r) * D + c * 4);
-    }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    acc *= inv;
-    if (!split) {
-      const int rtk = r / G;
-      const int rhh = r - rtk * G;
-      uint16_t* dst = args.out + (static_cast<int64_t>(it.q_start + rtk) * hq + g * G + rhh) * D + c * 4;
-      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    } else {
-      *reinterpret_cast<f32x4*>(args.partial_o + (slot * 16 + r) * D + c * 4) = acc;
-      if (c == 0) args.partial_lse[slot * 16 + r] = (lsum > 0.f) ? base + __builtin_log2f(lsum) : kNegInf;
-    }
+      for (int j = 0; j < 4; ++j) {
+        const int c = u * 16 + lq * 4 + j;
+        if (c < C::NCH)
+          *reinterpret_cast<u32x4*>(dst + c * 8) =
+              u32x4{pack_bf16x2(o[u][0][j], o[u][1][j]), pack_bf16x2(o[u][2][j], o[u][3][j]),
+                    pack_bf16x2(o[u][4][j], o[u][5][j]), pack_bf16x2(o[u][6][j], o[u][7][j])};
+      }
+  } else {
+    const int64_t slot = static_cast<int64_t>(it.partial_base) + it.split_index;
+    float* dst = args.partial_o + (slot * 16 + ln) * D;
+#pragma unroll
+    for (int u = 0; u < C::NU; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = u * 16 + lq * 4 + j;
+        if (c < C::NCH) {
+          *reinterpret_cast<f32x4*>(dst + c * 8) = f32x4{o[u][0][j], o[u][1][j], o[u][2][j], o[u][3][j]};
+          *reinterpret_cast<f32x4*>(dst + c * 8 + 4) = f32x4{o[u][4][j], o[u][5][j], o[u][6][j], o[u][7][j]};
+        }
+      }
+    if (lq == 0) args.partial_lse[slot * 16 + ln] = (lsum > 0.f) ? base + __builtin_log2f(lsum) : kNegInf;
   }
-
-  if (!split || !args.fused_merge) return;
-  // Last split of the group to finish merges all of them.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(args.counters + it.split_group, 1);
-    s_last = (prev == it.num_splits - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  merge_group<D>(args, args.groups[it.split_group], tid, C::NT);
-  if (tid == 0) atomicExch(args.counters + it.split_group, 0);
 }
 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int D, int NB, int NW, int BN>
-static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, hipStream_t stream) {
+template <int D, int NB, int NW, int BN, bool UNI>
+static hipError_t launch_prefill_u(const KernelArgs& a, int n_items, hipStream_t stream) {
   using C = PrefillCfg<D, NB, NW, BN>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_prefill_kernel<D, NB, NW, BN>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_prefill_kernel<D, NB, NW, BN, UNI>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((rpa_prefill_kernel<D, NB, NW, BN>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
+  hipLaunchKernelGGL((rpa_prefill_kernel<D, NB, NW, BN, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
                      stream, a);
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_decode_t(const KernelArgs& a, int n_items, hipStream_t stream) {
-  using C = DecodeCfg<D>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_decode_kernel<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((rpa_decode_kernel<D>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream, a);
+template <int D, int NB, int NW, int BN>
+static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, hipStream_t stream) {
+  if (a.page_size % BN == 0) return launch_prefill_u<D, NB, NW, BN, true>(a, n_items, stream);
+  return launch_prefill_u<D, NB, NW, BN, false>(a, n_items, stream);
+}
+
+template <int D, int NW, bool UNI>
+static hipError_t launch_decode_u(const KernelArgs& a, int n_items, hipStream_t stream) {
+  using C = DecodeCfg<D, NW>;
+  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream, a);
   return hipGetLastError();
+}
+
+// Eight-wave workgroups are not used for D = 512: two waves per SIMD cannot
+// hold its fragments.
+template <int D>
+static hipError_t launch_decode_t(const KernelArgs& a, int n_items, int waves, hipStream_t stream) {
+  const bool uni = a.page_size % 32 == 0;
+  if (waves == 8 && D < 512) return uni ? launch_decode_u<D, 8, true>(a, n_items, stream)
+                             : launch_decode_u<D, 8, false>(a, n_items, stream);
+  return uni ? launch_decode_u<D, 4, true>(a, n_items, stream) : launch_decode_u<D, 4, false>(a, n_items, stream);
 }
 
 template <int D>
@@ -661,7 +767,6 @@ static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
   a.groups = l.groups;
   a.partial_o = l.partial_o;
   a.partial_lse = l.partial_lse;
-  a.counters = l.counters;
   a.num_q_heads = l.num_q_heads;
   a.num_kv_heads = l.num_kv_heads;
   a.group = l.num_q_heads / l.num_kv_heads;
@@ -669,7 +774,6 @@ static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
   a.max_pages = l.max_pages;
   a.window = l.window;
   a.scale_log2 = l.scale_log2;
-  a.fused_merge = l.fused_merge;
   return a;
 }
 
@@ -690,11 +794,12 @@ hipError_t launch_decode(const LaunchArgs& l, const rpa_work_item* items, int n_
   if (n_items <= 0) return hipSuccess;
   const KernelArgs a = make_args(l, items);
   hipStream_t s = static_cast<hipStream_t>(l.stream);
+  const int w = l.decode_waves;
   switch (l.head_dim) {
-    case 64: return launch_decode_t<64>(a, n_items, s);
-    case 128: return launch_decode_t<128>(a, n_items, s);
-    case 256: return launch_decode_t<256>(a, n_items, s);
-    case 512: return launch_decode_t<512>(a, n_items, s);
+    case 64: return launch_decode_t<64>(a, n_items, w, s);
+    case 128: return launch_decode_t<128>(a, n_items, w, s);
+    case 256: return launch_decode_t<256>(a, n_items, w, s);
+    case 512: return launch_decode_t<512>(a, n_items, w, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -17,7 +17,6 @@ struct LaunchArgs {
   const rpa_work_item* groups;  // device
   float* partial_o;             // device [slots][16][D]
   float* partial_lse;           // device [slots][16]
-  int32_t* counters;            // device, one per split group
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;
@@ -25,7 +24,7 @@ struct LaunchArgs {
   int32_t max_pages;
   int32_t window;
   float scale_log2;
-  int32_t fused_merge;
+  int32_t decode_waves;  // waves per decode workgroup: 4 or 8
   void* stream;
 };
 

@@ -89,9 +89,10 @@ VARIANTS = [
     ("split64", {R.RPA_OPT_DECODE_SPLIT_KEYS: 64}),
     ("split96", {R.RPA_OPT_DECODE_SPLIT_KEYS: 96}),
     ("split_none", {R.RPA_OPT_DECODE_SPLIT_KEYS: 1 << 20}),
-    ("merge_kernel", {R.RPA_OPT_MERGE: 2}),
-    ("merge_kernel_split32", {R.RPA_OPT_MERGE: 2, R.RPA_OPT_DECODE_SPLIT_KEYS: 32}),
     ("decode_rows8", {R.RPA_OPT_DECODE_MAX_ROWS: 8}),
+    ("decode_waves8", {R.RPA_OPT_DECODE_WAVES: 8}),
+    ("decode_waves8_split32", {R.RPA_OPT_DECODE_WAVES: 8, R.RPA_OPT_DECODE_SPLIT_KEYS: 32}),
+    ("decode_waves8_split_none", {R.RPA_OPT_DECODE_WAVES: 8, R.RPA_OPT_DECODE_SPLIT_KEYS: 1 << 20}),
 ]
 
 

@@ -1,0 +1,143 @@
+"""Host planner (work-list builder) properties, through rpa_plan on the CPU.
+
+Every (token, query head) must be covered by exactly one item or one split
+group, whose key ranges are exactly the keys that token can see (checked
+against the oracle's visibility rule by brute force); splits partition their
+group's range; lists are deterministic and longest-first.
+"""
+import numpy as np
+import pytest
+
+import oracle.rpa_oracle as ora
+import rpa_workloads as wl
+from ragged_paged_attention_forward_amd import (RPA_OPT_DECODE_MAX_ROWS, RPA_OPT_DECODE_SPLIT_KEYS,
+                                                RPA_OPT_PATH, RaggedPagedAttention, metrics)
+
+
+def plan_for(w, options=()):
+    attn = RaggedPagedAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                                max(1, w.num_seqs), w.max_pages_per_seq, max(1, w.total_q))
+    for k, v in options:
+        attn.set_option(k, v)
+    cu = np.concatenate([[0], np.cumsum([q for q, _ in w.seqs])]).astype(np.int32)
+    kv = np.array([k for _, k in w.seqs], dtype=np.int32)
+    info, items = attn.plan(cu, kv, w.window)
+    attn.close()
+    return cu, kv, info, items
+
+
+def check_plan(w, cu, kv, info, items):
+    g_ratio = w.num_q_heads // w.num_kv_heads
+    assert info["num_prefill_items"] + info["num_decode_items"] == len(items)
+    assert info["visible_pairs"] == metrics.visible_pairs(w.seqs, w.window)
+    cover = {}   # (token, kv_head) -> list of items
+    for it in items:
+        s, g = it["seq"], it["kv_head"]
+        assert 0 <= g < w.num_kv_heads
+        assert cu[s] <= it["q_start"] and it["q_start"] + it["q_count"] <= cu[s + 1]
+        assert it["q_count"] >= 1
+        assert 0 <= it["kv_begin"] < it["kv_end"] <= kv[s]
+        assert it["q_pos0"] == kv[s] - (cu[s + 1] - cu[s]) + (it["q_start"] - cu[s])
+        if it["kind"] == 1:
+            assert it["q_count"] * g_ratio <= 16
+        else:
+            assert it["split_group"] == -1
+        for t in range(it["q_start"], it["q_start"] + it["q_count"]):
+            cover.setdefault((t, g), []).append(it)
+    for s in range(len(kv)):
+        q_len = cu[s + 1] - cu[s]
+        vis = ora.visible(q_len, kv[s], w.window)
+        for r in range(q_len):
+            want = set(np.nonzero(vis[r])[0].tolist())
+            for g in range(w.num_kv_heads):
+                its = cover[(cu[s] + r, g)]
+                groups = {it["split_group"] for it in its}
+                assert len(groups) == 1
+                if groups == {-1}:
+                    assert len(its) == 1
+                else:
+                    n = its[0]["num_splits"]
+                    assert len(its) == n
+                    assert sorted(it["split_index"] for it in its) == list(range(n))
+                    assert len({it["partial_base"] for it in its}) == 1
+                # union of the item key ranges, no overlap between splits
+                keys = []
+                for it in sorted(its, key=lambda x: x["kv_begin"]):
+                    keys.extend(range(it["kv_begin"], it["kv_end"]))
+                assert len(keys) == len(set(keys))
+                keys = set(keys)
+                assert want <= keys
+                # tight: the item range is the union over the item's rows
+                lo = min(it["kv_begin"] for it in its)
+                hi = max(it["kv_end"] for it in its)
+                rows = range(its[0]["q_start"] - cu[s], its[0]["q_start"] - cu[s] + its[0]["q_count"])
+                union = np.nonzero(vis[list(rows)].any(axis=0))[0]
+                assert lo == union.min() and hi == union.max() + 1
+
+
+WORKLOADS = [
+    wl.tiny(), wl.decode(), wl.swa_prefill(tokens=700), wl.global_prefill(tokens=300),
+    wl.custom([(2, 300), (2, 2), (1, 129), (2, 1000), (1, 1), (0, 5), (40, 170)], 8, 1, 256, 128, 0, 1),
+    wl.custom([(2, 300), (2, 2), (1, 129), (2, 1000), (1, 1), (0, 5), (40, 170)], 8, 1, 256, 128, 100, 1),
+    wl.custom([(5, 77), (1, 1), (130, 130), (3, 513)], 16, 1, 128, 16, 64, 2),
+    wl.custom([(5, 77), (1, 1), (130, 130), (3, 513)], 32, 1, 128, 16, 0, 3),
+    wl.custom([(9, 9), (1, 300)], 12, 4, 64, 1, 1, 4),
+]
+
+
+@pytest.mark.parametrize("w", WORKLOADS, ids=lambda w: w.name + f"_w{w.window}_g{w.num_q_heads // w.num_kv_heads}")
+def test_plan_covers_exactly_the_visible_keys(w):
+    cu, kv, info, items = plan_for(w)
+    check_plan(w, cu, kv, info, items)
+
+
+@pytest.mark.parametrize("options", [
+    [(RPA_OPT_PATH, 1)], [(RPA_OPT_PATH, 2)], [(RPA_OPT_DECODE_SPLIT_KEYS, 32)],
+    [(RPA_OPT_DECODE_SPLIT_KEYS, 100)], [(RPA_OPT_DECODE_SPLIT_KEYS, 1 << 20)],
+    [(RPA_OPT_DECODE_MAX_ROWS, 8)], [(RPA_OPT_DECODE_MAX_ROWS, 1)],
+])
+def test_plan_options_keep_coverage(options):
+    w = WORKLOADS[5]
+    cu, kv, info, items = plan_for(w, options)
+    check_plan(w, cu, kv, info, items)
+    opts = dict(options)
+    if opts.get(RPA_OPT_PATH) == 1:
+        assert info["num_decode_items"] == 0
+    if RPA_OPT_DECODE_SPLIT_KEYS in opts:
+        split = -(-opts[RPA_OPT_DECODE_SPLIT_KEYS] // 32) * 32
+        assert info["decode_split_keys"] == split
+        for it in items:
+            if it["kind"] == 1:
+                assert it["kv_end"] - it["kv_begin"] <= split
+
+
+def test_decode_selection_rule():
+    # q_len * G <= 16 -> decode kernel
+    w = wl.custom([(1, 50), (2, 50), (3, 50)], 8, 1, 256, 128, 0, 9)
+    cu, kv, info, items = plan_for(w)
+    kinds = {it["seq"]: it["kind"] for it in items}
+    assert kinds == {0: 1, 1: 1, 2: 0}
+
+
+def test_prefill_tile_rows_and_longest_first():
+    w = wl.swa_prefill(tokens=2000)
+    cu, kv, info, items = plan_for(w)
+    g_ratio = w.num_q_heads // w.num_kv_heads
+    assert all(it["q_count"] * g_ratio <= info["prefill_rows"] for it in items)
+    cost = [(it["kv_end"] - it["kv_begin"]) * it["q_count"] for it in items]
+    assert cost == sorted(cost, reverse=True)
+
+
+def test_auto_split_fills_the_chip():
+    w = wl.decode()
+    cu, kv, info, items = plan_for(w)
+    assert info["num_decode_items"] >= 256       # more workgroups than compute units
+    assert info["decode_split_keys"] % 128 == 0
+    assert info["num_partials"] == sum(it["split_group"] >= 0 for it in items)
+
+
+def test_plan_is_deterministic():
+    w = wl.mixed(window=1024)
+    a = plan_for(w)
+    b = plan_for(w)
+    assert a[2] == b[2] and a[3] == b[3]
