@@ -85,7 +85,8 @@ int rpa_create(const rpa_config* cfg, rpa_ctx** out_ctx);
  *              must already be in their pages
  *   num_seqs   0 <= num_seqs <= max_num_seqs
  *   window     0: full causal; W > 0: keys p - W + 1 .. p; negative is an error
- *   scale      finite multiplier of q.k before the softmax (usually 1/sqrt(D))
+ *   scale      finite positive multiplier of q.k before the softmax (usually
+ *              1/sqrt(D)); zero, negative or non-finite is an error
  *   out        device, bf16 [T, Hq, D]; must not overlap q
  *   stream     a hipStream_t (NULL = the null stream)
  *

@@ -81,6 +81,17 @@ RPA_DEV void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
 
 RPA_DEV u32x4 load16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Buffer resource over `bytes` bytes from `base` (gfx9 descriptor: 32-bit data
+// format, raw addressing).  Loads at offsets at or past `bytes` -- including
+// negative offsets, which wrap to huge unsigned values -- return zero.
+RPA_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                          static_cast<int>(bytes), 0x00020000);
+}
+RPA_DEV u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
+}
+
 // Wave-uniform load through the constant address space, so it becomes a
 // scalar load that does not wait behind the vector loads in flight.
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
@@ -112,47 +123,97 @@ RPA_DEV bool key_visible(int key, int pos, int kv_begin, int kv_end, int window)
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: NW waves x NB row blocks of 16 rows; BN keys per LDS tile.
+// Prefill: NW waves x NB blocks of 32 query rows; BN keys per LDS tile;
+// v_mfma_f32_32x32x16_bf16 for both products.
+//
+// K and V tiles go straight from HBM into LDS (buffer loads with an LDS
+// destination: no staging registers), double buffered, in their natural
+// [key][d] layout with a per-row XOR swizzle of the 16-byte chunks.
+//
+// S^T block (32 keys x 32 rows): lane (lq2 = lane/32, n = lane%32) holds keys
+// 8b + 4*lq2 + t (b, t in 0..3) of row n in accumulator slot 4b + t.  The PV
+// product consumes a 32-key block as two 16-key MFMAs h = 0, 1 whose k-slot
+// 8*lq2 + i holds key 16h + 8*(i/4) + 4*lq2 + i%4 -- accumulator slots
+// 8h .. 8h+7 of the same lane, so P never moves between lanes.  The V^T
+// operand of those MFMAs is read with two transposing LDS reads
+// (ds_read_b64_tr_b16): within a 16-lane group, lane i receives element i&3
+// of the 8-byte chunk addressed by lane 4j + (i>>2) as its element j, so when
+// lane L addresses key row r0 + (L>>2), columns d0 + 4*(L&3) .. +3, lane i
+// gets keys r0 .. r0+3 of column d0 + i.
 // ---------------------------------------------------------------------------
-template <int D, int NB, int NW, int BN>
-struct PrefillCfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int KSTRIDE = D + 8;            // bf16 elements per K row in LDS (padded)
-  static constexpr int NCHUNK = BN / 8;            // 16-byte chunks per V^T row
-  static constexpr int K_UNITS = BN * (D / 8);     // 16-byte K pieces per tile
-  static constexpr int K_PER_T = (K_UNITS + NT - 1) / NT;
-  static constexpr int V_UNITS = (BN / 32) * 4 * (D / 8);  // 8-key x 16-byte V pieces
-  static constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
-  static constexpr int LDS_K = BN * KSTRIDE;       // bf16 elements
-  static constexpr int LDS_V = D * BN;
-  static constexpr int LDS_BYTES = (LDS_K + LDS_V) * 2;
-  static_assert(BN % 32 == 0, "BN must be a multiple of 32");
-  static_assert(D % 32 == 0, "D must be a multiple of 32");
-};
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef const void __attribute__((address_space(1)))* global_cptr;
+typedef void __attribute__((address_space(3)))* lds_ptr;
+typedef v4i16 __attribute__((address_space(3)))* lds_v4i16_ptr;
 
-// Swizzled 16-byte chunk of V^T row r: spreads both the transposed writes
-// (rows 8 apart) and the MFMA operand reads (consecutive rows) over the banks.
-template <int BN>
-RPA_DEV int vt_chunk(int r, int chunk) {
-  constexpr int NC = BN / 8;
-  const int sw = (NC >= 8) ? (r ^ (r >> 3)) : ((r >> 1) ^ (r >> 3));
-  return chunk ^ (sw & (NC - 1));
+RPA_DEV f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int D, int NB, int NW, int BN, bool UNI>
-__global__ void __launch_bounds__(NW * 64)
+// 16 bytes per lane from a buffer straight into LDS at dst + 16 * lane.
+RPA_DEV void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst, int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst), 16, byte_off, 0, 0, 0);
+}
+// 16 bytes per lane from a global address straight into LDS at dst + 16 * lane.
+RPA_DEV void global_load_lds16(const char* src, char* dst) {
+  __builtin_amdgcn_global_load_lds((global_cptr)(src), (lds_ptr)(dst), 16, 0, 0);
+}
+// Transposing 8-byte LDS read (see the layout note above).
+RPA_DEV u32x2 lds_read_tr16(const char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p)));
+}
+
+// vmcnt(0) with the other counters left alone (gfx9 s_waitcnt encoding).
+RPA_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int D, int BN, int NW, int NB>
+struct PrefillCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int ROWS = NW * NB * 32;          // query rows per workgroup
+  static constexpr int ROW_B = D * 2;                // bytes per key row
+  static constexpr int RPI = ROW_B >= 1024 ? 1 : 1024 / ROW_B;   // key rows per 1 KB block
+  static constexpr int BLOCKS = BN * ROW_B / 1024;   // 1 KB blocks per K or V tile
+  // LDS layout of a tile: 1 KB blocks (one direct load each) followed by a
+  // pad; inside a block, row s sits at s*ROW_B with its 16-byte chunk c at
+  // position c ^ x(s).  K and V use different pads / XORs, chosen so that the
+  // K operand reads (16 consecutive rows, one chunk) and the transposing V
+  // reads (4 consecutive rows, two chunks) hit distinct banks, and so that the
+  // chunk index of an operand stays additive in the loop counter (the XOR
+  // only touches bit 0 for K and bits 0-1 for V).
+  static constexpr int PAD_K = RPI == 1 ? 16 : RPI == 2 ? 32 : 64;
+  static constexpr int PAD_V = RPI == 1 ? 32 : 64;
+  static constexpr int BLK_K = 1024 + PAD_K;
+  static constexpr int BLK_V = 1024 + PAD_V;
+  static constexpr int TILE_K = BLOCKS * BLK_K;
+  static constexpr int TILE_V = BLOCKS * BLK_V;
+  static constexpr int STAGE_B = TILE_K + TILE_V;
+  static constexpr int LDS_BYTES = 2 * STAGE_B;      // double buffered
+  static constexpr int LOADS = BLOCKS / NW;          // 1 KB direct loads per wave per tensor
+  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(BLOCKS % NW == 0, "tile must split into 1 KB loads per wave");
+  static_assert(16 % RPI == 0, "16-key steps must cover whole blocks");
+};
+
+RPA_DEV int xor_k(int s) { return s & 1; }
+RPA_DEV int xor_v(int s) { return (s & 1) * 2; }
+
+template <int D, int BN, int NW, int NB, bool UNI>
+__global__ void __launch_bounds__(NW * 64, 1)
 rpa_prefill_kernel(KernelArgs args) {
-  using C = PrefillCfg<D, NB, NW, BN>;
+  using C = PrefillCfg<D, BN, NW, NB>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* ks = smem;                  // [BN][KSTRIDE]
-  uint16_t* vt = smem + C::LDS_K;       // [D][BN], swizzled 16-byte chunks
+  char* lds = reinterpret_cast<char*>(smem);
 
   const rpa_work_item it = args.items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int ln = lane & 15;   // MFMA column: query row within a block; or key/d row
-  const int lq = lane >> 4;   // lane quad 0..3
+  const int n32 = lane & 31;   // MFMA column (query row) / A-operand row (key or d)
+  const int lq2 = lane >> 5;   // lane half 0..1
+  const int l16 = lane & 15;   // lane within a 16-lane group
+  const int grp = lane >> 4;   // 16-lane group 0..3
 
   const int hq = args.num_q_heads;
   const int hkv = args.num_kv_heads;
@@ -162,32 +223,38 @@ rpa_prefill_kernel(KernelArgs args) {
   const uint16_t* __restrict__ kbase = args.k;
   const uint16_t* __restrict__ vbase = args.v;
   const int page_size = args.page_size;
-  const int64_t row_stride = static_cast<int64_t>(hkv) * D;  // elements between slots of a page
+  const int row_bytes = hkv * D * 2;   // bytes between consecutive key rows of a page
 
-  // ---- per-lane rows, Q fragments (B operand of S^T = K Q^T) ----
+  // ---- rows of this lane, Q fragments (B operand of S^T = K Q^T) ----
   int row_pos[NB];
   bool row_ok[NB];
-  int64_t row_off[NB];  // element offset of (token, head) row in q/out
-  u32x4 qf[NB][D / 32];
+  int64_t row_off[NB];
+  u32x4 qf[NB][D / 16];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int r = (wave * NB + nb) * 16 + ln;
+    const int r = (wave * NB + nb) * 32 + n32;
     const int tk = r / G;
     const int hh = r - tk * G;
     row_ok[nb] = tk < it.q_count;
     row_pos[nb] = it.q_pos0 + tk;
     row_off[nb] = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      qf[nb][kk] = row_ok[nb] ? load16(args.q + row_off[nb] + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[nb][kk] = row_ok[nb] ? load16(args.q + row_off[nb] + kk * 16 + lq2 * 8) : u32x4{0, 0, 0, 0};
   }
+  // positions spanned by this wave's valid rows (tile skipping / mask-free tiles)
+  const int tk_lo = (wave * NB * 32) / G;
+  const int tk_hi_raw = ((wave + 1) * NB * 32 - 1) / G;
+  const int tk_hi = tk_hi_raw < it.q_count - 1 ? tk_hi_raw : it.q_count - 1;
+  const bool wave_active = tk_lo <= tk_hi;
+  const int wpos_lo = it.q_pos0 + tk_lo;
+  const int wpos_hi = it.q_pos0 + tk_hi;
 
-  f32x4 o[D / 16][NB];
+  f32x16 o[D / 32][NB];
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) o[db][nb] = f32x16{};
   float m_run[NB], l_run[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -199,206 +266,202 @@ rpa_prefill_kernel(KernelArgs args) {
   const int kv_end = it.kv_end;
   const int tile0 = (kv_begin / BN) * BN;  // tiles are aligned to BN keys
   const int n_tiles = (kv_end - tile0 + BN - 1) / BN;
-  const int pos_min = it.q_pos0;
-  const int pos_max = it.q_pos0 + it.q_count - 1;
   const int window = args.window;
   const float sl2 = args.scale_log2;
 
-  // ---- register staging of one K/V tile ----
-  u32x4 kreg[C::K_PER_T];
-  u32x4 vreg[C::V_PER_T][8];
+  // ---- direct HBM -> LDS staging of one K/V tile ----
+  // Load i of this wave fills block wave*LOADS + i of the K and V tiles; lane
+  // l writes 16 bytes at +16*l of the block: key row s = 16*l / ROW_B of the
+  // block, chunk position p, which holds source chunk p ^ x(s).
+  int srow[C::LOADS], sgk[C::LOADS], sgv[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int blk = wave * C::LOADS + i;
+    const int in_blk = lane * 16;
+    const int sr = in_blk / C::ROW_B;
+    const int p = (in_blk % C::ROW_B) / 16;
+    srow[i] = blk * C::RPI + sr;
+    sgk[i] = (p ^ xor_k(sr)) * 16;
+    sgv[i] = (p ^ xor_v(sr)) * 16;
+  }
+  int st_pidx = tile0 / page_size;
+  int st_slot = tile0 - st_pidx * page_size;
 
-  // Element offset of key `key` (KV head g).  With UNI every page holds a whole
-  // number of tiles, so one wave-uniform page lookup serves the tile.
-  auto load_tile = [&](int k0) {
-    int64_t ubase = 0;
+  auto stage = [&](int k0, int buf) {
+    char* kdst = lds + buf * C::STAGE_B + wave * C::LOADS * C::BLK_K;
+    char* vdst = lds + buf * C::STAGE_B + C::TILE_K + wave * C::LOADS * C::BLK_V;
+    const int hi = k0 + BN < kv_end ? k0 + BN : kv_end;
     if constexpr (UNI) {
-      const int pidx = k0 / page_size;
-      const int64_t page = uniform_load(pt_row, pidx);
-      ubase = ((page * page_size + (k0 - pidx * page_size)) * hkv + g) * D;
-    }
-    auto kv_row = [&](int key, int pid) -> int64_t {
-      if constexpr (UNI) {
-        return ubase + static_cast<int64_t>(key - k0) * row_stride;
-      } else {
-        const int slot = key - (key / page_size) * page_size;
-        return ((static_cast<int64_t>(pid) * page_size + slot) * hkv + g) * D;
+      // The tile lies in one page.  Rows [k0, hi) are real keys of the
+      // sequence (rows below kv_begin are masked later); rows past hi read as
+      // zero through the buffer's record count.
+      const int64_t page = uniform_load(pt_row, st_pidx);
+      const int64_t base_off = ((page * page_size + st_slot) * hkv + g) * D;
+      st_slot += BN;
+      if (st_slot == page_size) {
+        st_slot = 0;
+        ++st_pidx;
       }
-    };
-    // page ids of every row this thread loads, fetched before any K/V load
-    int kpid[C::K_PER_T];
-    int vpid[C::V_PER_T][8];
+      const uint32_t nbytes = static_cast<uint32_t>((hi - k0 - 1) * row_bytes + D * 2);
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + base_off, nbytes);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + base_off, nbytes);
 #pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      kpid[i] = 0;
-      if constexpr (!UNI) {
-        const int u = i * C::NT + tid;
-        const int key = k0 + u / (D / 8);
-        if (u < C::K_UNITS && key >= kv_begin && key < kv_end) kpid[i] = pt_row[key / page_size];
+      for (int i = 0; i < C::LOADS; ++i) {
+        buffer_load_lds16(krs, kdst + i * C::BLK_K, srow[i] * row_bytes + sgk[i]);
+        buffer_load_lds16(vrs, vdst + i * C::BLK_V, srow[i] * row_bytes + sgv[i]);
       }
-    }
+    } else {
+      // Small pages: each lane looks up its row's page.  Rows past the valid
+      // range are redirected to the last valid key so every value is finite.
 #pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int u = i * C::NT + tid;
-      const int grp = u / (D / 8);
-      const int t = grp >> 2;
-      const int qd = grp & 3;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        vpid[i][j] = 0;
-        if constexpr (!UNI) {
-          const int key = k0 + t * 32 + ((j < 4) ? (qd * 4 + j) : (16 + qd * 4 + j - 4));
-          if (u < C::V_UNITS && key >= kv_begin && key < kv_end) vpid[i][j] = pt_row[key / page_size];
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int u = i * C::NT + tid;
-      kreg[i] = u32x4{0, 0, 0, 0};
-      if (u < C::K_UNITS) {
-        const int key = k0 + u / (D / 8);
-        const int c = u % (D / 8);
-        if (key >= kv_begin && key < kv_end) kreg[i] = load16(kbase + kv_row(key, kpid[i]) + c * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int u = i * C::NT + tid;
-      const int c = u % (D / 8);
-      const int grp = u / (D / 8);      // (t, quad) pair
-      const int t = grp >> 2;
-      const int qd = grp & 3;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        vreg[i][j] = u32x4{0, 0, 0, 0};
-        const int key = k0 + t * 32 + ((j < 4) ? (qd * 4 + j) : (16 + qd * 4 + j - 4));
-        if (u < C::V_UNITS && key >= kv_begin && key < kv_end)
-          vreg[i][j] = load16(vbase + kv_row(key, vpid[i][j]) + c * 8);
+      for (int i = 0; i < C::LOADS; ++i) {
+        int key = k0 + srow[i];
+        key = key < hi ? key : hi - 1;
+        const int pidx = key / page_size;
+        const int64_t page = pt_row[pidx];
+        const int64_t off = ((page * page_size + (key - pidx * page_size)) * hkv + g) * D * 2;
+        global_load_lds16(reinterpret_cast<const char*>(kbase) + off + sgk[i], kdst + i * C::BLK_K);
+        global_load_lds16(reinterpret_cast<const char*>(vbase) + off + sgv[i], vdst + i * C::BLK_V);
       }
     }
   };
 
-  auto store_tile = [&]() {
+  // per-lane LDS byte offsets of the MFMA operands (tile relative); the loop
+  // counters only add immediates: kk*32 for K, 16-key steps and db*64 for V
+  int kaddr[BN / 32];
 #pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int u = i * C::NT + tid;
-      if (u < C::K_UNITS) {
-        const int key = u / (D / 8);
-        const int c = u % (D / 8);
-        *reinterpret_cast<u32x4*>(ks + key * C::KSTRIDE + c * 8) = kreg[i];
-      }
-    }
+  for (int kb = 0; kb < BN / 32; ++kb) {
+    const int r = kb * 32 + n32;
+    const int sr = r % C::RPI;
+    kaddr[kb] = (r / C::RPI) * C::BLK_K + sr * C::ROW_B + (lq2 ^ xor_k(sr)) * 16;
+  }
+  int vaddr[2];
 #pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int u = i * C::NT + tid;
-      if (u < C::V_UNITS) {
-        const int c = u % (D / 8);
-        const int grp = u / (D / 8);
-        u32x4 tr[8];
-        transpose8x8(vreg[i], tr);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = c * 8 + e;  // d index = V^T row
-          *reinterpret_cast<u32x4*>(vt + r * BN + vt_chunk<BN>(r, grp) * 8) = tr[e];
-        }
-      }
-    }
-  };
+  for (int half = 0; half < 2; ++half) {
+    const int r = 4 * lq2 + (l16 >> 2) + 8 * half;
+    const int sr = r % C::RPI;
+    const int cl = 2 * (grp & 1) + ((l16 & 3) >> 1);
+    vaddr[half] = C::TILE_K + (r / C::RPI) * C::BLK_V + sr * C::ROW_B + ((cl ^ xor_v(sr)) * 16) + (l16 & 1) * 8;
+  }
 
-  if (n_tiles > 0) load_tile(tile0);
+  if (n_tiles > 0) stage(tile0, 0);
+  wait_vmem();
+  __syncthreads();
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int k0 = tile0 + tile * BN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (tile + 1 < n_tiles) load_tile(k0 + BN);
+    const int cur = tile & 1;
+    if (tile + 1 < n_tiles) stage(k0 + BN, cur ^ 1);
 
-    // ---- S^T = K Q^T ----
-    f32x4 s[BN / 16][NB];
+    // tile fully masked for this wave's rows: nothing to add
+    const bool skip = !wave_active || k0 > wpos_hi || k0 + BN <= kv_begin ||
+                      (window > 0 && k0 + BN - 1 <= wpos_lo - window);
+    if (!skip) {
+      const char* ks = lds + cur * C::STAGE_B;
+      // ---- S^T = K Q^T ----
+      f32x16 sc[BN / 32][NB];
 #pragma unroll
-    for (int kb = 0; kb < BN / 16; ++kb)
+      for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) s[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; ++nb) sc[kb][nb] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
+      for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 16; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(ks + (kb * 16 + ln) * C::KSTRIDE + kk * 32 + lq * 8);
+        for (int kb = 0; kb < BN / 32; ++kb) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(ks + kaddr[kb] + kk * 32);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[kb][nb] = mfma16(a, qf[nb][kk], s[kb][nb]);
+          for (int nb = 0; nb < NB; ++nb) sc[kb][nb] = mfma32(a, qf[nb][kk], sc[kb][nb]);
+        }
       }
-    }
-
-    // ---- mask + online softmax (fp32, base 2) ----
-    const bool full = (k0 >= kv_begin) && (k0 + BN <= kv_end) && (k0 + BN - 1 <= pos_min) &&
-                      (window <= 0 || k0 > pos_max - window);
-    u32x4 pf[BN / 32][NB];
+      // ---- mask + online softmax (fp32, base 2) ----
+      // Scores stay raw; scale*log2(e) is folded into one FMA per element.
+      // The running maximum m_run is only raised when a row's new maximum
+      // exceeds it by more than 8 (in log2 units), so O is rescaled rarely;
+      // every p stays below 2^8 and the result is unchanged because the same
+      // reference maximum enters both O and l.
+      const bool full = (k0 >= kv_begin) && (k0 + BN <= kv_end) && (k0 + BN - 1 <= wpos_lo) &&
+                        (window <= 0 || k0 > wpos_hi - window);
+      u32x4 pf[BN / 16][NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float mx = kNegInf;
+      for (int nb = 0; nb < NB; ++nb) {
+        float mx = kNegInf;
+        if (full) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 16; ++kb) {
+          for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float x = s[kb][nb][j] * sl2;
-          if (!full) {
-            const int key = k0 + kb * 16 + lq * 4 + j;
-            if (!key_visible(key, row_pos[nb], kv_begin, kv_end, window)) x = kNegInf;
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][nb][j]);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * lq2 + (j & 3);
+              if (!key_visible(key, row_pos[nb], kv_begin, kv_end, window)) sc[kb][nb][j] = kNegInf;
+              mx = fmaxf(mx, sc[kb][nb][j]);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mx2 = mx * sl2;   // tile maximum in log2 units (scale > 0)
+        if (__any(mx2 > m_run[nb] + 8.f)) {
+          const float m_new = fmaxf(m_run[nb], mx2);
+          // 0 when the row had no visible key yet; 1 for a row that still has none
+          const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[nb] - m_new);
+          m_run[nb] = m_new;
+          l_run[nb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) o[db][nb] *= alpha;
+        }
+        const float base = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float p[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              p[i] = fast_exp2(__builtin_fmaf(sc[kb][nb][8 * h + i], sl2, -base));
+              lsum += p[i];
+            }
+            pf[kb * 2 + h][nb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
           }
-          s[kb][nb][j] = x;
-          mx = fmaxf(mx, x);
+        }
+        l_run[nb] += lsum;
+      }
+      // ---- O^T += V^T P^T: V^T operands by two transposing reads each ----
+#pragma unroll
+      for (int ks16 = 0; ks16 < BN / 16; ++ks16) {
+        const char* vrow = ks + ks16 * (16 / C::RPI) * C::BLK_V;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const u32x2 l2 = lds_read_tr16(vrow + vaddr[0] + db * 64);
+          const u32x2 h2 = lds_read_tr16(vrow + vaddr[1] + db * 64);
+          const u32x4 a = u32x4{l2[0], l2[1], h2[0], h2[1]};
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) o[db][nb] = mfma32(a, pf[ks16][nb], o[db][nb]);
         }
       }
-      mx = xor_max(mx);
-      const float m_new = fmaxf(m_run[nb], mx);
-      const float base = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[nb] - base);
-      m_run[nb] = m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int t = 0; t < BN / 32; ++t) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[j] = fast_exp2(s[2 * t][nb][j] - base);
-          p[4 + j] = fast_exp2(s[2 * t + 1][nb][j] - base);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) lsum += p[j];
-        pf[t][nb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-      }
-      l_run[nb] = l_run[nb] * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) o[db][nb] *= alpha;
     }
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int t = 0; t < BN / 32; ++t) {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const int r = db * 16 + ln;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(vt + r * BN + vt_chunk<BN>(r, t * 4 + lq) * 8);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[db][nb] = mfma16(a, pf[t][nb], o[db][nb]);
-      }
-    }
+    wait_vmem();
+    __syncthreads();
   }
 
-  // ---- epilogue: O / l -> bf16 ----
+  // ---- epilogue: O / l -> bf16; lane holds d = 32*db + 8*b + 4*lq2 + t of row n32 ----
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const float l = xor_sum(l_run[nb]);
+    const float l = l_run[nb] + __shfl_xor(l_run[nb], 32);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (row_ok[nb]) {
-      uint16_t* dst = args.out + row_off[nb] + lq * 4;
+      uint16_t* dst = args.out + row_off[nb] + lq2 * 4;
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const f32x4 v = o[db][nb] * inv;
-        *reinterpret_cast<u32x2*>(dst + db * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float* v = reinterpret_cast<const float*>(&o[db][nb]) + 4 * b;
+          *reinterpret_cast<u32x2*>(dst + db * 32 + b * 8) =
+              u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
+        }
       }
     }
   }
@@ -410,8 +473,9 @@ rpa_prefill_kernel(KernelArgs args) {
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) rpa_merge_kernel(KernelArgs args) {
-  const rpa_work_item grp = args.groups[blockIdx.x];
   constexpr int C4 = D / 4;
+  constexpr int NB = 8;   // splits fetched per batch: every load of a batch is in flight at once
+  const rpa_work_item grp = args.groups[blockIdx.x];
   const int rows = grp.q_count * args.group;
   const int n = grp.num_splits;
   const float* lse = args.partial_lse + static_cast<int64_t>(grp.partial_base) * 16;
@@ -419,17 +483,32 @@ __global__ void __launch_bounds__(256) rpa_merge_kernel(KernelArgs args) {
   for (int idx = threadIdx.x; idx < rows * C4; idx += blockDim.x) {
     const int r = idx / C4;
     const int c = idx - r * C4;
-    float mx = kNegInf;
-    for (int i = 0; i < n; ++i) mx = fmaxf(mx, lse[i * 16 + r]);
-    const float base = (mx == kNegInf) ? 0.f : mx;
-    float wsum = 0.f;
+    float mx = kNegInf, wsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int i = 0; i < n; ++i) {
-      const float w = fast_exp2(lse[i * 16 + r] - base);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(po + (static_cast<int64_t>(i) * 16 + r) * D + c * 4);
-      wsum += w;
-      acc += w * v;
+    for (int i0 = 0; i0 < n; i0 += NB) {
+      float l[NB];
+      f32x4 v[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const bool ok = i0 + b < n;
+        l[b] = ok ? lse[(i0 + b) * 16 + r] : kNegInf;
+        v[b] = ok ? *reinterpret_cast<const f32x4*>(po + (static_cast<int64_t>(i0 + b) * 16 + r) * D + c * 4)
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      float bm = mx;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) bm = fmaxf(bm, l[b]);
+      const float base = (bm == kNegInf) ? 0.f : bm;
+      const float rescale = fast_exp2(mx - base);   // running sums to the new maximum
+      wsum *= rescale;
+      acc *= rescale;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float w = fast_exp2(l[b] - base);
+        wsum += w;
+        acc += w * v[b];
+      }
+      mx = bm;
     }
     acc *= wsum > 0.f ? 1.f / wsum : 0.f;
     const int tk = r / args.group;
@@ -509,57 +588,79 @@ rpa_decode_kernel(KernelArgs args) {
   // 32-key chunks aligned to 32 keys; with UNI a chunk never crosses a page.
   const int chunk0 = (kv_begin / 32) * 32;
   const int n_chunks = (kv_end - chunk0 + 31) / 32;
+  const int row_bytes = static_cast<int>(row_stride) * 2;   // bytes between key rows of a page
+  int next_page = 0;
+  if constexpr (UNI) {
+    if (wave < n_chunks) next_page = uniform_load(pt_row, (chunk0 + wave * 32) / page_size);
+  }
   for (int ch = wave; ch < n_chunks; ch += NW) {
     const int k0 = chunk0 + ch * 32;
-    int64_t ubase = 0;
-    if constexpr (UNI) {
-      const int pidx = k0 / page_size;
-      const int64_t page = uniform_load(pt_row, pidx);
-      ubase = ((page * page_size + (k0 - pidx * page_size)) * hkv + g) * D;
-    }
     // keys of this lane: K rows k0 + 16*kb + ln; V rows k0 + 4*lq + j and k0 + 16 + 4*lq + j
-    int kkey[2], vkey[8];
+    u32x4 kf[2][D / 32];
+    u32x4 vf[C::NU][8];
+    if constexpr (UNI) {
+      // One page holds the whole chunk: buffer loads against the chunk's valid
+      // key rows [lo, hi); rows outside read as zero (negative offsets wrap
+      // above the record count), so there are no branches and no NaN reads.
+      const int page = next_page;
+      if (ch + NW < n_chunks) next_page = uniform_load(pt_row, (k0 + NW * 32) / page_size);
+      const int lo = k0 > kv_begin ? k0 : kv_begin;
+      const int hi = k0 + 32 < kv_end ? k0 + 32 : kv_end;
+      const int64_t lo_off = ((static_cast<int64_t>(page) * page_size + (lo - (lo / page_size) * page_size)) * hkv + g) * D;
+      const uint32_t nbytes = static_cast<uint32_t>((hi - lo - 1) * row_bytes + D * 2);
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + lo_off, nbytes);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + lo_off, nbytes);
+      const int rel = k0 - lo;   // <= 0
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) kkey[kb] = k0 + kb * 16 + ln;
+      for (int kb = 0; kb < 2; ++kb) {
+        const int off = (rel + kb * 16 + ln) * row_bytes + lq * 16;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vkey[j] = k0 + ((j < 4) ? (lq * 4 + j) : (16 + lq * 4 + j - 4));
-    int kpid[2] = {0, 0}, vpid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if constexpr (!UNI) {   // every page id first, then the K/V loads
+        for (int kk = 0; kk < D / 32; ++kk) kf[kb][kk] = buffer_load16(krs, off + kk * 64);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key_rel = rel + ((j < 4) ? (lq * 4 + j) : (16 + lq * 4 + j - 4));
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u) {
+          const int c = u * 16 + ln;
+          vf[u][j] = c < C::NCH ? buffer_load16(vrs, key_rel * row_bytes + c * 16) : u32x4{0, 0, 0, 0};
+        }
+      }
+    } else {
+      int kkey[2], vkey[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kkey[kb] = k0 + kb * 16 + ln;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vkey[j] = k0 + ((j < 4) ? (lq * 4 + j) : (16 + lq * 4 + j - 4));
+      int kpid[2] = {0, 0}, vpid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      // every page id first, then the K/V loads
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         if (kkey[kb] >= kv_begin && kkey[kb] < kv_end) kpid[kb] = pt_row[kkey[kb] / page_size];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (vkey[j] >= kv_begin && vkey[j] < kv_end) vpid[j] = pt_row[vkey[j] / page_size];
-    }
-    auto kv_row = [&](int key, int pid) -> int64_t {
-      if constexpr (UNI) {
-        return ubase + static_cast<int64_t>(key - k0) * row_stride;
-      } else {
+      auto kv_row = [&](int key, int pid) -> int64_t {
         const int slot = key - (key / page_size) * page_size;
         return ((static_cast<int64_t>(pid) * page_size + slot) * hkv + g) * D;
+      };
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bool ok = kkey[kb] >= kv_begin && kkey[kb] < kv_end;
+        const int64_t off = kv_row(kkey[kb], kpid[kb]);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+          kf[kb][kk] = ok ? load16(kbase + off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
       }
-    };
-    // K rows (A operand of S^T = K Q^T): d = 32*kk + 8*lq
-    u32x4 kf[2][D / 32];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bool ok = kkey[kb] >= kv_begin && kkey[kb] < kv_end;
-      const int64_t off = kv_row(kkey[kb], kpid[kb]);
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = vkey[j] >= kv_begin && vkey[j] < kv_end;
+        const int64_t off = kv_row(vkey[j], vpid[j]);
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk)
-        kf[kb][kk] = ok ? load16(kbase + off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
-    }
-    // V rows at 16-byte chunk 16*u + ln
-    u32x4 vf[C::NU][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = vkey[j] >= kv_begin && vkey[j] < kv_end;
-      const int64_t off = kv_row(vkey[j], vpid[j]);
-#pragma unroll
-      for (int u = 0; u < C::NU; ++u) {
-        const int c = u * 16 + ln;
-        vf[u][j] = (ok && c < C::NCH) ? load16(vbase + off + c * 8) : u32x4{0, 0, 0, 0};
+        for (int u = 0; u < C::NU; ++u) {
+          const int c = u * 16 + ln;
+          vf[u][j] = (ok && c < C::NCH) ? load16(vbase + off + c * 8) : u32x4{0, 0, 0, 0};
+        }
       }
     }
 
@@ -700,25 +801,27 @@ rpa_decode_kernel(KernelArgs args) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int D, int NB, int NW, int BN, bool UNI>
+template <int D, int BN, int NW, int NB, bool UNI>
 static hipError_t launch_prefill_u(const KernelArgs& a, int n_items, hipStream_t stream) {
-  using C = PrefillCfg<D, NB, NW, BN>;
+  using C = PrefillCfg<D, BN, NW, NB>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_prefill_kernel<D, NB, NW, BN, UNI>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, UNI>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((rpa_prefill_kernel<D, NB, NW, BN, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
+  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
                      stream, a);
   return hipGetLastError();
 }
 
-template <int D, int NB, int NW, int BN>
+template <int D, int BN, int NW, int NB>
 static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, hipStream_t stream) {
-  if (a.page_size % BN == 0) return launch_prefill_u<D, NB, NW, BN, true>(a, n_items, stream);
-  return launch_prefill_u<D, NB, NW, BN, false>(a, n_items, stream);
+  // one buffer descriptor per tile needs the tile inside one page and 32-bit offsets
+  const bool uni = a.page_size % BN == 0 && int64_t(a.page_size) * a.num_kv_heads * D * 2 < (int64_t(1) << 31);
+  if (uni) return launch_prefill_u<D, BN, NW, NB, true>(a, n_items, stream);
+  return launch_prefill_u<D, BN, NW, NB, false>(a, n_items, stream);
 }
 
 template <int D, int NW, bool UNI>
@@ -744,12 +847,18 @@ static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t 
   return hipGetLastError();
 }
 
+// Prefill tile shapes per head size: (BN keys, NW waves, NB 32-row blocks per wave).
+#define RPA_PREFILL_SHAPE_64 64, 64, 4, 2
+#define RPA_PREFILL_SHAPE_128 128, 64, 4, 1
+#define RPA_PREFILL_SHAPE_256 256, 64, 4, 1
+#define RPA_PREFILL_SHAPE_512 512, 32, 4, 1
+
 int prefill_rows_for(int head_dim) {
   switch (head_dim) {
-    case 64: return 4 * 2 * 16;
-    case 128: return 4 * 2 * 16;
-    case 256: return 4 * 2 * 16;
-    case 512: return 4 * 1 * 16;
+    case 64: return PrefillCfg<RPA_PREFILL_SHAPE_64>::ROWS;
+    case 128: return PrefillCfg<RPA_PREFILL_SHAPE_128>::ROWS;
+    case 256: return PrefillCfg<RPA_PREFILL_SHAPE_256>::ROWS;
+    case 512: return PrefillCfg<RPA_PREFILL_SHAPE_512>::ROWS;
     default: return 0;
   }
 }
@@ -782,10 +891,10 @@ hipError_t launch_prefill(const LaunchArgs& l, const rpa_work_item* items, int n
   const KernelArgs a = make_args(l, items);
   hipStream_t s = static_cast<hipStream_t>(l.stream);
   switch (l.head_dim) {
-    case 64: return launch_prefill_t<64, 2, 4, 64>(a, n_items, s);
-    case 128: return launch_prefill_t<128, 2, 4, 64>(a, n_items, s);
-    case 256: return launch_prefill_t<256, 2, 4, 64>(a, n_items, s);
-    case 512: return launch_prefill_t<512, 1, 4, 32>(a, n_items, s);
+    case 64: return launch_prefill_t<RPA_PREFILL_SHAPE_64>(a, n_items, s);
+    case 128: return launch_prefill_t<RPA_PREFILL_SHAPE_128>(a, n_items, s);
+    case 256: return launch_prefill_t<RPA_PREFILL_SHAPE_256>(a, n_items, s);
+    case 512: return launch_prefill_t<RPA_PREFILL_SHAPE_512>(a, n_items, s);
     default: return hipErrorInvalidValue;
   }
 }

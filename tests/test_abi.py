@@ -83,6 +83,8 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails on the h
     ("too many tokens", [0, 65], [100], 1, 0, 1.0, "max_q_tokens"),
     ("nan scale", [0, 1], [5], 1, 0, float("nan"), "scale"),
     ("inf scale", [0, 1], [5], 1, 0, float("inf"), "scale"),
+    ("zero scale", [0, 1], [5], 1, 0, 0.0, "scale"),
+    ("negative scale", [0, 1], [5], 1, 0, -0.5, "scale"),
 ])
 def test_forward_rejects_invalid_metadata(case, cu, kv, n, window, scale, msg):
     lib, st, ctx = _ctx()
