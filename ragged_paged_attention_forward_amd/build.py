@@ -17,7 +17,16 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "librpa.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["rpa_kernels.hip", "rpa_api.cpp", "rpa_plan.cpp"]
+# Kernel translation units, one per head size.  Accumulators of the head
+# sizes up to 256 fit in the architectural VGPRs, where MFMA results can be
+# used by VALU code without copies; head size 512 keeps them in AGPRs.
+KERNEL_SOURCES = {
+    "rpa_kernels_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "rpa_kernels_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "rpa_kernels_d256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "rpa_kernels_d512.hip": [],
+}
+HOST_SOURCES = ["rpa_dispatch.cpp", "rpa_api.cpp", "rpa_plan.cpp"]
 ARCH = "gfx950"
 
 
@@ -38,19 +47,24 @@ def compile_flags():
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source and link librpa.so in the package directory."""
+    """Compile every source (in parallel) and link librpa.so in the package directory."""
+    from concurrent.futures import ThreadPoolExecutor
     cc = hipcc()
     out_dir = os.path.join(ROOT, "_build")
     os.makedirs(out_dir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
+    jobs = []
+    for src, flags in KERNEL_SOURCES.items():
         obj = os.path.join(out_dir, src + ".o")
-        cmd = [cc] + compile_flags() + list(extra_flags) + ["-c", os.path.join(CSRC, src), "-o", obj]
-        if src.endswith(".cpp"):
-            cmd = [cc, "-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC,
-                   "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src), "-o", obj]
-        _run(cmd, verbose)
-        objs.append(obj)
+        jobs.append(([cc] + compile_flags() + flags + list(extra_flags) +
+                     ["-c", os.path.join(CSRC, src), "-o", obj], obj))
+    for src in HOST_SOURCES:
+        obj = os.path.join(out_dir, src + ".o")
+        jobs.append(([cc, "-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC,
+                      "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    objs = [o for _, o in jobs]
     tmp = LIB_PATH + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB_PATH)

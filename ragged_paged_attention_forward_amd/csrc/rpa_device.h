@@ -1,3 +1,6 @@
+// Device code of the ragged paged attention kernels (included by one
+// translation unit per head size, see rpa_kernels_d*.hip).
+#pragma once
 // Ragged paged attention kernels for CDNA4 (gfx950).
 //
 // Two kernels consume the host-built work list:
@@ -28,6 +31,7 @@
 
 #include "rpa.h"
 #include "rpa_launch.h"
+#include "rpa_kargs.h"
 
 namespace rpa {
 
@@ -99,24 +103,7 @@ RPA_DEV int32_t uniform_load(const int32_t* p, int idx) {
   return ((const_i32_ptr)(p))[idx];
 }
 
-struct KernelArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const int32_t* page_table;
-  uint16_t* out;
-  const rpa_work_item* items;
-  const rpa_work_item* groups;
-  float* partial_o;      // [slot][16 rows][D]
-  float* partial_lse;    // [slot][16 rows], base-2 log-sum-exp
-  int32_t num_q_heads;
-  int32_t num_kv_heads;
-  int32_t group;         // G = Hq / Hkv
-  int32_t page_size;
-  int32_t max_pages;
-  int32_t window;
-  float scale_log2;      // scale * log2(e)
-};
+// KernelArgs: see rpa_kargs.h
 
 RPA_DEV bool key_visible(int key, int pos, int kv_begin, int kv_end, int window) {
   return key >= kv_begin && key < kv_end && key <= pos && (window <= 0 || key > pos - window);
@@ -165,10 +152,31 @@ RPA_DEV u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p)));
 }
 
-// vmcnt(0) with the other counters left alone (gfx9 s_waitcnt encoding).
-RPA_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, other counters left
+// at their maxima).  Loads complete in issue order, so this waits for all but
+// the N most recent.
+template <int N>
+RPA_DEV void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+RPA_DEV void wait_vmem() { wait_vmem_le<0>(); }
 
-template <int D, int BN, int NW, int NB>
+// Wait until the loads of the oldest staged tile are complete, given that
+// `later` tiles of `LPT` loads each were staged after it.
+template <int LPT, int MAXLATER>
+RPA_DEV void wait_tile_loads(int later) {
+  if constexpr (MAXLATER >= 2) {
+    if (later >= 2) { wait_vmem_le<2 * LPT>(); return; }
+  }
+  if constexpr (MAXLATER >= 1) {
+    if (later >= 1) { wait_vmem_le<LPT>(); return; }
+  }
+  wait_vmem();
+}
+
+template <int D, int BN, int NW, int NB, int NS>
 struct PrefillCfg {
   static constexpr int NT = NW * 64;
   static constexpr int ROWS = NW * NB * 32;          // query rows per workgroup
@@ -189,8 +197,11 @@ struct PrefillCfg {
   static constexpr int TILE_K = BLOCKS * BLK_K;
   static constexpr int TILE_V = BLOCKS * BLK_V;
   static constexpr int STAGE_B = TILE_K + TILE_V;
-  static constexpr int LDS_BYTES = 2 * STAGE_B;      // double buffered
+  static constexpr int LDS_BYTES = NS * STAGE_B;     // NS tiles in flight
   static constexpr int LOADS = BLOCKS / NW;          // 1 KB direct loads per wave per tensor
+  static constexpr int LPT = 2 * LOADS;              // load instructions per wave per tile
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  static_assert((NS - 2) * LPT < 64, "vmcnt field");
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert(BLOCKS % NW == 0, "tile must split into 1 KB loads per wave");
   static_assert(16 % RPI == 0, "16-key steps must cover whole blocks");
@@ -199,10 +210,10 @@ struct PrefillCfg {
 RPA_DEV int xor_k(int s) { return s & 1; }
 RPA_DEV int xor_v(int s) { return (s & 1) * 2; }
 
-template <int D, int BN, int NW, int NB, bool UNI>
+template <int D, int BN, int NW, int NB, int NS, bool UNI>
 __global__ void __launch_bounds__(NW * 64, 1)
 rpa_prefill_kernel(KernelArgs args) {
-  using C = PrefillCfg<D, BN, NW, NB>;
+  using C = PrefillCfg<D, BN, NW, NB, NS>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   char* lds = reinterpret_cast<char*>(smem);
 
@@ -344,14 +355,17 @@ rpa_prefill_kernel(KernelArgs args) {
     vaddr[half] = C::TILE_K + (r / C::RPI) * C::BLK_V + sr * C::ROW_B + ((cl ^ xor_v(sr)) * 16) + (l16 & 1) * 8;
   }
 
-  if (n_tiles > 0) stage(tile0, 0);
-  wait_vmem();
+  // NS-stage pipeline: tiles t+1 .. t+NS-1 are in flight while tile t is used.
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < n_tiles) stage(tile0 + t * BN, t);
+  wait_tile_loads<C::LPT, NS - 2>((n_tiles < NS - 1 ? n_tiles : NS - 1) - 1);
   __syncthreads();
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int k0 = tile0 + tile * BN;
-    const int cur = tile & 1;
-    if (tile + 1 < n_tiles) stage(k0 + BN, cur ^ 1);
+    const int cur = tile % NS;
+    if (tile + NS - 1 < n_tiles) stage(k0 + (NS - 1) * BN, (tile + NS - 1) % NS);
 
     // tile fully masked for this wave's rows: nothing to add
     const bool skip = !wave_active || k0 > wpos_hi || k0 + BN <= kv_begin ||
@@ -359,19 +373,35 @@ rpa_prefill_kernel(KernelArgs args) {
     if (!skip) {
       const char* ks = lds + cur * C::STAGE_B;
       // ---- S^T = K Q^T ----
+      // With a single 32-key block per tile the kk reduction is split over two
+      // accumulators, so consecutive MFMAs never wait on each other's result.
+      constexpr int NACC = (BN / 32) * NB >= 2 ? 1 : 2;
       f32x16 sc[BN / 32][NB];
+      f32x16 sc2[BN / 32][NB];
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sc[kb][nb] = f32x16{};
+        for (int nb = 0; nb < NB; ++nb) {
+          sc[kb][nb] = f32x16{};
+          sc2[kb][nb] = f32x16{};
+        }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
           const u32x4 a = *reinterpret_cast<const u32x4*>(ks + kaddr[kb] + kk * 32);
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) sc[kb][nb] = mfma32(a, qf[nb][kk], sc[kb][nb]);
+          for (int nb = 0; nb < NB; ++nb) {
+            if (NACC == 2 && (kk & 1)) sc2[kb][nb] = mfma32(a, qf[nb][kk], sc2[kb][nb]);
+            else sc[kb][nb] = mfma32(a, qf[nb][kk], sc[kb][nb]);
+          }
         }
+      }
+      if constexpr (NACC == 2) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) sc[kb][nb] += sc2[kb][nb];
       }
       // ---- mask + online softmax (fp32, base 2) ----
       // Scores stay raw; scale*log2(e) is folded into one FMA per element.
@@ -443,7 +473,12 @@ rpa_prefill_kernel(KernelArgs args) {
         }
       }
     }
-    wait_vmem();
+    // tile+1 must have landed; tiles tile+2 .. tile+NS-1 may still be in flight
+    {
+      const int staged_last = (tile + NS - 1 < n_tiles ? tile + NS - 1 : n_tiles - 1);
+      const int later = staged_last - (tile + 1);
+      wait_tile_loads<C::LPT, NS - 2>(later < 0 ? 0 : later);
+    }
     __syncthreads();
   }
 
@@ -801,27 +836,27 @@ rpa_decode_kernel(KernelArgs args) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int D, int BN, int NW, int NB, bool UNI>
+template <int D, int BN, int NW, int NB, int NS, bool UNI>
 static hipError_t launch_prefill_u(const KernelArgs& a, int n_items, hipStream_t stream) {
-  using C = PrefillCfg<D, BN, NW, NB>;
+  using C = PrefillCfg<D, BN, NW, NB, NS>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, UNI>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, NS, UNI>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
+  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, NS, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
                      stream, a);
   return hipGetLastError();
 }
 
-template <int D, int BN, int NW, int NB>
+template <int D, int BN, int NW, int NB, int NS>
 static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, hipStream_t stream) {
   // one buffer descriptor per tile needs the tile inside one page and 32-bit offsets
   const bool uni = a.page_size % BN == 0 && int64_t(a.page_size) * a.num_kv_heads * D * 2 < (int64_t(1) << 31);
-  if (uni) return launch_prefill_u<D, BN, NW, NB, true>(a, n_items, stream);
-  return launch_prefill_u<D, BN, NW, NB, false>(a, n_items, stream);
+  if (uni) return launch_prefill_u<D, BN, NW, NB, NS, true>(a, n_items, stream);
+  return launch_prefill_u<D, BN, NW, NB, NS, false>(a, n_items, stream);
 }
 
 template <int D, int NW, bool UNI>
@@ -848,82 +883,24 @@ static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t 
 }
 
 // Prefill tile shapes per head size: (BN keys, NW waves, NB 32-row blocks per wave).
-#define RPA_PREFILL_SHAPE_64 64, 64, 4, 2
-#define RPA_PREFILL_SHAPE_128 128, 64, 4, 1
-#define RPA_PREFILL_SHAPE_256 256, 64, 4, 1
-#define RPA_PREFILL_SHAPE_512 512, 32, 4, 1
+// Prefill tile shapes per head size:
+// (D, BN keys per tile, NW waves, NB 32-row blocks per wave, NS pipeline stages).
+#define RPA_PREFILL_SHAPE_64 64, 64, 4, 2, 2
+#define RPA_PREFILL_SHAPE_128 128, 64, 4, 1, 2
+#define RPA_PREFILL_SHAPE_256 256, 32, 8, 1, 4
+#define RPA_PREFILL_SHAPE_512 512, 32, 4, 1, 2
 
-int prefill_rows_for(int head_dim) {
-  switch (head_dim) {
-    case 64: return PrefillCfg<RPA_PREFILL_SHAPE_64>::ROWS;
-    case 128: return PrefillCfg<RPA_PREFILL_SHAPE_128>::ROWS;
-    case 256: return PrefillCfg<RPA_PREFILL_SHAPE_256>::ROWS;
-    case 512: return PrefillCfg<RPA_PREFILL_SHAPE_512>::ROWS;
-    default: return 0;
-  }
-}
-
-bool head_dim_supported(int head_dim) { return prefill_rows_for(head_dim) > 0; }
-
-static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
-  KernelArgs a;
-  a.q = static_cast<const uint16_t*>(l.q);
-  a.k = static_cast<const uint16_t*>(l.k);
-  a.v = static_cast<const uint16_t*>(l.v);
-  a.page_table = l.page_table;
-  a.out = static_cast<uint16_t*>(l.out);
-  a.items = items;
-  a.groups = l.groups;
-  a.partial_o = l.partial_o;
-  a.partial_lse = l.partial_lse;
-  a.num_q_heads = l.num_q_heads;
-  a.num_kv_heads = l.num_kv_heads;
-  a.group = l.num_q_heads / l.num_kv_heads;
-  a.page_size = l.page_size;
-  a.max_pages = l.max_pages;
-  a.window = l.window;
-  a.scale_log2 = l.scale_log2;
-  return a;
-}
-
-hipError_t launch_prefill(const LaunchArgs& l, const rpa_work_item* items, int n_items) {
-  if (n_items <= 0) return hipSuccess;
-  const KernelArgs a = make_args(l, items);
-  hipStream_t s = static_cast<hipStream_t>(l.stream);
-  switch (l.head_dim) {
-    case 64: return launch_prefill_t<RPA_PREFILL_SHAPE_64>(a, n_items, s);
-    case 128: return launch_prefill_t<RPA_PREFILL_SHAPE_128>(a, n_items, s);
-    case 256: return launch_prefill_t<RPA_PREFILL_SHAPE_256>(a, n_items, s);
-    case 512: return launch_prefill_t<RPA_PREFILL_SHAPE_512>(a, n_items, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_decode(const LaunchArgs& l, const rpa_work_item* items, int n_items) {
-  if (n_items <= 0) return hipSuccess;
-  const KernelArgs a = make_args(l, items);
-  hipStream_t s = static_cast<hipStream_t>(l.stream);
-  const int w = l.decode_waves;
-  switch (l.head_dim) {
-    case 64: return launch_decode_t<64>(a, n_items, w, s);
-    case 128: return launch_decode_t<128>(a, n_items, w, s);
-    case 256: return launch_decode_t<256>(a, n_items, w, s);
-    case 512: return launch_decode_t<512>(a, n_items, w, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_merge(const LaunchArgs& l, int n_groups) {
-  if (n_groups <= 0) return hipSuccess;
-  const KernelArgs a = make_args(l, nullptr);
-  hipStream_t s = static_cast<hipStream_t>(l.stream);
-  switch (l.head_dim) {
-    case 64: return launch_merge_t<64>(a, n_groups, s);
-    case 128: return launch_merge_t<128>(a, n_groups, s);
-    case 256: return launch_merge_t<256>(a, n_groups, s);
-    case 512: return launch_merge_t<512>(a, n_groups, s);
-    default: return hipErrorInvalidValue;
-  }
-}
+// Defines the per-head-size entry points used by rpa_dispatch.hip.
+#define RPA_DEFINE_HEAD_DIM(D)                                                              \
+  hipError_t launch_prefill_d##D(const KernelArgs& a, int n, hipStream_t s) {               \
+    return launch_prefill_t<RPA_PREFILL_SHAPE_##D>(a, n, s);                               \
+  }                                                                                         \
+  hipError_t launch_decode_d##D(const KernelArgs& a, int n, int waves, hipStream_t s) {     \
+    return launch_decode_t<D>(a, n, waves, s);                                              \
+  }                                                                                         \
+  hipError_t launch_merge_d##D(const KernelArgs& a, int n, hipStream_t s) {                 \
+    return launch_merge_t<D>(a, n, s);                                                      \
+  }                                                                                         \
+  int prefill_rows_d##D() { return PrefillCfg<RPA_PREFILL_SHAPE_##D>::ROWS; }
 
 }  // namespace rpa

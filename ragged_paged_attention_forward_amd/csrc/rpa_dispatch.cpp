@@ -1,0 +1,104 @@
+// Host-side dispatch from the C ABI's launch arguments to the per-head-size
+// kernel translation units.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rpa.h"
+#include "rpa_kargs.h"
+#include "rpa_launch.h"
+
+namespace rpa {
+
+
+
+hipError_t launch_prefill_d64(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, hipStream_t s);
+hipError_t launch_merge_d64(const KernelArgs& a, int n, hipStream_t s);
+int prefill_rows_d64();
+hipError_t launch_prefill_d128(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, hipStream_t s);
+hipError_t launch_merge_d128(const KernelArgs& a, int n, hipStream_t s);
+int prefill_rows_d128();
+hipError_t launch_prefill_d256(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, hipStream_t s);
+hipError_t launch_merge_d256(const KernelArgs& a, int n, hipStream_t s);
+int prefill_rows_d256();
+hipError_t launch_prefill_d512(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, hipStream_t s);
+hipError_t launch_merge_d512(const KernelArgs& a, int n, hipStream_t s);
+int prefill_rows_d512();
+
+int prefill_rows_for(int head_dim) {
+  switch (head_dim) {
+    case 64: return prefill_rows_d64();
+    case 128: return prefill_rows_d128();
+    case 256: return prefill_rows_d256();
+    case 512: return prefill_rows_d512();
+    default: return 0;
+  }
+}
+
+bool head_dim_supported(int head_dim) { return prefill_rows_for(head_dim) > 0; }
+
+static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
+  KernelArgs a;
+  a.q = static_cast<const uint16_t*>(l.q);
+  a.k = static_cast<const uint16_t*>(l.k);
+  a.v = static_cast<const uint16_t*>(l.v);
+  a.page_table = l.page_table;
+  a.out = static_cast<uint16_t*>(l.out);
+  a.items = items;
+  a.groups = l.groups;
+  a.partial_o = l.partial_o;
+  a.partial_lse = l.partial_lse;
+  a.num_q_heads = l.num_q_heads;
+  a.num_kv_heads = l.num_kv_heads;
+  a.group = l.num_q_heads / l.num_kv_heads;
+  a.page_size = l.page_size;
+  a.max_pages = l.max_pages;
+  a.window = l.window;
+  a.scale_log2 = l.scale_log2;
+  return a;
+}
+
+hipError_t launch_prefill(const LaunchArgs& l, const rpa_work_item* items, int n_items) {
+  if (n_items <= 0) return hipSuccess;
+  const KernelArgs a = make_args(l, items);
+  hipStream_t s = static_cast<hipStream_t>(l.stream);
+  switch (l.head_dim) {
+    case 64: return launch_prefill_d64(a, n_items, s);
+    case 128: return launch_prefill_d128(a, n_items, s);
+    case 256: return launch_prefill_d256(a, n_items, s);
+    case 512: return launch_prefill_d512(a, n_items, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode(const LaunchArgs& l, const rpa_work_item* items, int n_items) {
+  if (n_items <= 0) return hipSuccess;
+  const KernelArgs a = make_args(l, items);
+  hipStream_t s = static_cast<hipStream_t>(l.stream);
+  const int w = l.decode_waves;
+  switch (l.head_dim) {
+    case 64: return launch_decode_d64(a, n_items, w, s);
+    case 128: return launch_decode_d128(a, n_items, w, s);
+    case 256: return launch_decode_d256(a, n_items, w, s);
+    case 512: return launch_decode_d512(a, n_items, w, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_merge(const LaunchArgs& l, int n_groups) {
+  if (n_groups <= 0) return hipSuccess;
+  const KernelArgs a = make_args(l, nullptr);
+  hipStream_t s = static_cast<hipStream_t>(l.stream);
+  switch (l.head_dim) {
+    case 64: return launch_merge_d64(a, n_groups, s);
+    case 128: return launch_merge_d128(a, n_groups, s);
+    case 256: return launch_merge_d256(a, n_groups, s);
+    case 512: return launch_merge_d512(a, n_groups, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace rpa

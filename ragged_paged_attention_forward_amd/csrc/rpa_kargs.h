@@ -1,0 +1,29 @@
+// Kernel argument block shared by the host dispatch and the device code.
+#pragma once
+
+#include <stdint.h>
+
+#include "rpa.h"
+
+namespace rpa {
+
+struct KernelArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* page_table;
+  uint16_t* out;
+  const rpa_work_item* items;
+  const rpa_work_item* groups;
+  float* partial_o;      // [slot][16 rows][D]
+  float* partial_lse;    // [slot][16 rows], base-2 log-sum-exp
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;         // G = Hq / Hkv
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t window;
+  float scale_log2;      // scale * log2(e)
+};
+
+}  // namespace rpa
