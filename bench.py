@@ -10,16 +10,28 @@ default workload is the decode batch: 128 single-token sequences with kv_len
 
 So that no step finds its inputs in the 256 MB last-level cache, the bench
 keeps R replicas of the inputs (at least 1 GiB in total) and step i reads
-replica i mod R.  Per-step HIP events on the launch stream give the kernel
-time behind ``roofline.achieved``; the wall clock over the K timed steps gives
+replica i mod R.  The library's kernel timing (HIP events recorded on the
+launch stream directly around every kernel) gives each kernel's duration
+behind ``roofline.achieved``; the wall clock over the K timed steps gives
 ``value`` and ``ms_per_step``.  The oracle's CPU time on a bounded sample of
 the same workload is reported as ``cpu_baseline``.
 
 Prints ONE JSON line.
+
+Counter runs (HBM traffic of the dominant kernel):
+
+    rocprofv3 --pmc FETCH_SIZE -d DIR_F -o run -- python3 bench.py --steps 8 --warmup 2 \
+        --no-cpu-baseline --copy-calibration
+    rocprofv3 --pmc WRITE_SIZE -d DIR_W -o run -- python3 bench.py ...same...
+    python3 bench.py --pmc-summary DIR_F DIR_W      # writes profiles/traffic_<workload>.json
+
+The copy calibration runs a plain elementwise kernel over a buffer of known
+size in the same process, so that the counters can be scaled to bytes.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -32,42 +44,69 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention tokens/s + achieved TFLOP/s (prefill) and KV GB/s (decode), % of peak"
-HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20
-KERNEL_SOURCE = os.path.join(ROOT, "ragged_paged_attention_forward_amd", "csrc", "rpa_kernels.hip")
-
-# workload -> (dominant kernel name prefix, roofline bound)
-DOMINANT = {
-    "decode": ("rpa_decode_kernel", "hbm"),
-    "tiny": ("rpa_prefill_kernel", "mfma"),
-    "swa_prefill": ("rpa_prefill_kernel", "mfma"),
-    "global_prefill": ("rpa_prefill_kernel", "mfma"),
-    "mixed": ("rpa_prefill_kernel", "mfma"),
-    "mixed_swa": ("rpa_prefill_kernel", "hbm"),
-}
+CSRC = os.path.join(ROOT, "ragged_paged_attention_forward_amd", "csrc")
+COPY_BYTES = 1 << 30            # calibration buffer (read once, written once)
+KERNEL_NAMES = {"prefill": "rpa_prefill_kernel", "decode": "rpa_decode_kernel", "merge": "rpa_merge_kernel"}
+WORKLOADS = ("decode", "tiny", "swa_prefill", "global_prefill", "mixed", "mixed_swa")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every kernel and host source of the library."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("kernel") != kernel:
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
+def kernel_work(w, items):
+    """Algorithmic FLOPs and bytes of each kernel kind for the planned step.
+
+    A sequence belongs to the kernel kind of its work items.  Bytes count Q,
+    the unique K/V rows its queries see and its page-table entries; O goes to
+    the kernel that writes it (the merge for split decode sequences).
+    """
+    from ragged_paged_attention_forward_amd import metrics
+    kind_of = {}
+    split = set()
+    for it in items:
+        kind_of[it["seq"]] = "decode" if it["kind"] == 1 else "prefill"
+        if it["num_splits"] > 1:
+            split.add(it["seq"])
+    out = {}
+    for kind in ("prefill", "decode"):
+        ids = [s for s, k in kind_of.items() if k == kind]
+        seqs = [w.seqs[s] for s in ids]
+        q_b = metrics.qo_bytes(seqs, w.num_q_heads, w.head_dim) // 2
+        o_b = metrics.qo_bytes([w.seqs[s] for s in ids if s not in split], w.num_q_heads, w.head_dim) // 2
+        kv = metrics.kv_bytes(seqs, w.window, w.num_kv_heads, w.head_dim)
+        pages = sum(-(-kvl // w.page_size) for _, kvl in seqs) * 4
+        out[kind] = {"flops": int(metrics.flops(seqs, w.window, w.num_q_heads, w.head_dim)),
+                     "bytes": int(q_b + o_b + kv + pages), "seqs": len(seqs)}
+    # the merge writes O of the split sequences (its fp32 partial reads are overhead)
+    seqs = [w.seqs[s] for s in sorted(split)]
+    out["merge"] = {"flops": 0, "bytes": int(metrics.qo_bytes(seqs, w.num_q_heads, w.head_dim) // 2),
+                    "seqs": len(seqs)}
+    return out
+
+
 def cpu_baseline(w, budget_s: float):
     """Time the fp64 oracle on a bounded sample of the workload on the host cores."""
-    import torch
     import oracle.rpa_oracle as ora
     import rpa_workloads as wl
     try:
@@ -79,53 +118,77 @@ def cpu_baseline(w, budget_s: float):
     inp = wl.make_inputs(w)
     cu = inp.cu_q_lens.tolist()
     t_total = cu[-1]
-    # sample: whole sequences for short ones; a strided set of rows for long prefills
+    # sample: whole sequences for short ones, a random set of rows for long
+    # prefills; passes over the batch repeat until the time budget is spent
     rng = np.random.default_rng(w.seed)
-    order = rng.permutation(w.num_seqs)
     done_tokens = 0
-    t0 = time.perf_counter()
     rows_per_call = 64
-    desc = []
-    for s in order:
-        q_len = cu[s + 1] - cu[s]
-        if q_len == 0:
-            continue
-        if q_len <= rows_per_call:
-            rows = list(range(cu[s], cu[s + 1]))
-        else:
-            rows = sorted(rng.choice(np.arange(cu[s], cu[s + 1]), rows_per_call, replace=False).tolist())
-        ora.forward_rows(inp.q, inp.k_pages, inp.v_pages, inp.page_table, inp.cu_q_lens,
-                         inp.kv_lens, inp.window, inp.scale, rows)
-        done_tokens += len(rows)
-        desc.append(len(rows))
-        if time.perf_counter() - t0 > budget_s:
-            break
+    n_seq = 0
+    passes = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        passes += 1
+        for s in rng.permutation(w.num_seqs):
+            q_len = cu[s + 1] - cu[s]
+            if q_len == 0:
+                continue
+            if q_len <= rows_per_call:
+                rows = list(range(cu[s], cu[s + 1]))
+            else:
+                rows = sorted(rng.choice(np.arange(cu[s], cu[s + 1]), rows_per_call, replace=False).tolist())
+            ora.forward_rows(inp.q, inp.k_pages, inp.v_pages, inp.page_table, inp.cu_q_lens,
+                             inp.kv_lens, inp.window, inp.scale, rows)
+            done_tokens += len(rows)
+            n_seq += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
     el = time.perf_counter() - t0
-    return {"value": done_tokens / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done_tokens} of {t_total} query tokens ({len(desc)} sequences, up to "
-                      f"{rows_per_call} rows each) in {el:.1f} s, fp64 numpy",
+    return {"value": round(done_tokens / el, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done_tokens} query tokens of a {t_total}-token step ({n_seq} sequence "
+                      f"visits over {passes} pass(es), up to {rows_per_call} rows each, fp64 numpy) "
+                      f"in {el:.1f} s",
             "seconds": round(el, 2)}
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=sorted(DOMINANT))
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU time")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = >= 1 GiB total)")
-    args = ap.parse_args(argv)
+def stats_ms(a):
+    a = np.asarray(a, dtype=np.float64)
+    if a.size == 0:
+        return None
+    return {"launches": int(a.size), "mean_ms": round(float(a.mean()), 6),
+            "p10_ms": round(float(np.percentile(a, 10)), 6), "p50_ms": round(float(np.median(a)), 6),
+            "p90_ms": round(float(np.percentile(a, 90)), 6)}
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(sharding is described in the design notes); run with --gpus 1.", file=sys.stderr)
-        return 2
 
+_SLEEP_CAL = []
+
+
+def sleep_cycles_per_ms(torch) -> float:
+    """Cycles of torch.cuda._sleep per millisecond, measured once with events."""
+    if not _SLEEP_CAL:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(20_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CAL.append(20_000_000 / max(a.elapsed_time(b), 1e-3))
+    return _SLEEP_CAL[0]
+
+
+def copy_calibration(torch, dev):
+    """A plain elementwise kernel over COPY_BYTES: reads them once and writes them once."""
+    a = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def run(args):
     import torch
     import rpa_workloads as wl
-    from ragged_paged_attention_forward_amd import RaggedPagedAttention, metrics
+    import ragged_paged_attention_forward_amd as R
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -135,7 +198,6 @@ def main(argv=None):
 
     w = wl.by_name(args.workload)
     host = wl.make_inputs(w)
-    seqs = w.seqs
     t_q = w.total_q
     per_replica = sum(t.numel() * t.element_size() for t in (host.q, host.k_pages, host.v_pages)) * 2
     reps = args.replicas or max(2, int(np.ceil(4 * LLC_BYTES / per_replica)))
@@ -143,12 +205,14 @@ def main(argv=None):
     for _ in range(reps):
         d = host.to(dev)
         replicas.append((d, torch.empty_like(d.q)))
-    cu = host.cu_q_lens.numpy()
-    kv = host.kv_lens.numpy()
+    cu = np.ascontiguousarray(host.cu_q_lens.numpy().astype(np.int32))
+    kv = np.ascontiguousarray(host.kv_lens.numpy().astype(np.int32))
 
-    attn = RaggedPagedAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
-                                w.num_seqs, w.max_pages_per_seq, t_q)
-    info, _ = attn.plan(cu, kv, w.window)
+    attn = R.RaggedPagedAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                                  w.num_seqs, w.max_pages_per_seq, t_q)
+    t_plan = time.perf_counter()
+    info, items = attn.plan(cu, kv, w.window)
+    planner_us = (time.perf_counter() - t_plan) * 1e6
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
@@ -156,43 +220,70 @@ def main(argv=None):
         attn.forward(d.q, d.k_pages, d.v_pages, d.page_table, cu, kv, w.window, w.scale, out=out,
                      stream=stream)
 
+    torch.cuda.synchronize()
+    t_cold = time.perf_counter()
+    step(0)   # builds the plan and uploads the work list
+    torch.cuda.synchronize()
+    cold_ms = (time.perf_counter() - t_cold) * 1e3
     for i in range(args.warmup):
-        step(i)
+        step(1 + i)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: K steps, wall clock, no instrumentation.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        starts[i].record(stream)
-        step(args.warmup + i)
-        ends[i].record(stream)
+        step(1 + args.warmup + i)
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    enqueue_ms = (t_enq - t0) * 1e3 / args.steps
 
-    ms_per_step = wall * 1e3 / args.steps
-    kernel_ms = float(np.mean(ev_ms))
-    flops = metrics.flops(seqs, w.window, w.num_q_heads, w.head_dim)
-    alg_bytes = metrics.total_bytes(seqs, w.window, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                    w.page_size)
-    kvb = metrics.kv_bytes(seqs, w.window, w.num_kv_heads, w.head_dim)
-    assert info["visible_pairs"] == metrics.visible_pairs(seqs, w.window)
+    # Kernel durations: up to --timing-steps of the same steps again with the library's HIP events
+    # around every kernel.  A sleep kernel queued first lets the host run
+    # ahead, so that no kernel waits for its own launch inside its brackets.
+    timed = min(args.steps, args.timing_steps)
+    head_ms = 1.5 * enqueue_ms * timed + 1.0
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, timed)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(head_ms * sleep_cycles_per_ms(torch)))
+    for i in range(timed):
+        step(1 + args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    kernels = {}
+    for name, kind in R.KERNEL_KINDS.items():
+        st = stats_ms(attn.kernel_times(kind))
+        if st is not None:
+            kernels[name] = st
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 0)
 
-    kname, bound = DOMINANT[args.workload]
-    if bound == "hbm":
-        achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
-        peak, unit = HBM_PEAK_GBS, "GB/s"
+    work = kernel_work(w, items)
+    dom = max(kernels, key=lambda k: kernels[k]["mean_ms"])
+    kw = work[dom]
+    k_ms = kernels[dom]["mean_ms"]
+    t_mfma = kw["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = kw["bytes"] / (HBM_PEAK_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        bound, achieved, peak, unit = "mfma", kw["flops"] / (k_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
-        achieved = flops / (kernel_ms * 1e-3) / 1e12
-        peak, unit = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        bound, achieved, peak, unit = "hbm", kw["bytes"] / (k_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": load_traffic(args.workload),
-                "kernel": kname, "kernel_ms_mean": round(kernel_ms, 5),
-                "kernel_ms_p10": round(float(np.percentile(ev_ms, 10)), 5),
-                "kernel_ms_p90": round(float(np.percentile(ev_ms, 90)), 5),
-                "algorithmic_bytes": int(alg_bytes), "algorithmic_flops": int(flops)}
+                "frac": round(achieved / peak, 4),
+                "traffic": load_traffic(args.workload, KERNEL_NAMES[dom]),
+                "kernel": KERNEL_NAMES[dom], "kernel_ms_mean": k_ms,
+                "algorithmic_bytes": kw["bytes"], "algorithmic_flops": kw["flops"],
+                "source_sha256_16": kernel_source_hash()}
+
+    from ragged_paged_attention_forward_amd import metrics
+    step_flops = metrics.flops(w.seqs, w.window, w.num_q_heads, w.head_dim)
+    step_bytes = metrics.total_bytes(w.seqs, w.window, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                     w.page_size)
+    kv_b = metrics.kv_bytes(w.seqs, w.window, w.num_kv_heads, w.head_dim)
+    assert info["visible_pairs"] == metrics.visible_pairs(w.seqs, w.window)
+    ms_per_step = wall * 1e3 / args.steps
+    for name in kernels:
+        kernels[name]["algorithmic_bytes"] = work[name]["bytes"]
+        kernels[name]["algorithmic_flops"] = work[name]["flops"]
 
     res = {
         "metric": METRIC,
@@ -201,27 +292,125 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled page tables)",
         "config": {"workload": args.workload, "description": w.description, "seed": w.seed,
                    "num_seqs": w.num_seqs, "q_tokens": t_q, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "window": w.window, "replicas": reps,
                    "parallelism": "single GPU"},
-        "tflops": round(flops / (kernel_ms * 1e-3) / 1e12, 3),
-        "kv_gbps": round(kvb / (kernel_ms * 1e-3) / 1e9, 1),
+        "step_tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_kv_gbps": round(kv_b / (ms_per_step * 1e-3) / 1e9, 1),
+        "enqueue_ms_per_step": round(enqueue_ms, 6),
+        "planner_us": round(planner_us, 1),
+        "cold_call_ms": round(cold_ms, 3),
+        "kernels": kernels,
         "plan": info,
         "roofline": roofline,
     }
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(res), flush=True)
     attn.close()
     return 0
+
+
+def _pmc_per_dispatch(d, counter):
+    """Per-dispatch values of one counter for every kernel name in a rocprofv3 output dir."""
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    vals = {}
+    for db in dbs:
+        con = sqlite3.connect(db)
+        cols = [r[1] for r in con.execute("pragma table_info(pmc_events)")]
+        key = "dispatch_id" if "dispatch_id" in cols else "rowid"
+        q = (f"select name, {key}, sum(counter_value) from pmc_events where counter_name = ? "
+             f"group by name, {key}")
+        for name, _, v in con.execute(q, (counter,)):
+            vals.setdefault(name, []).append(float(v))
+        con.close()
+    return vals
+
+
+def pmc_summary(args):
+    """Turn a FETCH_SIZE and a WRITE_SIZE run into HBM bytes per launch of the dominant kernel."""
+    fdir, wdir = args.pmc_summary
+    fetch = _pmc_per_dispatch(fdir, "FETCH_SIZE")
+    write = _pmc_per_dispatch(wdir, "WRITE_SIZE")
+
+    def pick(vals, needle):
+        names = [n for n in vals if needle in n]
+        if not names:
+            raise SystemExit(f"no dispatch of {needle} in the counter run")
+        v = [x for n in names for x in vals[n]]
+        return float(np.mean(v)), len(v)
+
+    cf, _ = pick(fetch, "neg")        # KiB per dispatch of the calibration kernel
+    cw, _ = pick(write, "neg")
+    f_scale = COPY_BYTES / (cf * 1024.0)
+    w_scale = COPY_BYTES / (cw * 1024.0)
+    kernel = args.pmc_kernel
+    kf, nf = pick(fetch, kernel)
+    kwr, nw = pick(write, kernel)
+    rec = {
+        "workload": args.workload, "kernel": kernel,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "fetch_kib_per_dispatch": round(kf, 1), "write_kib_per_dispatch": round(kwr, 1),
+        "dispatches": [nf, nw],
+        "calibration": {"kernel": "torch.neg over a bf16 buffer", "bytes": COPY_BYTES,
+                        "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+                        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "hbm_bytes_per_launch": int(round(kf * 1024.0 * f_scale + kwr * 1024.0 * w_scale)),
+        "commands": args.pmc_commands or [],
+    }
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    out = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+    return 0
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode", choices=WORKLOADS)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle CPU time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--timing-steps", type=int, default=200,
+                    help="steps of the event-timed pass (at most --steps)")
+    ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = >= 1 GiB total)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run the elementwise calibration kernel (for counter runs)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (no GPU needed)")
+    ap.add_argument("--pmc-kernel", default="rpa_decode_kernel")
+    ap.add_argument("--pmc-commands", nargs="*")
+    args = ap.parse_args(argv)
+
+    if args.pmc_summary:
+        return pmc_summary(args)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(how it would shard is described in the design notes); run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+    return run(args)
 
 
 if __name__ == "__main__":

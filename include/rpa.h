@@ -126,10 +126,30 @@ enum {
                                     prefill kernel, 2 decode kernel wherever the
                                     rows of a sequence fit one decode item      */
   RPA_OPT_DECODE_MAX_ROWS = 4,   /* most q_len * G rows of a decode item (1..16)  */
-  RPA_OPT_DECODE_WAVES = 5       /* waves per decode workgroup: 0 automatic, 4, 8 */
+  RPA_OPT_DECODE_WAVES = 5,      /* waves per decode workgroup: 0 automatic, 4, 8 */
+  RPA_OPT_KERNEL_TIMING = 6      /* n > 0: time up to n launches per kernel kind
+                                    (see rpa_kernel_times); 0 = off (default),
+                                    n <= 65536                                  */
 };
 /* Returns RPA_OK or RPA_ERR_INVALID_ARG (unknown option or bad value). */
 int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);
+
+/*
+ * Kernel timing.  With RPA_OPT_KERNEL_TIMING = n, every rpa_forward records a
+ * pair of HIP timing events on its stream directly before and after each
+ * kernel it launches, for the first n launches of each kind since the last
+ * read.  The events only mark the stream: results are unchanged.
+ *
+ * rpa_kernel_times -- wait for the recorded launches of `kind` to finish and
+ * copy their durations in milliseconds (GPU time between the two events, in
+ * launch order) to ms[0 .. min(count, capacity)), set *count to the number
+ * recorded, and clear the record of that kind.  `ms` is host memory owned by
+ * the caller (may be NULL when capacity is 0).  Returns RPA_OK,
+ * RPA_ERR_INVALID_ARG (null ctx/count, bad kind, negative capacity) or
+ * RPA_ERR_HIP.
+ */
+enum { RPA_KERNEL_PREFILL = 0, RPA_KERNEL_DECODE = 1, RPA_KERNEL_MERGE = 2 };
+int rpa_kernel_times(rpa_ctx* ctx, int32_t kind, float* ms, int32_t capacity, int32_t* count);
 
 /*
  * Planner introspection (host only, no device call).  The host builds the

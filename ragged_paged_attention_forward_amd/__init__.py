@@ -20,15 +20,19 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import (RPA_ERR_HIP, RPA_ERR_INVALID_ARG, RPA_ERR_OOM, RPA_ERR_UNSUPPORTED, RPA_OK,
+from ._lib import (RPA_ERR_HIP, RPA_ERR_INVALID_ARG, RPA_ERR_OOM, RPA_ERR_UNSUPPORTED,
+                   RPA_KERNEL_DECODE, RPA_KERNEL_MERGE, RPA_KERNEL_PREFILL, RPA_OK,
                    RPA_OPT_DECODE_MAX_ROWS, RPA_OPT_DECODE_SPLIT_KEYS, RPA_OPT_DECODE_WAVES,
-                   RPA_OPT_PATH,
+                   RPA_OPT_KERNEL_TIMING, RPA_OPT_PATH,
                    PlanInfo, RpaError, WorkItem)
 
 __all__ = ["RaggedPagedAttention", "rpa_forward", "RpaError", "library_path", "RPA_OK",
            "RPA_ERR_INVALID_ARG", "RPA_ERR_UNSUPPORTED", "RPA_ERR_OOM", "RPA_ERR_HIP",
            "RPA_OPT_DECODE_SPLIT_KEYS", "RPA_OPT_PATH", "RPA_OPT_DECODE_MAX_ROWS",
-           "RPA_OPT_DECODE_WAVES"]
+           "RPA_OPT_DECODE_WAVES", "RPA_OPT_KERNEL_TIMING", "RPA_KERNEL_PREFILL", "RPA_KERNEL_DECODE",
+           "RPA_KERNEL_MERGE", "KERNEL_KINDS"]
+
+KERNEL_KINDS = {"prefill": RPA_KERNEL_PREFILL, "decode": RPA_KERNEL_DECODE, "merge": RPA_KERNEL_MERGE}
 
 
 def library_path() -> str:
@@ -59,6 +63,9 @@ class RaggedPagedAttention:
         if st != RPA_OK:
             raise RpaError(st, f"rpa_create failed: {self._lib.rpa_status_string(st).decode()}")
         self._ctx = ctx
+        self._timing_cap = 0
+        self._stream_obj = None
+        self._stream_ptr = None
         self.num_q_heads = num_q_heads
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
@@ -86,6 +93,8 @@ class RaggedPagedAttention:
         st = self._lib.rpa_set_option(self._ctx, int(option), int(value))
         if st != RPA_OK:
             raise self._error(st, "rpa_set_option")
+        if option == RPA_OPT_KERNEL_TIMING:
+            self._timing_cap = int(value)
 
     def plan(self, cu_q_lens, kv_lens, window: int = 0) -> Tuple[dict, list]:
         cu = _host_i32(cu_q_lens)
@@ -103,6 +112,20 @@ class RaggedPagedAttention:
         if st != RPA_OK:
             raise self._error(st, "rpa_plan")
         return info.as_dict(), [items[i].as_dict() for i in range(total)]
+
+    def kernel_times(self, kind: int) -> np.ndarray:
+        """Per-launch durations (ms) recorded for a kernel kind since the last read.
+
+        Recording is switched on with ``set_option(RPA_OPT_KERNEL_TIMING, n)``; this
+        waits for the recorded launches to finish and clears their record."""
+        buf = np.zeros(max(self._timing_cap, 1), np.float32)
+        count = ctypes.c_int32(0)
+        st = self._lib.rpa_kernel_times(self._ctx, int(kind),
+                                        buf.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                        int(buf.shape[0]), ctypes.byref(count))
+        if st != RPA_OK:
+            raise self._error(st, "rpa_kernel_times")
+        return buf[:min(count.value, buf.shape[0])].copy()
 
     # -- forward --------------------------------------------------------------
     def forward(self, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
@@ -137,10 +160,16 @@ class RaggedPagedAttention:
             raise ValueError("out must be a contiguous bf16 tensor shaped like q")
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
-        with torch.cuda.device(q.device):
-            st = self._lib.rpa_forward(self._ctx, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
-                                       page_table.data_ptr(), _i32p(cu), _i32p(kv), n, int(window),
-                                       float(scale), out.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        if stream is not self._stream_obj:
+            self._stream_obj, self._stream_ptr = stream, ctypes.c_void_p(stream.cuda_stream)
+        args = (self._ctx, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), page_table.data_ptr(),
+                cu.ctypes.data, kv.ctypes.data, n, int(window), float(scale), out.data_ptr(),
+                self._stream_ptr)
+        if q.device.index == torch.cuda.current_device():
+            st = self._lib.rpa_forward(*args)
+        else:
+            with torch.cuda.device(q.device):
+                st = self._lib.rpa_forward(*args)
         if st != RPA_OK:
             raise self._error(st, "rpa_forward")
         return out

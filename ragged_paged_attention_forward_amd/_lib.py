@@ -17,9 +17,14 @@ RPA_OPT_DECODE_SPLIT_KEYS = 1
 RPA_OPT_PATH = 2
 RPA_OPT_DECODE_MAX_ROWS = 4
 RPA_OPT_DECODE_WAVES = 5
+RPA_OPT_KERNEL_TIMING = 6
+
+RPA_KERNEL_PREFILL = 0
+RPA_KERNEL_DECODE = 1
+RPA_KERNEL_MERGE = 2
 
 EXPORTED = ("rpa_create", "rpa_forward", "rpa_destroy", "rpa_status_string", "rpa_last_error",
-            "rpa_set_option", "rpa_plan")
+            "rpa_set_option", "rpa_plan", "rpa_kernel_times")
 
 
 class Config(ctypes.Structure):
@@ -70,7 +75,8 @@ def load() -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.rpa_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(vp)]
     lib.rpa_create.restype = ctypes.c_int
-    lib.rpa_forward.argtypes = [vp, vp, vp, vp, vp, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+    # host metadata arrays are passed as plain addresses (numpy .ctypes.data)
+    lib.rpa_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
                                 ctypes.c_float, vp, vp]
     lib.rpa_forward.restype = ctypes.c_int
     lib.rpa_destroy.argtypes = [vp]
@@ -84,5 +90,8 @@ def load() -> ctypes.CDLL:
     lib.rpa_plan.argtypes = [vp, i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(PlanInfo),
                              ctypes.POINTER(WorkItem), ctypes.c_int32]
     lib.rpa_plan.restype = ctypes.c_int
+    lib.rpa_kernel_times.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
+                                     i32p]
+    lib.rpa_kernel_times.restype = ctypes.c_int
     _lib = lib
     return lib

@@ -882,7 +882,6 @@ static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t 
   return hipGetLastError();
 }
 
-// Prefill tile shapes per head size: (BN keys, NW waves, NB 32-row blocks per wave).
 // Prefill tile shapes per head size:
 // (D, BN keys per tile, NW waves, NB 32-row blocks per wave, NS pipeline stages).
 #define RPA_PREFILL_SHAPE_64 64, 64, 4, 2, 2
@@ -890,7 +889,7 @@ static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t 
 #define RPA_PREFILL_SHAPE_256 256, 32, 8, 1, 4
 #define RPA_PREFILL_SHAPE_512 512, 32, 4, 1, 2
 
-// Defines the per-head-size entry points used by rpa_dispatch.hip.
+// Defines the per-head-size entry points called by rpa_dispatch.cpp.
 #define RPA_DEFINE_HEAD_DIM(D)                                                              \
   hipError_t launch_prefill_d##D(const KernelArgs& a, int n, hipStream_t s) {               \
     return launch_prefill_t<RPA_PREFILL_SHAPE_##D>(a, n, s);                               \

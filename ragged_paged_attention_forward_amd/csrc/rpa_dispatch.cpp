@@ -9,8 +9,6 @@
 
 namespace rpa {
 
-
-
 hipError_t launch_prefill_d64(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, hipStream_t s);
 hipError_t launch_merge_d64(const KernelArgs& a, int n, hipStream_t s);

@@ -1,4 +1,5 @@
-// Interface between the host library (rpa_api.cpp) and the kernels (rpa_kernels.hip).
+// Interface between the host library (rpa_api.cpp) and the kernel dispatch
+// (rpa_dispatch.cpp, which calls the per-head-size rpa_kernels_d*.hip units).
 #pragma once
 
 #include <hip/hip_runtime_api.h>

@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("rpa_create", "rpa_forward", "rpa_destroy", "rpa_status_string", "rpa_plan"):
+    for n in ("rpa_create", "rpa_forward", "rpa_destroy", "rpa_status_string", "rpa_plan",
+              "rpa_kernel_times"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)
 
@@ -137,6 +138,29 @@ def test_set_option_validation():
     assert lib.rpa_set_option(ctx, 999, 0) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_PATH, 1) == _lib.RPA_OK
     assert lib.rpa_set_option(None, _lib.RPA_OPT_PATH, 1) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_KERNEL_TIMING, -1) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_KERNEL_TIMING, 65537) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_KERNEL_TIMING, 16) == _lib.RPA_OK
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_KERNEL_TIMING, 0) == _lib.RPA_OK
+    lib.rpa_destroy(ctx)
+
+
+def test_kernel_times_validation_and_empty_read():
+    lib, st, ctx = _ctx()
+    count = ctypes.c_int32(-7)
+    buf = (ctypes.c_float * 4)()
+    assert lib.rpa_kernel_times(None, 0, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_kernel_times(ctx, 3, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_kernel_times(ctx, -1, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_kernel_times(ctx, 0, buf, -1, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_kernel_times(ctx, 0, None, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_kernel_times(ctx, 0, buf, 4, None) == _lib.RPA_ERR_INVALID_ARG
+    # nothing recorded yet: count 0, no device call
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_KERNEL_TIMING, 4) == _lib.RPA_OK
+    for kind in (_lib.RPA_KERNEL_PREFILL, _lib.RPA_KERNEL_DECODE, _lib.RPA_KERNEL_MERGE):
+        assert lib.rpa_kernel_times(ctx, kind, buf, 4, ctypes.byref(count)) == _lib.RPA_OK
+        assert count.value == 0
+    assert lib.rpa_kernel_times(ctx, 1, None, 0, ctypes.byref(count)) == _lib.RPA_OK
     lib.rpa_destroy(ctx)
 
 

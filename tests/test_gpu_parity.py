@@ -197,3 +197,25 @@ def test_plan_cache_reuse_and_change():
             attn = make_attn(w, max_num_seqs=4, max_q_tokens=64)
         for _ in range(2):
             compare(run_gpu(attn, inp), oracle_rows(inp), label=f"seed{seed}")
+
+
+def test_kernel_timing_leaves_results_unchanged():
+    """Timing events only mark the stream: same bits, one duration per launch."""
+    w = mixed_small(0, seed=91)
+    inp = wl.make_inputs(w, poison=True)
+    attn = make_attn(w)
+    base = run_gpu(attn, inp).clone()
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 2)
+    for _ in range(3):   # the third call is past the cap and is not recorded
+        timed = run_gpu(attn, inp)
+        assert torch.equal(base, timed)
+    info, _ = attn.plan(inp.cu_q_lens, inp.kv_lens, w.window)
+    for kind, present in ((R.RPA_KERNEL_PREFILL, info["num_prefill_items"] > 0),
+                          (R.RPA_KERNEL_DECODE, info["num_decode_items"] > 0),
+                          (R.RPA_KERNEL_MERGE, info["num_split_groups"] > 0)):
+        t = attn.kernel_times(kind)
+        assert len(t) == (2 if present else 0)
+        assert np.all(t > 0) and np.all(t < 1000)
+        assert len(attn.kernel_times(kind)) == 0   # reading clears the record
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 0)
+    assert torch.equal(base, run_gpu(attn, inp))
