@@ -17,14 +17,14 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "librpa.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-# Kernel translation units, one per head size.  Accumulators of the head
-# sizes up to 256 fit in the architectural VGPRs, where MFMA results can be
-# used by VALU code without copies; head size 512 keeps them in AGPRs.
+# Kernel translation units, one per head size (each may take its own
+# register-allocation options).  MFMA accumulators live in the architectural
+# VGPRs, where the softmax and rescaling code uses them without copies.
 KERNEL_SOURCES = {
     "rpa_kernels_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "rpa_kernels_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "rpa_kernels_d256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "rpa_kernels_d512.hip": [],
+    "rpa_kernels_d512.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 HOST_SOURCES = ["rpa_dispatch.cpp", "rpa_api.cpp", "rpa_plan.cpp"]
 ARCH = "gfx950"

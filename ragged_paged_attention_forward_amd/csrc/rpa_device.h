@@ -176,10 +176,16 @@ RPA_DEV void wait_tile_loads(int later) {
   wait_vmem();
 }
 
-template <int D, int BN, int NW, int NB, int NS>
+// DS = 2 splits the head dimension over a pair of waves: both waves of a pair
+// hold the same 32 query rows, each the Q and O columns of one half of d; the
+// two partial score blocks are added through LDS, so that each wave holds the
+// full scores, runs the same softmax and accumulates its half of O.  This
+// keeps Q and O of d = 512 within one wave's registers.
+template <int D, int BN, int NW, int NB, int NS, int DS = 1>
 struct PrefillCfg {
   static constexpr int NT = NW * 64;
-  static constexpr int ROWS = NW * NB * 32;          // query rows per workgroup
+  static constexpr int DH = D / DS;                  // head columns per wave
+  static constexpr int ROWS = (NW / DS) * NB * 32;   // query rows per workgroup
   static constexpr int ROW_B = D * 2;                // bytes per key row
   static constexpr int RPI = ROW_B >= 1024 ? 1 : 1024 / ROW_B;   // key rows per 1 KB block
   static constexpr int BLOCKS = BN * ROW_B / 1024;   // 1 KB blocks per K or V tile
@@ -205,15 +211,19 @@ struct PrefillCfg {
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert(BLOCKS % NW == 0, "tile must split into 1 KB loads per wave");
   static_assert(16 % RPI == 0, "16-key steps must cover whole blocks");
+  static_assert(DS == 1 || (DS == 2 && NW % 2 == 0 && BN == 32 && NB == 1), "d split: wave pairs, one 32x32 score block");
+  // the score exchange of a d split reuses the K tile of the current stage
+  static_assert(DS == 1 || NW * 4096 <= TILE_K, "score exchange must fit the K tile");
 };
 
 RPA_DEV int xor_k(int s) { return s & 1; }
 RPA_DEV int xor_v(int s) { return (s & 1) * 2; }
 
-template <int D, int BN, int NW, int NB, int NS, bool UNI>
+template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI>
 __global__ void __launch_bounds__(NW * 64, 1)
 rpa_prefill_kernel(KernelArgs args) {
-  using C = PrefillCfg<D, BN, NW, NB, NS>;
+  using C = PrefillCfg<D, BN, NW, NB, NS, DS>;
+  constexpr int DH = C::DH;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   char* lds = reinterpret_cast<char*>(smem);
 
@@ -221,6 +231,8 @@ rpa_prefill_kernel(KernelArgs args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int rw = wave / DS;    // row block of this wave
+  const int dh = wave % DS;    // head-column half of this wave (d split)
   const int n32 = lane & 31;   // MFMA column (query row) / A-operand row (key or d)
   const int lq2 = lane >> 5;   // lane half 0..1
   const int l16 = lane & 15;   // lane within a 16-lane group
@@ -240,30 +252,30 @@ rpa_prefill_kernel(KernelArgs args) {
   int row_pos[NB];
   bool row_ok[NB];
   int64_t row_off[NB];
-  u32x4 qf[NB][D / 16];
+  u32x4 qf[NB][DH / 16];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int r = (wave * NB + nb) * 32 + n32;
+    const int r = (rw * NB + nb) * 32 + n32;
     const int tk = r / G;
     const int hh = r - tk * G;
     row_ok[nb] = tk < it.q_count;
     row_pos[nb] = it.q_pos0 + tk;
     row_off[nb] = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      qf[nb][kk] = row_ok[nb] ? load16(args.q + row_off[nb] + kk * 16 + lq2 * 8) : u32x4{0, 0, 0, 0};
+    for (int kk = 0; kk < DH / 16; ++kk)
+      qf[nb][kk] = row_ok[nb] ? load16(args.q + row_off[nb] + dh * DH + kk * 16 + lq2 * 8) : u32x4{0, 0, 0, 0};
   }
   // positions spanned by this wave's valid rows (tile skipping / mask-free tiles)
-  const int tk_lo = (wave * NB * 32) / G;
-  const int tk_hi_raw = ((wave + 1) * NB * 32 - 1) / G;
+  const int tk_lo = (rw * NB * 32) / G;
+  const int tk_hi_raw = ((rw + 1) * NB * 32 - 1) / G;
   const int tk_hi = tk_hi_raw < it.q_count - 1 ? tk_hi_raw : it.q_count - 1;
   const bool wave_active = tk_lo <= tk_hi;
   const int wpos_lo = it.q_pos0 + tk_lo;
   const int wpos_hi = it.q_pos0 + tk_hi;
 
-  f32x16 o[D / 32][NB];
+  f32x16 o[DH / 32][NB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[db][nb] = f32x16{};
   float m_run[NB], l_run[NB];
@@ -370,13 +382,13 @@ rpa_prefill_kernel(KernelArgs args) {
     // tile fully masked for this wave's rows: nothing to add
     const bool skip = !wave_active || k0 > wpos_hi || k0 + BN <= kv_begin ||
                       (window > 0 && k0 + BN - 1 <= wpos_lo - window);
+    const char* ks = lds + cur * C::STAGE_B;
+    f32x16 sc[BN / 32][NB];
     if (!skip) {
-      const char* ks = lds + cur * C::STAGE_B;
       // ---- S^T = K Q^T ----
       // With a single 32-key block per tile the kk reduction is split over two
       // accumulators, so consecutive MFMAs never wait on each other's result.
       constexpr int NACC = (BN / 32) * NB >= 2 ? 1 : 2;
-      f32x16 sc[BN / 32][NB];
       f32x16 sc2[BN / 32][NB];
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
@@ -386,10 +398,10 @@ rpa_prefill_kernel(KernelArgs args) {
           sc2[kb][nb] = f32x16{};
         }
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
+      for (int kk = 0; kk < DH / 16; ++kk) {
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(ks + kaddr[kb] + kk * 32);
+          const u32x4 a = *reinterpret_cast<const u32x4*>(ks + kaddr[kb] + dh * DH * 2 + kk * 32);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             if (NACC == 2 && (kk & 1)) sc2[kb][nb] = mfma32(a, qf[nb][kk], sc2[kb][nb]);
@@ -403,6 +415,30 @@ rpa_prefill_kernel(KernelArgs args) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) sc[kb][nb] += sc2[kb][nb];
       }
+    }
+    if constexpr (DS == 2) {
+      // ---- d split: add the partner wave's partial scores ----
+      // Every wave has finished its reads of this stage's K tile, whose space
+      // then carries the exchange (16 B per lane and store, lanes contiguous).
+      // Float addition commutes, so both waves of a pair hold identical sums.
+      __syncthreads();
+      f32x4* xb = reinterpret_cast<f32x4*>(lds + cur * C::STAGE_B);
+      if (!skip) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          xb[(wave * 4 + c) * 64 + lane] = f32x4{sc[0][0][4 * c], sc[0][0][4 * c + 1], sc[0][0][4 * c + 2], sc[0][0][4 * c + 3]};
+      }
+      __syncthreads();
+      if (!skip) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 y = xb[((wave ^ 1) * 4 + c) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[0][0][4 * c + e] += y[e];
+        }
+      }
+    }
+    if (!skip) {
       // ---- mask + online softmax (fp32, base 2) ----
       // Scores stay raw; scale*log2(e) is folded into one FMA per element.
       // The running maximum m_run is only raised when a row's new maximum
@@ -439,7 +475,7 @@ rpa_prefill_kernel(KernelArgs args) {
           m_run[nb] = m_new;
           l_run[nb] *= alpha;
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) o[db][nb] *= alpha;
+          for (int db = 0; db < DH / 32; ++db) o[db][nb] *= alpha;
         }
         const float base = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
         float lsum = 0.f;
@@ -464,9 +500,9 @@ rpa_prefill_kernel(KernelArgs args) {
       for (int ks16 = 0; ks16 < BN / 16; ++ks16) {
         const char* vrow = ks + ks16 * (16 / C::RPI) * C::BLK_V;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const u32x2 l2 = lds_read_tr16(vrow + vaddr[0] + db * 64);
-          const u32x2 h2 = lds_read_tr16(vrow + vaddr[1] + db * 64);
+        for (int db = 0; db < DH / 32; ++db) {
+          const u32x2 l2 = lds_read_tr16(vrow + vaddr[0] + dh * DH * 2 + db * 64);
+          const u32x2 h2 = lds_read_tr16(vrow + vaddr[1] + dh * DH * 2 + db * 64);
           const u32x4 a = u32x4{l2[0], l2[1], h2[0], h2[1]};
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) o[db][nb] = mfma32(a, pf[ks16][nb], o[db][nb]);
@@ -488,9 +524,9 @@ rpa_prefill_kernel(KernelArgs args) {
     const float l = l_run[nb] + __shfl_xor(l_run[nb], 32);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (row_ok[nb]) {
-      uint16_t* dst = args.out + row_off[nb] + lq2 * 4;
+      uint16_t* dst = args.out + row_off[nb] + dh * DH + lq2 * 4;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
+      for (int db = 0; db < DH / 32; ++db) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const float* v = reinterpret_cast<const float*>(&o[db][nb]) + 4 * b;
@@ -836,27 +872,27 @@ rpa_decode_kernel(KernelArgs args) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int D, int BN, int NW, int NB, int NS, bool UNI>
+template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI>
 static hipError_t launch_prefill_u(const KernelArgs& a, int n_items, hipStream_t stream) {
-  using C = PrefillCfg<D, BN, NW, NB, NS>;
+  using C = PrefillCfg<D, BN, NW, NB, NS, DS>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, NS, UNI>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, NS, DS, UNI>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, NS, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
+  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, NS, DS, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
                      stream, a);
   return hipGetLastError();
 }
 
-template <int D, int BN, int NW, int NB, int NS>
+template <int D, int BN, int NW, int NB, int NS, int DS>
 static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, hipStream_t stream) {
   // one buffer descriptor per tile needs the tile inside one page and 32-bit offsets
   const bool uni = a.page_size % BN == 0 && int64_t(a.page_size) * a.num_kv_heads * D * 2 < (int64_t(1) << 31);
-  if (uni) return launch_prefill_u<D, BN, NW, NB, NS, true>(a, n_items, stream);
-  return launch_prefill_u<D, BN, NW, NB, NS, false>(a, n_items, stream);
+  if (uni) return launch_prefill_u<D, BN, NW, NB, NS, DS, true>(a, n_items, stream);
+  return launch_prefill_u<D, BN, NW, NB, NS, DS, false>(a, n_items, stream);
 }
 
 template <int D, int NW, bool UNI>
@@ -871,8 +907,10 @@ static hipError_t launch_decode_u(const KernelArgs& a, int n_items, hipStream_t 
 template <int D>
 static hipError_t launch_decode_t(const KernelArgs& a, int n_items, int waves, hipStream_t stream) {
   const bool uni = a.page_size % 32 == 0;
-  if (waves == 8 && D < 512) return uni ? launch_decode_u<D, 8, true>(a, n_items, stream)
-                             : launch_decode_u<D, 8, false>(a, n_items, stream);
+  if constexpr (D < 512) {
+    if (waves == 8) return uni ? launch_decode_u<D, 8, true>(a, n_items, stream)
+                               : launch_decode_u<D, 8, false>(a, n_items, stream);
+  }
   return uni ? launch_decode_u<D, 4, true>(a, n_items, stream) : launch_decode_u<D, 4, false>(a, n_items, stream);
 }
 
@@ -883,11 +921,12 @@ static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t 
 }
 
 // Prefill tile shapes per head size:
-// (D, BN keys per tile, NW waves, NB 32-row blocks per wave, NS pipeline stages).
-#define RPA_PREFILL_SHAPE_64 64, 64, 4, 2, 2
-#define RPA_PREFILL_SHAPE_128 128, 64, 4, 1, 2
-#define RPA_PREFILL_SHAPE_256 256, 32, 8, 1, 4
-#define RPA_PREFILL_SHAPE_512 512, 32, 4, 1, 2
+// (D, BN keys per tile, NW waves, NB 32-row blocks per wave, NS pipeline
+// stages, DS waves sharing a row block by splitting d).
+#define RPA_PREFILL_SHAPE_64 64, 64, 4, 2, 2, 1
+#define RPA_PREFILL_SHAPE_128 128, 64, 4, 1, 2, 1
+#define RPA_PREFILL_SHAPE_256 256, 32, 8, 1, 4, 1
+#define RPA_PREFILL_SHAPE_512 512, 32, 8, 1, 2, 2
 
 // Defines the per-head-size entry points called by rpa_dispatch.cpp.
 #define RPA_DEFINE_HEAD_DIM(D)                                                              \
