@@ -127,9 +127,13 @@ enum {
                                     rows of a sequence fit one decode item      */
   RPA_OPT_DECODE_MAX_ROWS = 4,   /* most q_len * G rows of a decode item (1..16)  */
   RPA_OPT_DECODE_WAVES = 5,      /* waves per decode workgroup: 0 automatic, 4, 8 */
-  RPA_OPT_KERNEL_TIMING = 6      /* n > 0: time up to n launches per kernel kind
+  RPA_OPT_KERNEL_TIMING = 6,     /* n > 0: time up to n launches per kernel kind
                                     (see rpa_kernel_times); 0 = off (default),
                                     n <= 65536                                  */
+  RPA_OPT_XCD_GROUPS = 7         /* prefill launch order: neighbouring tiles go to
+                                    the same one of X chiplets (workgroup b runs
+                                    on chiplet b mod X; MI355X has 8); 0 or 1 =
+                                    plain longest-first order (default), <= 64  */
 };
 /* Returns RPA_OK or RPA_ERR_INVALID_ARG (unknown option or bad value). */
 int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);

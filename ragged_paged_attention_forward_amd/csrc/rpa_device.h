@@ -140,9 +140,23 @@ RPA_DEV f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
 }
 
 // 16 bytes per lane from a buffer straight into LDS at dst + 16 * lane.
+//
+// Written as inline assembly on purpose: the compiler's own form of this load
+// makes it assume that any later LDS read or barrier may depend on the copy,
+// and it then drains every outstanding load (s_waitcnt vmcnt(0)) inside the
+// tile loop, which defeats the multi-stage pipeline.  The kernels order these
+// copies themselves: wait_tile_loads() on the issuing wave, then a barrier.
+// The prefill prologue waits for every load (its own global loads and these
+// copies) before the tile loop, and the loop issues no other vector loads, so
+// a wait the compiler places for its own loads is never too short.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 RPA_DEV void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst, int byte_off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst), 16, byte_off, 0, 0, 0);
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)(dst)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(byte_off), "s"(base), "s"(rs) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 // 16 bytes per lane from a global address straight into LDS at dst + 16 * lane.
 RPA_DEV void global_load_lds16(const char* src, char* dst) {
   __builtin_amdgcn_global_load_lds((global_cptr)(src), (lds_ptr)(dst), 16, 0, 0);
@@ -181,6 +195,19 @@ RPA_DEV void wait_tile_loads(int later) {
 // two partial score blocks are added through LDS, so that each wave holds the
 // full scores, runs the same softmax and accumulates its half of O.  This
 // keeps Q and O of d = 512 within one wave's registers.
+// Scheduling request for a block of N operand fetches of R LDS reads each,
+// every fetch feeding M MFMAs: the first PF fetches are issued up front, then
+// each fetch's MFMAs are followed by the reads of the fetch PF places later.
+template <int N, int PF, int R, int M>
+RPA_DEV void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, PF * R, 0);   // DS reads
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);      // MFMA
+    if (i + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+}
+
 template <int D, int BN, int NW, int NB, int NS, int DS = 1>
 struct PrefillCfg {
   static constexpr int NT = NW * 64;
@@ -367,11 +394,118 @@ rpa_prefill_kernel(KernelArgs args) {
     vaddr[half] = C::TILE_K + (r / C::RPI) * C::BLK_V + sr * C::ROW_B + ((cl ^ xor_v(sr)) * 16) + (l16 & 1) * 8;
   }
 
+  // tile starting at key kt fully masked for this wave's rows: nothing to add
+  auto tile_skipped = [&](int kt) {
+    return !wave_active || kt > wpos_hi || kt + BN <= kv_begin || (window > 0 && kt + BN - 1 <= wpos_lo - window);
+  };
+  // ---- S^T = K Q^T for the K tile at kbuf ----
+  // LDS reads run KPF operands ahead of the MFMAs that use them, so that the
+  // read latency overlaps the matrix work instead of stalling every MFMA.
+  auto scores = [&](const char* kbuf, f32x16 (&acc)[BN / 32][NB]) {
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[kb][nb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + kaddr[kb] + dh * DH * 2 + kk * 32);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[kb][nb] = mfma32(a, qf[nb][kk], acc[kb][nb]);
+      }
+    }
+    constexpr int KREADS = (DH / 16) * (BN / 32);
+    constexpr int KPF = KREADS < 4 ? KREADS : 4;
+    sched_reads_ahead<KREADS, KPF, 1, NB>();
+  };
+
+  // ---- mask + online softmax + O^T += V^T P^T for the tile at ks (keys k0..) ----
+  auto softmax_pv = [&](f32x16 (&sc)[BN / 32][NB], const char* ks, int k0) __attribute__((always_inline)) {
+    // ---- mask + online softmax (fp32, base 2) ----
+    // Scores stay raw; scale*log2(e) is folded into one FMA per element.
+    // The running maximum m_run is only raised when a row's new maximum
+    // exceeds it by more than 8 (in log2 units), so O is rescaled rarely;
+    // every p stays below 2^8 and the result is unchanged because the same
+    // reference maximum enters both O and l.
+    const bool full = (k0 >= kv_begin) && (k0 + BN <= kv_end) && (k0 + BN - 1 <= wpos_lo) &&
+                      (window <= 0 || k0 > wpos_hi - window);
+    u32x4 pf[BN / 16][NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float mx = kNegInf;
+      if (full) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][nb][j]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * lq2 + (j & 3);
+            if (!key_visible(key, row_pos[nb], kv_begin, kv_end, window)) sc[kb][nb][j] = kNegInf;
+            mx = fmaxf(mx, sc[kb][nb][j]);
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mx2 = mx * sl2;   // tile maximum in log2 units (scale > 0)
+      if (__any(mx2 > m_run[nb] + 8.f)) {
+        const float m_new = fmaxf(m_run[nb], mx2);
+        // 0 when the row had no visible key yet; 1 for a row that still has none
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[nb] - m_new);
+        m_run[nb] = m_new;
+        l_run[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DH / 32; ++db) o[db][nb] *= alpha;
+      }
+      const float base = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float p[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            p[i] = fast_exp2(__builtin_fmaf(sc[kb][nb][8 * h + i], sl2, -base));
+            lsum += p[i];
+          }
+          pf[kb * 2 + h][nb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        }
+      }
+      l_run[nb] += lsum;
+    }
+    // ---- O^T += V^T P^T: V^T operands by two transposing reads each ----
+#pragma unroll
+    for (int ks16 = 0; ks16 < BN / 16; ++ks16) {
+      const char* vrow = ks + ks16 * (16 / C::RPI) * C::BLK_V;
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db) {
+        const u32x2 l2 = lds_read_tr16(vrow + vaddr[0] + dh * DH * 2 + db * 64);
+        const u32x2 h2 = lds_read_tr16(vrow + vaddr[1] + dh * DH * 2 + db * 64);
+        const u32x4 a = u32x4{l2[0], l2[1], h2[0], h2[1]};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[db][nb] = mfma32(a, pf[ks16][nb], o[db][nb]);
+      }
+    }
+    constexpr int VOPS = (BN / 16) * (DH / 32);
+    constexpr int VPF = VOPS < 4 ? VOPS : 4;
+    sched_reads_ahead<VOPS, VPF, 2, NB>();
+  };
+
   // NS-stage pipeline: tiles t+1 .. t+NS-1 are in flight while tile t is used.
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t)
     if (t < n_tiles) stage(tile0 + t * BN, t);
-  wait_tile_loads<C::LPT, NS - 2>((n_tiles < NS - 1 ? n_tiles : NS - 1) - 1);
+  if constexpr (UNI) {
+    // Q and the first tiles: every load of the prologue is complete before the loop
+    wait_vmem();
+  } else {
+    wait_tile_loads<C::LPT, NS - 2>((n_tiles < NS - 1 ? n_tiles : NS - 1) - 1);
+  }
   __syncthreads();
 
   for (int tile = 0; tile < n_tiles; ++tile) {
@@ -379,43 +513,10 @@ rpa_prefill_kernel(KernelArgs args) {
     const int cur = tile % NS;
     if (tile + NS - 1 < n_tiles) stage(k0 + (NS - 1) * BN, (tile + NS - 1) % NS);
 
-    // tile fully masked for this wave's rows: nothing to add
-    const bool skip = !wave_active || k0 > wpos_hi || k0 + BN <= kv_begin ||
-                      (window > 0 && k0 + BN - 1 <= wpos_lo - window);
+    const bool skip = tile_skipped(k0);
     const char* ks = lds + cur * C::STAGE_B;
     f32x16 sc[BN / 32][NB];
-    if (!skip) {
-      // ---- S^T = K Q^T ----
-      // With a single 32-key block per tile the kk reduction is split over two
-      // accumulators, so consecutive MFMAs never wait on each other's result.
-      constexpr int NACC = (BN / 32) * NB >= 2 ? 1 : 2;
-      f32x16 sc2[BN / 32][NB];
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          sc[kb][nb] = f32x16{};
-          sc2[kb][nb] = f32x16{};
-        }
-#pragma unroll
-      for (int kk = 0; kk < DH / 16; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(ks + kaddr[kb] + dh * DH * 2 + kk * 32);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            if (NACC == 2 && (kk & 1)) sc2[kb][nb] = mfma32(a, qf[nb][kk], sc2[kb][nb]);
-            else sc[kb][nb] = mfma32(a, qf[nb][kk], sc[kb][nb]);
-          }
-        }
-      }
-      if constexpr (NACC == 2) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) sc[kb][nb] += sc2[kb][nb];
-      }
-    }
+    if (!skip) scores(ks, sc);
     if constexpr (DS == 2) {
       // ---- d split: add the partner wave's partial scores ----
       // Every wave has finished its reads of this stage's K tile, whose space
@@ -438,77 +539,7 @@ rpa_prefill_kernel(KernelArgs args) {
         }
       }
     }
-    if (!skip) {
-      // ---- mask + online softmax (fp32, base 2) ----
-      // Scores stay raw; scale*log2(e) is folded into one FMA per element.
-      // The running maximum m_run is only raised when a row's new maximum
-      // exceeds it by more than 8 (in log2 units), so O is rescaled rarely;
-      // every p stays below 2^8 and the result is unchanged because the same
-      // reference maximum enters both O and l.
-      const bool full = (k0 >= kv_begin) && (k0 + BN <= kv_end) && (k0 + BN - 1 <= wpos_lo) &&
-                        (window <= 0 || k0 > wpos_hi - window);
-      u32x4 pf[BN / 16][NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float mx = kNegInf;
-        if (full) {
-#pragma unroll
-          for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][nb][j]);
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * lq2 + (j & 3);
-              if (!key_visible(key, row_pos[nb], kv_begin, kv_end, window)) sc[kb][nb][j] = kNegInf;
-              mx = fmaxf(mx, sc[kb][nb][j]);
-            }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mx2 = mx * sl2;   // tile maximum in log2 units (scale > 0)
-        if (__any(mx2 > m_run[nb] + 8.f)) {
-          const float m_new = fmaxf(m_run[nb], mx2);
-          // 0 when the row had no visible key yet; 1 for a row that still has none
-          const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[nb] - m_new);
-          m_run[nb] = m_new;
-          l_run[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DH / 32; ++db) o[db][nb] *= alpha;
-        }
-        const float base = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float p[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              p[i] = fast_exp2(__builtin_fmaf(sc[kb][nb][8 * h + i], sl2, -base));
-              lsum += p[i];
-            }
-            pf[kb * 2 + h][nb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-          }
-        }
-        l_run[nb] += lsum;
-      }
-      // ---- O^T += V^T P^T: V^T operands by two transposing reads each ----
-#pragma unroll
-      for (int ks16 = 0; ks16 < BN / 16; ++ks16) {
-        const char* vrow = ks + ks16 * (16 / C::RPI) * C::BLK_V;
-#pragma unroll
-        for (int db = 0; db < DH / 32; ++db) {
-          const u32x2 l2 = lds_read_tr16(vrow + vaddr[0] + dh * DH * 2 + db * 64);
-          const u32x2 h2 = lds_read_tr16(vrow + vaddr[1] + dh * DH * 2 + db * 64);
-          const u32x4 a = u32x4{l2[0], l2[1], h2[0], h2[1]};
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) o[db][nb] = mfma32(a, pf[ks16][nb], o[db][nb]);
-        }
-      }
-    }
+    if (!skip) softmax_pv(sc, ks, k0);
     // tile+1 must have landed; tiles tile+2 .. tile+NS-1 may still be in flight
     {
       const int staged_last = (tile + NS - 1 < n_tiles ? tile + NS - 1 : n_tiles - 1);

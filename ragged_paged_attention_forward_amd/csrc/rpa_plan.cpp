@@ -35,6 +35,27 @@ int32_t range_begin(int64_t pos0, int32_t window) {
   return lo > 0 ? static_cast<int32_t>(lo) : 0;
 }
 
+// Workgroup b of a launch runs on chiplet (XCD) b mod X, and each chiplet has
+// its own L2.  Neighbouring items of the sorted list (consecutive query tiles
+// of one sequence and KV head) read mostly the same keys, so each round of
+// `round` items is cut into X contiguous chunks and chunk x is placed on the
+// launch positions of chiplet x: the tiles a chiplet runs side by side then
+// share their K/V through its L2 instead of each fetching them again.
+void interleave_for_chiplets(std::vector<rpa_work_item>* items, int round, int X) {
+  const int64_t n = static_cast<int64_t>(items->size());
+  if (X <= 1 || round < X || n <= X) return;
+  std::vector<rpa_work_item> out(items->size());
+  for (int64_t r0 = 0; r0 < n; r0 += round) {
+    const int64_t m = std::min<int64_t>(round, n - r0);
+    int64_t src = r0;
+    for (int x = 0; x < X; ++x) {
+      // launch positions r0 + x, r0 + x + X, ... below r0 + m belong to chiplet x
+      for (int64_t pos = x; pos < m; pos += X) out[r0 + pos] = (*items)[src++];
+    }
+  }
+  items->swap(out);
+}
+
 }  // namespace
 
 int validate_metadata(const PlanParams& p, const int32_t* cu, const int32_t* kv,
@@ -142,6 +163,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
                      const int64_t cb = int64_t(b.kv_end - b.kv_begin) * b.q_count;
                      return ca > cb;
                    });
+  interleave_for_chiplets(&out->prefill, p.num_cus, p.xcd_groups);
 
   // Decode split size: enough splits to give every compute unit a few
   // workgroups, in whole multiples of what one workgroup takes per step.

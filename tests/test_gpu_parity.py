@@ -93,6 +93,8 @@ VARIANTS = [
     ("decode_waves8", {R.RPA_OPT_DECODE_WAVES: 8}),
     ("decode_waves8_split32", {R.RPA_OPT_DECODE_WAVES: 8, R.RPA_OPT_DECODE_SPLIT_KEYS: 32}),
     ("decode_waves8_split_none", {R.RPA_OPT_DECODE_WAVES: 8, R.RPA_OPT_DECODE_SPLIT_KEYS: 1 << 20}),
+    ("plain_order", {R.RPA_OPT_XCD_GROUPS: 0}),
+    ("chiplets3", {R.RPA_OPT_XCD_GROUPS: 3}),
 ]
 
 

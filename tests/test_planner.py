@@ -11,7 +11,8 @@ import pytest
 import oracle.rpa_oracle as ora
 import rpa_workloads as wl
 from ragged_paged_attention_forward_amd import (RPA_OPT_DECODE_MAX_ROWS, RPA_OPT_DECODE_SPLIT_KEYS,
-                                                RPA_OPT_PATH, RaggedPagedAttention, metrics)
+                                                RPA_OPT_PATH, RPA_OPT_XCD_GROUPS, RaggedPagedAttention,
+                                                metrics)
 
 
 def plan_for(w, options=()):
@@ -121,11 +122,36 @@ def test_decode_selection_rule():
 
 def test_prefill_tile_rows_and_longest_first():
     w = wl.swa_prefill(tokens=2000)
-    cu, kv, info, items = plan_for(w)
+    cu, kv, info, items = plan_for(w, [(RPA_OPT_XCD_GROUPS, 0)])
     g_ratio = w.num_q_heads // w.num_kv_heads
     assert all(it["q_count"] * g_ratio <= info["prefill_rows"] for it in items)
     cost = [(it["kv_end"] - it["kv_begin"]) * it["q_count"] for it in items]
     assert cost == sorted(cost, reverse=True)
+
+
+@pytest.mark.parametrize("w", [wl.swa_prefill(), wl.global_prefill(tokens=3000), wl.mixed(window=0)],
+                         ids=["swa", "global3000", "mixed"])
+@pytest.mark.parametrize("groups", [8, 3])
+def test_chiplet_order_is_a_chunked_permutation(w, groups):
+    """Launch position b runs on chiplet b mod X: each chiplet's positions in a
+    round of 256 (one workgroup per compute unit) hold one contiguous run of the
+    longest-first list, chiplet 0 first."""
+    plain = [it for it in plan_for(w, [(RPA_OPT_XCD_GROUPS, 0)])[3] if it["kind"] == 0]
+    cu, kv, info, items = plan_for(w, [(RPA_OPT_XCD_GROUPS, groups)])
+    check_plan(w, cu, kv, info, items)
+    got = [it for it in items if it["kind"] == 0]
+    assert len(got) == len(plain)
+    rnd = 256
+    for r0 in range(0, len(plain), rnd):
+        m = min(rnd, len(plain) - r0)
+        src = r0
+        for x in range(groups):
+            for pos in range(x, m, groups):
+                assert got[r0 + pos] == plain[src]
+                src += 1
+        assert src == r0 + m
+    if len(plain) > groups:
+        assert got != plain
 
 
 def test_auto_split_fills_the_chip():
