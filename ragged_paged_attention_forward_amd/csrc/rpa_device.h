@@ -62,11 +62,20 @@ RPA_DEV float xor_sum(float v) {
   return v;
 }
 
-// float -> bf16 bits, round to nearest even (NaN stays NaN).
-RPA_DEV uint32_t bf16_bits(float f) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));
+// Two floats -> packed bf16 pair (lo in bits 0-15), round to nearest even,
+// NaN stays NaN: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+RPA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
-RPA_DEV uint32_t pack_bf16x2(float lo, float hi) { return bf16_bits(lo) | (bf16_bits(hi) << 16); }
+// The same rounding, one value at a time (the decode kernel's register
+// allocation fares better with this form).
+RPA_DEV uint32_t pack_bf16x2_split(float lo, float hi) {
+  const uint32_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
+  const uint32_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
+  return a | (b << 16);
+}
 
 // 8x8 transpose of 16-bit elements held as 8 rows of 16 bytes: out[e] holds
 // element e of rows 0..7 (row j in half-word j).
@@ -107,6 +116,17 @@ RPA_DEV int32_t uniform_load(const int32_t* p, int idx) {
 
 RPA_DEV bool key_visible(int key, int pos, int kv_begin, int kv_end, int window) {
   return key >= kv_begin && key < kv_end && key <= pos && (window <= 0 || key > pos - window);
+}
+// The keys that key_visible() admits for position pos form one range
+// [lo, lo + span]: key (>= 0) is visible iff unsigned(key - lo) <=
+// unsigned(span).  An empty range is encoded as lo = -2^30, span = 0, which
+// no key >= 0 passes.
+RPA_DEV void visible_range(int pos, int kv_begin, int kv_end, int window, int& lo, int& span) {
+  int a = kv_begin;
+  if (window > 0 && pos - window + 1 > a) a = pos - window + 1;
+  const int b = pos < kv_end - 1 ? pos : kv_end - 1;
+  lo = b >= a ? a : -(1 << 30);
+  span = b >= a ? b - a : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -277,6 +297,7 @@ rpa_prefill_kernel(KernelArgs args) {
 
   // ---- rows of this lane, Q fragments (B operand of S^T = K Q^T) ----
   int row_pos[NB];
+  int vis_lo[NB], vis_span[NB];   // visible keys of the lane's rows (visible_range)
   bool row_ok[NB];
   int64_t row_off[NB];
   u32x4 qf[NB][DH / 16];
@@ -287,6 +308,7 @@ rpa_prefill_kernel(KernelArgs args) {
     const int hh = r - tk * G;
     row_ok[nb] = tk < it.q_count;
     row_pos[nb] = it.q_pos0 + tk;
+    visible_range(row_pos[nb], it.kv_begin, it.kv_end, args.window, vis_lo[nb], vis_span[nb]);
     row_off[nb] = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
 #pragma unroll
     for (int kk = 0; kk < DH / 16; ++kk)
@@ -336,6 +358,8 @@ rpa_prefill_kernel(KernelArgs args) {
   }
   int st_pidx = tile0 / page_size;
   int st_slot = tile0 - st_pidx * page_size;
+  // page of the next tile to stage, looked up one stage ahead (scalar load)
+  int64_t st_page = (UNI && n_tiles > 0) ? uniform_load(pt_row, st_pidx) : 0;
 
   auto stage = [&](int k0, int buf) {
     char* kdst = lds + buf * C::STAGE_B + wave * C::LOADS * C::BLK_K;
@@ -345,13 +369,14 @@ rpa_prefill_kernel(KernelArgs args) {
       // The tile lies in one page.  Rows [k0, hi) are real keys of the
       // sequence (rows below kv_begin are masked later); rows past hi read as
       // zero through the buffer's record count.
-      const int64_t page = uniform_load(pt_row, st_pidx);
+      const int64_t page = st_page;
       const int64_t base_off = ((page * page_size + st_slot) * hkv + g) * D;
       st_slot += BN;
       if (st_slot == page_size) {
         st_slot = 0;
         ++st_pidx;
       }
+      if (k0 + BN < kv_end) st_page = uniform_load(pt_row, st_pidx);
       const uint32_t nbytes = static_cast<uint32_t>((hi - k0 - 1) * row_bytes + D * 2);
       const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + base_off, nbytes);
       const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + base_off, nbytes);
@@ -440,12 +465,14 @@ rpa_prefill_kernel(KernelArgs args) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][nb][j]);
       } else {
+        // key - lo for element j of block kb is rel + kb*32 + 8*(j/4) + (j%4)
+        const int rel = k0 + 4 * lq2 - vis_lo[nb];
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * lq2 + (j & 3);
-            if (!key_visible(key, row_pos[nb], kv_begin, kv_end, window)) sc[kb][nb][j] = kNegInf;
+            const uint32_t d = static_cast<uint32_t>(rel + kb * 32 + 8 * (j >> 2) + (j & 3));
+            if (d > static_cast<uint32_t>(vis_span[nb])) sc[kb][nb][j] = kNegInf;
             mx = fmaxf(mx, sc[kb][nb][j]);
           }
       }
@@ -496,24 +523,38 @@ rpa_prefill_kernel(KernelArgs args) {
     sched_reads_ahead<VOPS, VPF, 2, NB>();
   };
 
-  // NS-stage pipeline: tiles t+1 .. t+NS-1 are in flight while tile t is used.
+  // NS-stage pipeline, TPB tiles per step: while the TPB tiles of a step are
+  // used, the loads of the next NS - TPB tiles are in flight.  One barrier per
+  // step guards the reuse of the buffers (two tiles per step halve the
+  // barriers, waits and page lookups per tile when four stages fit).
+  constexpr int TPB = (DS == 1 && NS >= 4) ? 2 : 1;
+  static_assert(NS > TPB, "a step's loads need buffers of their own");
 #pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
+  for (int t = 0; t < NS - TPB; ++t)
     if (t < n_tiles) stage(tile0 + t * BN, t);
   if constexpr (UNI) {
     // Q and the first tiles: every load of the prologue is complete before the loop
     wait_vmem();
   } else {
-    wait_tile_loads<C::LPT, NS - 2>((n_tiles < NS - 1 ? n_tiles : NS - 1) - 1);
+    // the first step's tiles must have landed
+    const int later = (n_tiles < NS - TPB ? n_tiles : NS - TPB) - TPB;
+    wait_tile_loads<C::LPT, NS - 2 * TPB>(later < 0 ? 0 : later);
   }
   __syncthreads();
 
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  for (int step0 = 0; step0 < n_tiles; step0 += TPB) {
+#pragma unroll
+  for (int s = 0; s < TPB; ++s) {
+    const int ts = step0 + NS - TPB + s;   // into the buffer of tile step0 - TPB + s
+    if (ts < n_tiles) stage(tile0 + ts * BN, ts % NS);
+  }
+#pragma unroll
+  for (int s = 0; s < TPB; ++s) {
+    const int tile = step0 + s;
     const int k0 = tile0 + tile * BN;
     const int cur = tile % NS;
-    if (tile + NS - 1 < n_tiles) stage(k0 + (NS - 1) * BN, (tile + NS - 1) % NS);
-
-    const bool skip = tile_skipped(k0);
+    // (the last step may hold one tile fewer than TPB)
+    const bool skip = (TPB > 1 && tile >= n_tiles) || tile_skipped(k0);
     const char* ks = lds + cur * C::STAGE_B;
     f32x16 sc[BN / 32][NB];
     if (!skip) scores(ks, sc);
@@ -540,11 +581,12 @@ rpa_prefill_kernel(KernelArgs args) {
       }
     }
     if (!skip) softmax_pv(sc, ks, k0);
-    // tile+1 must have landed; tiles tile+2 .. tile+NS-1 may still be in flight
+  }
+    // the next step's tiles must have landed; later ones may still be in flight
     {
-      const int staged_last = (tile + NS - 1 < n_tiles ? tile + NS - 1 : n_tiles - 1);
-      const int later = staged_last - (tile + 1);
-      wait_tile_loads<C::LPT, NS - 2>(later < 0 ? 0 : later);
+      const int staged_last = (step0 + NS - 1 < n_tiles ? step0 + NS - 1 : n_tiles - 1);
+      const int later = staged_last - (step0 + 2 * TPB - 1);
+      wait_tile_loads<C::LPT, NS - 2 * TPB>(later < 0 ? 0 : later);
     }
     __syncthreads();
   }
@@ -801,8 +843,8 @@ rpa_decode_kernel(KernelArgs args) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) lsum += p[j];
     l_run = l_run * alpha + lsum;
-    const u32x4 pf = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    const u32x4 pf = {pack_bf16x2_split(p[0], p[1]), pack_bf16x2_split(p[2], p[3]),
+                      pack_bf16x2_split(p[4], p[5]), pack_bf16x2_split(p[6], p[7])};
 #pragma unroll
     for (int u = 0; u < C::NU; ++u) {
       u32x4 vt[8];
@@ -880,8 +922,8 @@ rpa_decode_kernel(KernelArgs args) {
         const int c = u * 16 + lq * 4 + j;
         if (c < C::NCH)
           *reinterpret_cast<u32x4*>(dst + c * 8) =
-              u32x4{pack_bf16x2(o[u][0][j], o[u][1][j]), pack_bf16x2(o[u][2][j], o[u][3][j]),
-                    pack_bf16x2(o[u][4][j], o[u][5][j]), pack_bf16x2(o[u][6][j], o[u][7][j])};
+              u32x4{pack_bf16x2_split(o[u][0][j], o[u][1][j]), pack_bf16x2_split(o[u][2][j], o[u][3][j]),
+                    pack_bf16x2_split(o[u][4][j], o[u][5][j]), pack_bf16x2_split(o[u][6][j], o[u][7][j])};
       }
   } else {
     const int64_t slot = static_cast<int64_t>(it.partial_base) + it.split_index;
