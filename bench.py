@@ -74,12 +74,13 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def kernel_work(w, items):
+def kernel_work(w, items, merge_kernel=True):
     """Algorithmic FLOPs and bytes of each kernel kind for the planned step.
 
     A sequence belongs to the kernel kind of its work items.  Bytes count Q,
     the unique K/V rows its queries see and its page-table entries; O goes to
-    the kernel that writes it (the merge for split decode sequences).
+    the kernel that writes it (the merge kernel for split decode sequences
+    when it runs, else the decode kernel, whose last split merges them).
     """
     from ragged_paged_attention_forward_amd import metrics
     kind_of = {}
@@ -93,7 +94,8 @@ def kernel_work(w, items):
         ids = [s for s, k in kind_of.items() if k == kind]
         seqs = [w.seqs[s] for s in ids]
         q_b = metrics.qo_bytes(seqs, w.num_q_heads, w.head_dim) // 2
-        o_b = metrics.qo_bytes([w.seqs[s] for s in ids if s not in split], w.num_q_heads, w.head_dim) // 2
+        o_ids = ids if (kind == "decode" and not merge_kernel) else [s for s in ids if s not in split]
+        o_b = metrics.qo_bytes([w.seqs[s] for s in o_ids], w.num_q_heads, w.head_dim) // 2
         kv = metrics.kv_bytes(seqs, w.window, w.num_kv_heads, w.head_dim)
         pages = sum(-(-kvl // w.page_size) for _, kvl in seqs) * 4
         out[kind] = {"flops": int(metrics.flops(seqs, w.window, w.num_q_heads, w.head_dim)),
@@ -257,7 +259,7 @@ def run(args):
             kernels[name] = st
     attn.set_option(R.RPA_OPT_KERNEL_TIMING, 0)
 
-    work = kernel_work(w, items)
+    work = kernel_work(w, items, merge_kernel="merge" in kernels)
     dom = max(kernels, key=lambda k: kernels[k]["mean_ms"])
     kw = work[dom]
     k_ms = kernels[dom]["mean_ms"]

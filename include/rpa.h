@@ -126,14 +126,19 @@ enum {
                                     prefill kernel, 2 decode kernel wherever the
                                     rows of a sequence fit one decode item      */
   RPA_OPT_DECODE_MAX_ROWS = 4,   /* most q_len * G rows of a decode item (1..16)  */
-  RPA_OPT_DECODE_WAVES = 5,      /* waves per decode workgroup: 0 automatic, 4, 8 */
+  RPA_OPT_DECODE_WAVES = 5,      /* waves per decode workgroup: 0 automatic (8
+                                    below head size 512, else 4), 4, 8 (head
+                                    size 512 always runs 4)                     */
   RPA_OPT_KERNEL_TIMING = 6,     /* n > 0: time up to n launches per kernel kind
                                     (see rpa_kernel_times); 0 = off (default),
                                     n <= 65536                                  */
-  RPA_OPT_XCD_GROUPS = 7         /* prefill launch order: neighbouring tiles go to
+  RPA_OPT_XCD_GROUPS = 7,        /* prefill launch order: neighbouring tiles go to
                                     the same one of X chiplets (workgroup b runs
                                     on chiplet b mod X; MI355X has 8); 0 or 1 =
                                     plain longest-first order (default), <= 64  */
+  RPA_OPT_FUSED_MERGE = 8        /* 1 (default): the decode split that finishes
+                                    last merges its group's partials; 0: a
+                                    separate merge kernel does (same result)    */
 };
 /* Returns RPA_OK or RPA_ERR_INVALID_ARG (unknown option or bad value). */
 int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);

@@ -19,6 +19,7 @@ RPA_OPT_DECODE_MAX_ROWS = 4
 RPA_OPT_DECODE_WAVES = 5
 RPA_OPT_KERNEL_TIMING = 6
 RPA_OPT_XCD_GROUPS = 7
+RPA_OPT_FUSED_MERGE = 8
 
 RPA_KERNEL_PREFILL = 0
 RPA_KERNEL_DECODE = 1

@@ -613,18 +613,25 @@ rpa_prefill_kernel(KernelArgs args) {
 
 // ---------------------------------------------------------------------------
 // Split merge: out = sum_i 2^(lse_i - M) O_i / sum_i 2^(lse_i - M), M = max_i lse_i.
-// One workgroup per group; each thread owns one 4-float column of one row.
+// One workgroup per group; each thread owns one 4-float column of one row,
+// with enough threads (MergeCfg::THREADS) that a decode group's 16 x D/4 columns
+// take at most two passes and each thread's loads are in flight together.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(256) rpa_merge_kernel(KernelArgs args) {
+struct MergeCfg {
+  static constexpr int THREADS = 4 * D < 1024 ? 4 * D : 1024;
+};
+// Merges the n partials of one split group (rows q_count * G of tokens from
+// q_start, KV head kv_head) into the bf16 output; threads tid of nthreads.
+template <int D>
+RPA_DEV void merge_group(const KernelArgs& args, int q_start, int q_count, int kv_head, int partial_base,
+                         int n, int tid, int nthreads) {
   constexpr int C4 = D / 4;
   constexpr int NB = 8;   // splits fetched per batch: every load of a batch is in flight at once
-  const rpa_work_item grp = args.groups[blockIdx.x];
-  const int rows = grp.q_count * args.group;
-  const int n = grp.num_splits;
-  const float* lse = args.partial_lse + static_cast<int64_t>(grp.partial_base) * 16;
-  const float* po = args.partial_o + static_cast<int64_t>(grp.partial_base) * 16 * D;
-  for (int idx = threadIdx.x; idx < rows * C4; idx += blockDim.x) {
+  const int rows = q_count * args.group;
+  const float* lse = args.partial_lse + static_cast<int64_t>(partial_base) * 16;
+  const float* po = args.partial_o + static_cast<int64_t>(partial_base) * 16 * D;
+  for (int idx = tid; idx < rows * C4; idx += nthreads) {
     const int r = idx / C4;
     const int c = idx - r * C4;
     float mx = kNegInf, wsum = 0.f;
@@ -657,10 +664,17 @@ __global__ void __launch_bounds__(256) rpa_merge_kernel(KernelArgs args) {
     acc *= wsum > 0.f ? 1.f / wsum : 0.f;
     const int tk = r / args.group;
     const int hh = r - tk * args.group;
-    uint16_t* dst = args.out + (static_cast<int64_t>(grp.q_start + tk) * args.num_q_heads +
-                                grp.kv_head * args.group + hh) * D + c * 4;
+    uint16_t* dst = args.out + (static_cast<int64_t>(q_start + tk) * args.num_q_heads +
+                                kv_head * args.group + hh) * D + c * 4;
     *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
   }
+}
+
+template <int D>
+__global__ void __launch_bounds__(MergeCfg<D>::THREADS) rpa_merge_kernel(KernelArgs args) {
+  const rpa_work_item grp = args.groups[blockIdx.x];
+  merge_group<D>(args, grp.q_start, grp.q_count, grp.kv_head, grp.partial_base, grp.num_splits,
+                 threadIdx.x, blockDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -675,7 +689,7 @@ struct DecodeCfg {
   static constexpr int NU = (NCH + 15) / 16;          // V chunk rounds per lane
   static constexpr int OSTRIDE = D + 4;               // floats per LDS row (padded)
   static constexpr int LDS_O = (NW / 2) * 16 * OSTRIDE; // tree-combine slots
-  static constexpr int LDS_BYTES = LDS_O * 4 + NW * 16 * 2 * 4;
+  static constexpr int LDS_BYTES = LDS_O * 4 + NW * 16 * 2 * 4 + 16;   // + merge flag
 };
 
 // Second launch bound: waves per SIMD to fit (two, so a compute unit holds two
@@ -688,6 +702,7 @@ rpa_decode_kernel(KernelArgs args) {
   float* lds_o = dsm;                     // [NW/2][16][OSTRIDE]
   float* lds_m = dsm + C::LDS_O;          // [NW][16]
   float* lds_l = lds_m + NW * 16;         // [NW][16]
+  int* lds_flag = reinterpret_cast<int*>(lds_l + NW * 16);
 
   const rpa_work_item it = args.items[blockIdx.x];
   const int tid = threadIdx.x;
@@ -909,11 +924,10 @@ rpa_decode_kernel(KernelArgs args) {
     }
     if (half > 1) __syncthreads();
   }
-  if (wave != 0 || !row_ok) return;
-
   // ---- wave 0 writes the output row (or the split's partial) from registers ----
   const bool split = it.split_group >= 0;
   if (!split) {
+    if (wave != 0 || !row_ok) return;
     uint16_t* dst = args.out + q_off;
 #pragma unroll
     for (int u = 0; u < C::NU; ++u)
@@ -925,7 +939,9 @@ rpa_decode_kernel(KernelArgs args) {
               u32x4{pack_bf16x2_split(o[u][0][j], o[u][1][j]), pack_bf16x2_split(o[u][2][j], o[u][3][j]),
                     pack_bf16x2_split(o[u][4][j], o[u][5][j]), pack_bf16x2_split(o[u][6][j], o[u][7][j])};
       }
-  } else {
+    return;
+  }
+  if (wave == 0 && row_ok) {
     const int64_t slot = static_cast<int64_t>(it.partial_base) + it.split_index;
     float* dst = args.partial_o + (slot * 16 + ln) * D;
 #pragma unroll
@@ -940,6 +956,29 @@ rpa_decode_kernel(KernelArgs args) {
       }
     if (lq == 0) args.partial_lse[slot * 16 + ln] = (lsum > 0.f) ? base + __builtin_log2f(lsum) : kNegInf;
   }
+  if (!args.fused_merge) return;
+
+  // ---- last split of the group merges it (the group's ticket counts arrivals) ----
+  // The workspace is uncached device memory: the stores above reach memory,
+  // where every workgroup's loads and the ticket atomic see them, once this
+  // wave's vmcnt reaches zero.  The split that draws the last ticket then
+  // reads all partials back (its own included) and merges them in split order
+  // with the same arithmetic as the merge kernel, and resets the ticket for
+  // the next call.
+  if (wave == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int ticket = 0;
+    if (lane == 0)
+      ticket = __hip_atomic_fetch_add(args.merge_tickets + it.split_group, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    ticket = __shfl(ticket, 0);
+    if (lane == 0) *lds_flag = (ticket == it.num_splits - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (*lds_flag == 0) return;
+  asm volatile("" ::: "memory");
+  merge_group<D>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, tid, C::NT);
+  if (tid == 0) __hip_atomic_store(args.merge_tickets + it.split_group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -989,7 +1028,7 @@ static hipError_t launch_decode_t(const KernelArgs& a, int n_items, int waves, h
 
 template <int D>
 static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t stream) {
-  hipLaunchKernelGGL((rpa_merge_kernel<D>), dim3(n_groups), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((rpa_merge_kernel<D>), dim3(n_groups), dim3(MergeCfg<D>::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -49,6 +49,8 @@ static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
   a.groups = l.groups;
   a.partial_o = l.partial_o;
   a.partial_lse = l.partial_lse;
+  a.merge_tickets = l.merge_tickets;
+  a.fused_merge = l.fused_merge;
   a.num_q_heads = l.num_q_heads;
   a.num_kv_heads = l.num_kv_heads;
   a.group = l.num_q_heads / l.num_kv_heads;

@@ -18,6 +18,8 @@ struct LaunchArgs {
   const rpa_work_item* groups;  // device
   float* partial_o;             // device [slots][16][D]
   float* partial_lse;           // device [slots][16]
+  int32_t* merge_tickets;       // device [groups], zero between calls
+  int32_t fused_merge;          // 1: decode kernel merges split groups itself
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;

@@ -146,6 +146,9 @@ def test_set_option_validation():
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_XCD_GROUPS, 65) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_XCD_GROUPS, 0) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_XCD_GROUPS, 8) == _lib.RPA_OK
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FUSED_MERGE, 2) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FUSED_MERGE, 0) == _lib.RPA_OK
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FUSED_MERGE, 1) == _lib.RPA_OK
     lib.rpa_destroy(ctx)
 
 

@@ -91,9 +91,14 @@ VARIANTS = [
     ("split_none", {R.RPA_OPT_DECODE_SPLIT_KEYS: 1 << 20}),
     ("decode_rows8", {R.RPA_OPT_DECODE_MAX_ROWS: 8}),
     ("decode_waves8", {R.RPA_OPT_DECODE_WAVES: 8}),
+    ("decode_waves4", {R.RPA_OPT_DECODE_WAVES: 4}),
+    ("decode_waves4_split32", {R.RPA_OPT_DECODE_WAVES: 4, R.RPA_OPT_DECODE_SPLIT_KEYS: 32}),
+    ("decode_waves4_split_none", {R.RPA_OPT_DECODE_WAVES: 4, R.RPA_OPT_DECODE_SPLIT_KEYS: 1 << 20}),
     ("decode_waves8_split32", {R.RPA_OPT_DECODE_WAVES: 8, R.RPA_OPT_DECODE_SPLIT_KEYS: 32}),
     ("decode_waves8_split_none", {R.RPA_OPT_DECODE_WAVES: 8, R.RPA_OPT_DECODE_SPLIT_KEYS: 1 << 20}),
     ("plain_order", {R.RPA_OPT_XCD_GROUPS: 0}),
+    ("merge_kernel", {R.RPA_OPT_FUSED_MERGE: 0}),
+    ("merge_kernel_split32", {R.RPA_OPT_FUSED_MERGE: 0, R.RPA_OPT_DECODE_SPLIT_KEYS: 32}),
     ("chiplets3", {R.RPA_OPT_XCD_GROUPS: 3}),
 ]
 
@@ -214,10 +219,39 @@ def test_kernel_timing_leaves_results_unchanged():
     info, _ = attn.plan(inp.cu_q_lens, inp.kv_lens, w.window)
     for kind, present in ((R.RPA_KERNEL_PREFILL, info["num_prefill_items"] > 0),
                           (R.RPA_KERNEL_DECODE, info["num_decode_items"] > 0),
-                          (R.RPA_KERNEL_MERGE, info["num_split_groups"] > 0)):
+                          (R.RPA_KERNEL_MERGE, False)):   # merged inside the decode kernel
         t = attn.kernel_times(kind)
         assert len(t) == (2 if present else 0)
         assert np.all(t > 0) and np.all(t < 1000)
         assert len(attn.kernel_times(kind)) == 0   # reading clears the record
     attn.set_option(R.RPA_OPT_KERNEL_TIMING, 0)
     assert torch.equal(base, run_gpu(attn, inp))
+
+
+@pytest.mark.parametrize("window", [0, 300])
+def test_fused_merge_matches_merge_kernel_bitwise(window):
+    """The last split merges its group with the merge kernel's arithmetic:
+    same bits as the separate merge kernel, over repeated calls (the tickets
+    must return to zero after every call)."""
+    w = wl.custom([(1, int(k)) for k in np.random.default_rng(5).integers(40, 3000, 96)] + [(3, 700), (2, 2)],
+                  8, 1, 256, 128, window, seed=17)
+    inp = wl.make_inputs(w, poison=True)
+    ref = oracle_rows(inp)
+    sep = make_attn(w)
+    sep.set_option(R.RPA_OPT_FUSED_MERGE, 0)
+    sep.set_option(R.RPA_OPT_DECODE_SPLIT_KEYS, 64)
+    base = run_gpu(sep, inp).clone()
+    compare(base, ref, label="merge kernel")
+    fused = make_attn(w)
+    fused.set_option(R.RPA_OPT_DECODE_SPLIT_KEYS, 64)
+    info, _ = fused.plan(inp.cu_q_lens, inp.kv_lens, window)
+    assert info["num_split_groups"] > 50
+    for _ in range(3):
+        got = run_gpu(fused, inp)
+        assert torch.equal(got, base)
+    for d in (64, 512):   # other head sizes, several KV heads
+        w2 = wl.custom([(1, 900), (2, 333), (1, 70), (4, 1500)], 16, 4 if d == 64 else 2, d, 64, window, seed=d)
+        inp2 = wl.make_inputs(w2, poison=True)
+        a = make_attn(w2)
+        a.set_option(R.RPA_OPT_DECODE_SPLIT_KEYS, 64)
+        compare(run_gpu(a, inp2), oracle_rows(inp2), label=f"fused d{d}")
