@@ -9,8 +9,8 @@ default workload is the decode batch: 128 single-token sequences with kv_len
 ~ U[64, 640], 8 query heads sharing one KV head of width 256, 128-token pages.
 
 So that no step finds its inputs in the 256 MB last-level cache, the bench
-keeps R replicas of the inputs (at least 1 GiB in total) and step i reads
-replica i mod R.  The library's kernel timing (HIP events recorded on the
+keeps R replicas of the inputs (at least 1 GiB in total, at most 64 of them:
+a workload of a few KB stays cache resident) and step i reads replica i mod R.  The library's kernel timing (HIP events recorded on the
 launch stream directly around every kernel) gives each kernel's duration
 behind ``roofline.achieved``; the wall clock over the K timed steps gives
 ``value`` and ``ms_per_step``.  The oracle's CPU time on a bounded sample of
@@ -202,7 +202,9 @@ def run(args):
     host = wl.make_inputs(w)
     t_q = w.total_q
     per_replica = sum(t.numel() * t.element_size() for t in (host.q, host.k_pages, host.v_pages)) * 2
-    reps = args.replicas or max(2, int(np.ceil(4 * LLC_BYTES / per_replica)))
+    # enough replicas that the set exceeds the last-level cache four times,
+    # at most 64 (small workloads then stay cache resident, like in serving)
+    reps = args.replicas or min(64, max(2, int(np.ceil(4 * LLC_BYTES / per_replica))))
     replicas = []
     for _ in range(reps):
         d = host.to(dev)

@@ -255,3 +255,18 @@ def test_fused_merge_matches_merge_kernel_bitwise(window):
         a = make_attn(w2)
         a.set_option(R.RPA_OPT_DECODE_SPLIT_KEYS, 64)
         compare(run_gpu(a, inp2), oracle_rows(inp2), label=f"fused d{d}")
+
+
+def test_long_contexts_sampled():
+    """Decodes over 40K-key contexts (many splits per group) and a 2048-token
+    chunk on a 30K prefix, with and without a window; sampled rows."""
+    seqs = [(1, 40_000), (1, 23_457), (2048, 30_000), (1, 129), (3, 17_001)]
+    for window in (0, 1024):
+        w = wl.custom(seqs, 8, 1, 256, 128, window, seed=71 + window)
+        inp = wl.make_inputs(w, poison=True)
+        got = run_gpu(make_attn(w), inp)
+        t = w.total_q
+        cu = inp.cu_q_lens.tolist()
+        must = [0, 1, cu[2], cu[2] + 1, cu[3] - 1, cu[3], t - 1, t - 2, t - 3]
+        rows = wl.sample_rows(t, 24, w.seed, must)
+        compare(got, oracle_rows(inp, rows), rows=rows, label=f"long w{window}")
