@@ -298,21 +298,19 @@ rpa_prefill_kernel(KernelArgs args) {
   // ---- rows of this lane, Q fragments (B operand of S^T = K Q^T) ----
   int row_pos[NB];
   int vis_lo[NB], vis_span[NB];   // visible keys of the lane's rows (visible_range)
-  bool row_ok[NB];
-  int64_t row_off[NB];
   u32x4 qf[NB][DH / 16];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int r = (rw * NB + nb) * 32 + n32;
     const int tk = r / G;
     const int hh = r - tk * G;
-    row_ok[nb] = tk < it.q_count;
+    const bool row_ok = tk < it.q_count;
     row_pos[nb] = it.q_pos0 + tk;
     visible_range(row_pos[nb], it.kv_begin, it.kv_end, args.window, vis_lo[nb], vis_span[nb]);
-    row_off[nb] = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
+    const int64_t row_off = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
 #pragma unroll
     for (int kk = 0; kk < DH / 16; ++kk)
-      qf[nb][kk] = row_ok[nb] ? load16(args.q + row_off[nb] + dh * DH + kk * 16 + lq2 * 8) : u32x4{0, 0, 0, 0};
+      qf[nb][kk] = row_ok ? load16(args.q + row_off + dh * DH + kk * 16 + lq2 * 8) : u32x4{0, 0, 0, 0};
   }
   // positions spanned by this wave's valid rows (tile skipping / mask-free tiles)
   const int tk_lo = (rw * NB * 32) / G;
@@ -591,23 +589,51 @@ rpa_prefill_kernel(KernelArgs args) {
     __syncthreads();
   }
 
-  // ---- epilogue: O / l -> bf16; lane holds d = 32*db + 8*b + 4*lq2 + t of row n32 ----
+  // ---- epilogue: O / l -> bf16, staged through LDS ----
+  // A lane holds d = 32*db + 8*b + 4*lq2 + t of row n32, i.e. 8-byte pieces
+  // strewn over 32 rows; stored directly, every store instruction would touch
+  // 32 lines with 16 bytes each, and with all workgroups of a launch ending
+  // together those partial-line writes queue at the L2 for microseconds.  So
+  // each wave first writes its rows into its own LDS slice (the K/V buffers
+  // are free after the loop's last barrier), then stores 16 contiguous bytes
+  // per lane with consecutive lanes along a row: whole rows per instruction.
+  // The row pitch OP (8 bytes of pad) keeps the 8-byte LDS writes of 32 rows
+  // on distinct banks.
+  constexpr int OP = DH * 2 + 8;
+  constexpr int OROWS = NB * 32;
+  constexpr int CPR = DH * 2 / 16;   // 16-byte chunks per row slice
+  constexpr int RPS = 64 / CPR;      // rows per store instruction
+  static_assert(NW * OROWS * OP <= C::LDS_BYTES, "output staging must fit the tile buffers");
+  static_assert(64 % CPR == 0 && OROWS % RPS == 0, "whole rows per store");
+  char* ost = lds + wave * OROWS * OP;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float l = l_run[nb] + __shfl_xor(l_run[nb], 32);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (row_ok[nb]) {
-      uint16_t* dst = args.out + row_off[nb] + dh * DH + lq2 * 4;
+    char* srow = ost + (nb * 32 + n32) * OP + lq2 * 8;
 #pragma unroll
-      for (int db = 0; db < DH / 32; ++db) {
+    for (int db = 0; db < DH / 32; ++db) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const float* v = reinterpret_cast<const float*>(&o[db][nb]) + 4 * b;
-          *reinterpret_cast<u32x2*>(dst + db * 32 + b * 8) =
-              u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
-        }
+      for (int b = 0; b < 4; ++b) {
+        const float* v = reinterpret_cast<const float*>(&o[db][nb]) + 4 * b;
+        *reinterpret_cast<u32x2*>(srow + (db * 32 + b * 8) * 2) =
+            u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
       }
     }
+  }
+  __syncthreads();
+  const int cr = lane / CPR;
+  const int cc = lane - cr * CPR;
+#pragma unroll
+  for (int i = 0; i < OROWS / RPS; ++i) {
+    const int lr = i * RPS + cr;          // nb * 32 + n of the wave's rows
+    const int r = rw * NB * 32 + lr;      // row of the workgroup's tile
+    const int tk = r / G;
+    const int hh = r - tk * G;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ost + lr * OP + cc * 16);
+    if (tk < it.q_count)
+      *reinterpret_cast<u32x4*>(args.out + (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D +
+                                dh * DH + cc * 8) = v;
   }
 }
 
