@@ -132,10 +132,11 @@ enum {
   RPA_OPT_KERNEL_TIMING = 6,     /* n > 0: time up to n launches per kernel kind
                                     (see rpa_kernel_times); 0 = off (default),
                                     n <= 65536                                  */
-  RPA_OPT_XCD_GROUPS = 7,        /* prefill launch order: neighbouring tiles go to
-                                    the same one of X chiplets (workgroup b runs
-                                    on chiplet b mod X; MI355X has 8); 0 or 1 =
-                                    plain longest-first order (default), <= 64  */
+  RPA_OPT_XCD_GROUPS = 7,        /* prefill launch order: runs of 4 neighbouring
+                                    tiles go to the same one of X chiplets
+                                    (workgroup b runs on chiplet b mod X; MI355X
+                                    has 8, the default); 0 or 1 = plain
+                                    longest-first order; <= 64                  */
   RPA_OPT_FUSED_MERGE = 8        /* 1 (default): the decode split that finishes
                                     last merges its group's partials; 0: a
                                     separate merge kernel does (same result)    */

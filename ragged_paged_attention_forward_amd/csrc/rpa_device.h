@@ -336,6 +336,20 @@ rpa_prefill_kernel(KernelArgs args) {
   const int kv_end = it.kv_end;
   const int tile0 = (kv_begin / BN) * BN;  // tiles are aligned to BN keys
   const int n_tiles = (kv_end - tile0 + BN - 1) / BN;
+  // Tile order: step t takes tile (t + rot) mod n_tiles of the range, with rot
+  // chosen so that its global index (key / BN) is congruent to t modulo
+  // n_tiles.  The online softmax is indifferent to the order of the tiles,
+  // and neighbouring query tiles of a sliding window (same n_tiles, ranges
+  // shifted by a few tiles) then read the same K/V tile at the same step: the
+  // workgroups that one chiplet runs side by side fetch each tile from HBM
+  // once and share it through their L2, instead of each streaming the window
+  // in its own phase.  Full-causal ranges start at key 0 and keep their order.
+  const int rot = n_tiles > 0 ? (n_tiles - (tile0 / BN) % n_tiles) % n_tiles : 0;
+  auto key_of = [&](int t) {
+    int u = t + rot;
+    u -= u >= n_tiles ? n_tiles : 0;
+    return tile0 + u * BN;
+  };
   const int window = args.window;
   const float sl2 = args.scale_log2;
 
@@ -354,12 +368,23 @@ rpa_prefill_kernel(KernelArgs args) {
     sgk[i] = (p ^ xor_k(sr)) * 16;
     sgv[i] = (p ^ xor_v(sr)) * 16;
   }
-  int st_pidx = tile0 / page_size;
-  int st_slot = tile0 - st_pidx * page_size;
-  // page of the next tile to stage, looked up one stage ahead (scalar load)
-  int64_t st_page = (UNI && n_tiles > 0) ? uniform_load(pt_row, st_pidx) : 0;
+  // Page and slot of the next tile to stage, advanced tile by tile (a tile
+  // never crosses a page here) and reset when the order wraps to the start of
+  // the range; the page id is looked up one stage ahead (scalar load).
+  int st_u = rot;
+  int st_pidx = 0, st_slot = 0, wrap_pidx = 0, wrap_slot = 0;
+  int64_t st_page = 0;
+  if constexpr (UNI) {
+    wrap_pidx = tile0 / page_size;
+    wrap_slot = tile0 - wrap_pidx * page_size;
+    const int kr = tile0 + rot * BN;
+    st_pidx = kr / page_size;
+    st_slot = kr - st_pidx * page_size;
+    if (n_tiles > 0) st_page = uniform_load(pt_row, st_pidx);
+  }
 
-  auto stage = [&](int k0, int buf) {
+  auto stage = [&](int ts, int buf) {
+    const int k0 = key_of(ts);
     char* kdst = lds + buf * C::STAGE_B + wave * C::LOADS * C::BLK_K;
     char* vdst = lds + buf * C::STAGE_B + C::TILE_K + wave * C::LOADS * C::BLK_V;
     const int hi = k0 + BN < kv_end ? k0 + BN : kv_end;
@@ -374,7 +399,12 @@ rpa_prefill_kernel(KernelArgs args) {
         st_slot = 0;
         ++st_pidx;
       }
-      if (k0 + BN < kv_end) st_page = uniform_load(pt_row, st_pidx);
+      if (++st_u == n_tiles) {
+        st_u = 0;
+        st_pidx = wrap_pidx;
+        st_slot = wrap_slot;
+      }
+      if (ts + 1 < n_tiles) st_page = uniform_load(pt_row, st_pidx);
       const uint32_t nbytes = static_cast<uint32_t>((hi - k0 - 1) * row_bytes + D * 2);
       const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + base_off, nbytes);
       const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + base_off, nbytes);
@@ -443,9 +473,8 @@ rpa_prefill_kernel(KernelArgs args) {
     sched_reads_ahead<KREADS, KPF, 1, NB>();
   };
 
-  // ---- mask + online softmax + O^T += V^T P^T for the tile at ks (keys k0..) ----
-  auto softmax_pv = [&](f32x16 (&sc)[BN / 32][NB], const char* ks, int k0) __attribute__((always_inline)) {
-    // ---- mask + online softmax (fp32, base 2) ----
+  // ---- mask + online softmax of the tile at keys k0.. -> bf16 probabilities pf ----
+  auto softmax = [&](f32x16 (&sc)[BN / 32][NB], int k0, u32x4 (&pf)[BN / 16][NB]) __attribute__((always_inline)) {
     // Scores stay raw; scale*log2(e) is folded into one FMA per element.
     // The running maximum m_run is only raised when a row's new maximum
     // exceeds it by more than 8 (in log2 units), so O is rescaled rarely;
@@ -453,16 +482,9 @@ rpa_prefill_kernel(KernelArgs args) {
     // reference maximum enters both O and l.
     const bool full = (k0 >= kv_begin) && (k0 + BN <= kv_end) && (k0 + BN - 1 <= wpos_lo) &&
                       (window <= 0 || k0 > wpos_hi - window);
-    u32x4 pf[BN / 16][NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float mx = kNegInf;
-      if (full) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][nb][j]);
-      } else {
+      if (!full) {
         // key - lo for element j of block kb is rel + kb*32 + 8*(j/4) + (j%4)
         const int rel = k0 + 4 * lq2 - vis_lo[nb];
 #pragma unroll
@@ -471,12 +493,20 @@ rpa_prefill_kernel(KernelArgs args) {
           for (int j = 0; j < 16; ++j) {
             const uint32_t d = static_cast<uint32_t>(rel + kb * 32 + 8 * (j >> 2) + (j & 3));
             if (d > static_cast<uint32_t>(vis_span[nb])) sc[kb][nb][j] = kNegInf;
-            mx = fmaxf(mx, sc[kb][nb][j]);
           }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mx2 = mx * sl2;   // tile maximum in log2 units (scale > 0)
-      if (__any(mx2 > m_run[nb] + 8.f)) {
+      // Maximum over this lane's keys; a row's keys are split over lanes n and
+      // n + 32.  A row's maximum exceeds m_run + 8 iff one of its halves does,
+      // so the exchange of the halves' maxima is only needed on the (rare)
+      // path that raises m_run.
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][nb][j]);
+      if (__any(mx * sl2 > m_run[nb] + 8.f)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mx2 = mx * sl2;   // the row's tile maximum in log2 units (scale > 0)
         const float m_new = fmaxf(m_run[nb], mx2);
         // 0 when the row had no visible key yet; 1 for a row that still has none
         const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[nb] - m_new);
@@ -503,7 +533,10 @@ rpa_prefill_kernel(KernelArgs args) {
       }
       l_run[nb] += lsum;
     }
-    // ---- O^T += V^T P^T: V^T operands by two transposing reads each ----
+  };
+
+  // ---- O^T += V^T P^T for the V tile at ks: V^T operands by two transposing reads each ----
+  auto pv = [&](const u32x4 (&pf)[BN / 16][NB], const char* ks) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks16 = 0; ks16 < BN / 16; ++ks16) {
       const char* vrow = ks + ks16 * (16 / C::RPI) * C::BLK_V;
@@ -521,38 +554,29 @@ rpa_prefill_kernel(KernelArgs args) {
     sched_reads_ahead<VOPS, VPF, 2, NB>();
   };
 
-  // NS-stage pipeline, TPB tiles per step: while the TPB tiles of a step are
-  // used, the loads of the next NS - TPB tiles are in flight.  One barrier per
-  // step guards the reuse of the buffers (two tiles per step halve the
-  // barriers, waits and page lookups per tile when four stages fit).
-  constexpr int TPB = (DS == 1 && NS >= 4) ? 2 : 1;
-  static_assert(NS > TPB, "a step's loads need buffers of their own");
+  // NS-stage pipeline: while tile t is used, the loads of tiles t+1 ..
+  // t+NS-1 are in flight; one barrier per tile guards the reuse of a buffer.
+  // (Measured: two tiles per barrier step, or running half of the waves one
+  // phase behind the other half, are both slower on this kernel.)
 #pragma unroll
-  for (int t = 0; t < NS - TPB; ++t)
-    if (t < n_tiles) stage(tile0 + t * BN, t);
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < n_tiles) stage(t, t);
   if constexpr (UNI) {
     // Q and the first tiles: every load of the prologue is complete before the loop
     wait_vmem();
   } else {
-    // the first step's tiles must have landed
-    const int later = (n_tiles < NS - TPB ? n_tiles : NS - TPB) - TPB;
-    wait_tile_loads<C::LPT, NS - 2 * TPB>(later < 0 ? 0 : later);
+    // the first tile must have landed
+    const int later = (n_tiles < NS - 1 ? n_tiles : NS - 1) - 1;
+    wait_tile_loads<C::LPT, NS - 2>(later < 0 ? 0 : later);
   }
   __syncthreads();
 
-  for (int step0 = 0; step0 < n_tiles; step0 += TPB) {
-#pragma unroll
-  for (int s = 0; s < TPB; ++s) {
-    const int ts = step0 + NS - TPB + s;   // into the buffer of tile step0 - TPB + s
-    if (ts < n_tiles) stage(tile0 + ts * BN, ts % NS);
-  }
-#pragma unroll
-  for (int s = 0; s < TPB; ++s) {
-    const int tile = step0 + s;
-    const int k0 = tile0 + tile * BN;
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int ts = tile + NS - 1;   // into the buffer of tile - 1, released by the last barrier
+    if (ts < n_tiles) stage(ts, ts % NS);
+    const int k0 = key_of(tile);
     const int cur = tile % NS;
-    // (the last step may hold one tile fewer than TPB)
-    const bool skip = (TPB > 1 && tile >= n_tiles) || tile_skipped(k0);
+    const bool skip = tile_skipped(k0);
     const char* ks = lds + cur * C::STAGE_B;
     f32x16 sc[BN / 32][NB];
     if (!skip) scores(ks, sc);
@@ -578,13 +602,16 @@ rpa_prefill_kernel(KernelArgs args) {
         }
       }
     }
-    if (!skip) softmax_pv(sc, ks, k0);
-  }
-    // the next step's tiles must have landed; later ones may still be in flight
+    if (!skip) {
+      u32x4 pf[BN / 16][NB];
+      softmax(sc, k0, pf);
+      pv(pf, ks);
+    }
+    // the next tile must have landed; later ones may still be in flight
     {
-      const int staged_last = (step0 + NS - 1 < n_tiles ? step0 + NS - 1 : n_tiles - 1);
-      const int later = staged_last - (step0 + 2 * TPB - 1);
-      wait_tile_loads<C::LPT, NS - 2 * TPB>(later < 0 ? 0 : later);
+      const int staged_last = (tile + NS - 1 < n_tiles ? tile + NS - 1 : n_tiles - 1);
+      const int later = staged_last - (tile + 1);
+      wait_tile_loads<C::LPT, NS - 2>(later < 0 ? 0 : later);
     }
     __syncthreads();
   }

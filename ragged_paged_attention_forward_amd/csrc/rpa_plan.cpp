@@ -37,20 +37,34 @@ int32_t range_begin(int64_t pos0, int32_t window) {
 
 // Workgroup b of a launch runs on chiplet (XCD) b mod X, and each chiplet has
 // its own L2.  Neighbouring items of the sorted list (consecutive query tiles
-// of one sequence and KV head) read mostly the same keys, so each round of
-// `round` items is cut into X contiguous chunks and chunk x is placed on the
-// launch positions of chiplet x: the tiles a chiplet runs side by side then
-// share their K/V through its L2 instead of each fetching them again.
-void interleave_for_chiplets(std::vector<rpa_work_item>* items, int round, int X) {
+// of one sequence and KV head) read mostly the same keys.  So within each
+// round of `round` launch positions (one workgroup per compute unit), the
+// longest-first list is dealt to the chiplets in runs of `run` consecutive
+// items: the tiles of a run execute side by side on one chiplet and share
+// their K/V through its L2.  The runs go to chiplets 0, 1, .., X-1, then
+// X-1, .., 0, and so on, so that every chiplet gets long and short items
+// alike and the chiplets' total work stays even; a chiplet whose positions
+// are used up passes the run on to the next one.
+void interleave_for_chiplets(std::vector<rpa_work_item>* items, int round, int X, int run) {
   const int64_t n = static_cast<int64_t>(items->size());
-  if (X <= 1 || round < X || n <= X) return;
+  if (X <= 1 || round < X || n <= X || run < 1) return;
   std::vector<rpa_work_item> out(items->size());
+  std::vector<int64_t> next(X);
   for (int64_t r0 = 0; r0 < n; r0 += round) {
     const int64_t m = std::min<int64_t>(round, n - r0);
-    int64_t src = r0;
-    for (int x = 0; x < X; ++x) {
-      // launch positions r0 + x, r0 + x + X, ... below r0 + m belong to chiplet x
-      for (int64_t pos = x; pos < m; pos += X) out[r0 + pos] = (*items)[src++];
+    for (int x = 0; x < X; ++x) next[x] = x;   // next free position of chiplet x
+    int64_t c = 0;                             // run counter
+    int in_run = 0;
+    for (int64_t k = 0; k < m; ++k) {
+      const int64_t lap = c / X;
+      int x = static_cast<int>(lap % 2 == 0 ? c % X : X - 1 - c % X);
+      while (next[x] >= m) x = (x + 1) % X;    // free positions remain: m - k > 0
+      out[r0 + next[x]] = (*items)[r0 + k];
+      next[x] += X;
+      if (++in_run == run) {
+        in_run = 0;
+        ++c;
+      }
     }
   }
   items->swap(out);
@@ -163,7 +177,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
                      const int64_t cb = int64_t(b.kv_end - b.kv_begin) * b.q_count;
                      return ca > cb;
                    });
-  interleave_for_chiplets(&out->prefill, p.num_cus, p.xcd_groups);
+  interleave_for_chiplets(&out->prefill, p.num_cus, p.xcd_groups, p.xcd_run);
 
   // Decode split size: enough splits to give every compute unit a few
   // workgroups, in whole multiples of what one workgroup takes per step.

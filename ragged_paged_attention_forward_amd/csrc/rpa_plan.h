@@ -26,8 +26,9 @@ struct PlanParams {
   int64_t decode_split_keys = 0;  // 0: automatic
   int path_mode = 0;           // 0 auto, 1 all prefill kernel, 2 decode where it fits
   int num_cus = 256;           // compute units to fill
-  int xcd_groups = 1;          // prefill order: workgroups b, b+X, b+2X, ... share a
+  int xcd_groups = 8;          // prefill order: workgroups b, b+X, b+2X, ... share a
                                // chiplet (and its L2); <= 1 keeps the plain order
+  int xcd_run = 4;             // consecutive items dealt to one chiplet at a time
 };
 
 struct Plan {

@@ -132,26 +132,46 @@ def test_prefill_tile_rows_and_longest_first():
 @pytest.mark.parametrize("w", [wl.swa_prefill(), wl.global_prefill(tokens=3000), wl.mixed(window=0)],
                          ids=["swa", "global3000", "mixed"])
 @pytest.mark.parametrize("groups", [8, 3])
-def test_chiplet_order_is_a_chunked_permutation(w, groups):
-    """Launch position b runs on chiplet b mod X: each chiplet's positions in a
-    round of 256 (one workgroup per compute unit) hold one contiguous run of the
-    longest-first list, chiplet 0 first."""
-    plain = [it for it in plan_for(w, [(RPA_OPT_XCD_GROUPS, 0)])[3] if it["kind"] == 0]
+def test_chiplet_order_deals_short_runs(w, groups):
+    """Launch position b runs on chiplet b mod X.  Each round of 256 positions
+    (one workgroup per compute unit) holds the same items as that round of the
+    longest-first list; every chiplet takes them in list order, in runs of 4
+    consecutive items dealt to the chiplets 0..X-1, then X-1..0, and so on
+    (exactly so when a round splits evenly), which keeps the chiplets' work
+    within a few percent of each other."""
+    key = lambda it: (it["seq"], it["kv_head"], it["q_start"])
+    plain = [key(it) for it in plan_for(w, [(RPA_OPT_XCD_GROUPS, 0)])[3] if it["kind"] == 0]
     cu, kv, info, items = plan_for(w, [(RPA_OPT_XCD_GROUPS, groups)])
     check_plan(w, cu, kv, info, items)
-    got = [it for it in items if it["kind"] == 0]
-    assert len(got) == len(plain)
-    rnd = 256
+    pre = [it for it in items if it["kind"] == 0]
+    got = [key(it) for it in pre]
+    rank = {k: i for i, k in enumerate(plain)}
+    assert len(got) == len(plain) and len(rank) == len(plain)
+    rnd, run = 256, 4
     for r0 in range(0, len(plain), rnd):
         m = min(rnd, len(plain) - r0)
-        src = r0
+        assert sorted(got[r0:r0 + m]) == sorted(plain[r0:r0 + m])
         for x in range(groups):
-            for pos in range(x, m, groups):
-                assert got[r0 + pos] == plain[src]
-                src += 1
-        assert src == r0 + m
+            ranks = [rank[got[r0 + pos]] for pos in range(x, m, groups)]
+            assert ranks == sorted(ranks)
+            if m % (2 * groups * run) == 0:
+                runs = [c for c in range(m // run) if (c % groups if (c // groups) % 2 == 0
+                                                       else groups - 1 - c % groups) == x]
+                assert ranks == [r0 + run * c + i for c in runs for i in range(run)]
     if len(plain) > groups:
         assert got != plain
+    if len(plain) >= rnd and groups == 8:
+        cost = [0] * groups
+        for b, it in enumerate(pre):
+            cost[b % groups] += (it["kv_end"] - it["kv_begin"]) * it["q_count"]
+        assert max(cost) <= 1.03 * min(cost)
+
+
+def test_chiplet_order_is_the_default():
+    w = wl.swa_prefill()
+    default = plan_for(w)[3]
+    assert default == plan_for(w, [(RPA_OPT_XCD_GROUPS, 8)])[3]
+    assert default != plan_for(w, [(RPA_OPT_XCD_GROUPS, 0)])[3]
 
 
 def test_auto_split_fills_the_chip():
