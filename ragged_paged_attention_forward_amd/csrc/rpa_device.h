@@ -295,6 +295,20 @@ rpa_prefill_kernel(KernelArgs args) {
   const int page_size = args.page_size;
   const int row_bytes = hkv * D * 2;   // bytes between consecutive key rows of a page
 
+  // Page ids of the key range, one per lane, 64 at a time (pw_ids holds pages
+  // pw_base ..), loaded ahead of Q so that the first tile's staging does not
+  // wait behind the Q loads.
+  const int tile0 = (it.kv_begin / BN) * BN;  // tiles are aligned to BN keys
+  const int wrap_pidx = tile0 / args.page_size;
+  const int p_last = it.kv_end > tile0 ? (it.kv_end - 1) / args.page_size : -1;
+  int pw_base = 0, pw_ids = 0;
+  auto load_window = [&](int base) {
+    pw_base = base;
+    const int pi = base + lane;
+    pw_ids = pi <= p_last ? pt_row[pi] : 0;
+  };
+  if (UNI) load_window(wrap_pidx);
+
   // ---- rows of this lane, Q fragments (B operand of S^T = K Q^T) ----
   int row_pos[NB];
   int vis_lo[NB], vis_span[NB];   // visible keys of the lane's rows (visible_range)
@@ -334,7 +348,6 @@ rpa_prefill_kernel(KernelArgs args) {
 
   const int kv_begin = it.kv_begin;
   const int kv_end = it.kv_end;
-  const int tile0 = (kv_begin / BN) * BN;  // tiles are aligned to BN keys
   const int n_tiles = (kv_end - tile0 + BN - 1) / BN;
   // Tile order: step t takes tile (t + rot) mod n_tiles of the range, with rot
   // chosen so that its global index (key / BN) is congruent to t modulo
@@ -370,17 +383,17 @@ rpa_prefill_kernel(KernelArgs args) {
   }
   // Page and slot of the next tile to stage, advanced tile by tile (a tile
   // never crosses a page here) and reset when the order wraps to the start of
-  // the range; the page id is looked up one stage ahead (scalar load).
+  // the range.  The range's page ids sit in a register, one per lane, 64 at a
+  // time (pw_ids holds pages pw_base ..), so a stage reads its page id with
+  // v_readlane instead of waiting on a load in the loop; a range of more than
+  // 64 pages reloads the window, and waits for it, when the order leaves it.
   int st_u = rot;
-  int st_pidx = 0, st_slot = 0, wrap_pidx = 0, wrap_slot = 0;
-  int64_t st_page = 0;
+  int st_pidx = 0, st_slot = 0, wrap_slot = 0;
   if constexpr (UNI) {
-    wrap_pidx = tile0 / page_size;
     wrap_slot = tile0 - wrap_pidx * page_size;
     const int kr = tile0 + rot * BN;
     st_pidx = kr / page_size;
     st_slot = kr - st_pidx * page_size;
-    if (n_tiles > 0) st_page = uniform_load(pt_row, st_pidx);
   }
 
   auto stage = [&](int ts, int buf) {
@@ -392,7 +405,11 @@ rpa_prefill_kernel(KernelArgs args) {
       // The tile lies in one page.  Rows [k0, hi) are real keys of the
       // sequence (rows below kv_begin are masked later); rows past hi read as
       // zero through the buffer's record count.
-      const int64_t page = st_page;
+      if (static_cast<unsigned>(st_pidx - pw_base) >= 64u) {   // left the window (ranges of more than 64 pages)
+        load_window(st_pidx);
+        wait_vmem();
+      }
+      const int64_t page = __builtin_amdgcn_readlane(pw_ids, st_pidx - pw_base);
       const int64_t base_off = ((page * page_size + st_slot) * hkv + g) * D;
       st_slot += BN;
       if (st_slot == page_size) {
@@ -404,7 +421,6 @@ rpa_prefill_kernel(KernelArgs args) {
         st_pidx = wrap_pidx;
         st_slot = wrap_slot;
       }
-      if (ts + 1 < n_tiles) st_page = uniform_load(pt_row, st_pidx);
       const uint32_t nbytes = static_cast<uint32_t>((hi - k0 - 1) * row_bytes + D * 2);
       const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + base_off, nbytes);
       const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + base_off, nbytes);
