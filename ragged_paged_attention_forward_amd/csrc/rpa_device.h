@@ -6,26 +6,29 @@
 // Two kernels consume the host-built work list:
 //
 //  * rpa_prefill_kernel -- one workgroup per (sequence, KV head, query tile)
-//    item.  The tile packs NW*NB*16 rows of (token, query head of the KV
-//    group) so every streamed key serves all grouped heads (the pages' kernel
-//    scales its query block with the head ratio: "Chasing speed of light on
-//    TPU v6e", footnote 6 of section Attention).  K/V pages are gathered by
-//    coalesced 16-byte loads into LDS (V transposed on the way), the next tile
-//    is fetched into registers while the current one is multiplied, and the
-//    scores never leave the chip (footnote 5 of the same section).
+//    item.  The tile packs (NW/DS)*NB*32 rows of (token, query head of the KV
+//    group), so every streamed key serves all grouped heads (the pages'
+//    kernel scales its query block with the head ratio: "Chasing speed of
+//    light on TPU v6e", footnote 6 of section Attention).  K/V tiles of BN
+//    keys go from HBM straight into NS LDS buffers (buffer loads with an LDS
+//    destination, XOR-swizzled rows), in a rotated order that lets
+//    neighbouring query tiles share them through the L2; S^T = K Q^T and
+//    O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with V^T read by
+//    transposing LDS reads, and the scores never leave the chip (footnote 5
+//    of the same section).
 //
 //  * rpa_decode_kernel -- one workgroup per (sequence, KV head, key split) of
 //    a sequence with few query rows (decode).  Decode is memory-bound at every
 //    batch size ("TPU Deep Dive", chapter 4 and 7), so the waves of a
 //    workgroup each stream a different 32-key chunk straight from HBM into
-//    MFMA operand registers, and splits of long sequences run in parallel and
-//    are merged by log-sum-exp in rpa_merge_kernel.
+//    v_mfma_f32_16x16x32_bf16 operand registers; the waves are combined
+//    through LDS, and the splits of a long sequence are merged by log-sum-exp
+//    by the split that finishes last (or by rpa_merge_kernel).
 //
-// Both compute S^T = K * Q^T and O^T = V^T * P^T with the bf16 MFMA
-// v_mfma_f32_16x16x32_bf16, so that a query row is always the MFMA column
-// index (lane % 16): row maxima, row sums and the O rescale stay within the
-// four lanes {n, n+16, n+32, n+48} of row n.  Softmax runs in fp32 in base 2
-// with log2(e) folded into the scale; the output is rounded to bf16 (RNE).
+// Both compute scores transposed (S^T = K Q^T), so a query row is an MFMA
+// column and the probabilities feed the P V product from the same lanes.
+// Softmax runs in fp32 in base 2 with log2(e) folded into the scale; the
+// output is rounded to bf16 (round to nearest even).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
