@@ -137,9 +137,16 @@ enum {
                                     (workgroup b runs on chiplet b mod X; MI355X
                                     has 8, the default); 0 or 1 = plain
                                     longest-first order; <= 64                  */
-  RPA_OPT_FUSED_MERGE = 8        /* 1 (default): the decode split that finishes
-                                    last merges its group's partials; 0: a
-                                    separate merge kernel does (same result)    */
+  RPA_OPT_FUSED_MERGE = 8,       /* 1 (default): the split (decode or prefill)
+                                    that finishes last merges its group's
+                                    partials; 0: a separate merge kernel does
+                                    (same result)                               */
+  RPA_OPT_PREFILL_SPLIT_KEYS = 9  /* keys per split of a long prefill item: 0 =
+                                    automatic (split only when the longest item
+                                    exceeds the average work of a compute unit
+                                    by half), -1 = never split, > 0 = split every
+                                    item longer than 1.5x this many keys (rounded
+                                    up to 256); <= 2^30                         */
 };
 /* Returns RPA_OK or RPA_ERR_INVALID_ARG (unknown option or bad value). */
 int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);
@@ -179,17 +186,21 @@ typedef struct rpa_work_item {
   int32_t split_index;  /* 0 .. num_splits-1 within the group                      */
   int32_t num_splits;   /* splits in the group (1 when split_group == -1)          */
   int32_t partial_base; /* first partial-result slot of the group                  */
-  int32_t kind;         /* 0: prefill kernel item, 1: decode kernel item           */
+  int32_t kind;         /* 0: prefill kernel item, 1: decode kernel item; a split
+                           group has the kind of its splits                       */
 } rpa_work_item;
 
 typedef struct rpa_plan_info {
   int32_t num_prefill_items;
   int32_t num_decode_items;
   int32_t num_split_groups;
-  int32_t num_partials;     /* partial-result slots used                            */
+  int32_t num_partials;     /* partial-result slots used (16 rows of d floats each;
+                               a prefill split takes prefill_rows / 16 of them)    */
   int32_t prefill_rows;     /* query rows (tokens x grouped heads) per prefill tile */
   int32_t decode_split_keys;/* keys per decode split chosen                         */
   int64_t visible_pairs;    /* visible (query, key) pairs per query head            */
+  int32_t prefill_split_keys;/* keys per prefill split chosen, 0 when none split    */
+  int32_t reserved;
 } rpa_plan_info;
 
 /*

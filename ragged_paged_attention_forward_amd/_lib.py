@@ -20,6 +20,7 @@ RPA_OPT_DECODE_WAVES = 5
 RPA_OPT_KERNEL_TIMING = 6
 RPA_OPT_XCD_GROUPS = 7
 RPA_OPT_FUSED_MERGE = 8
+RPA_OPT_PREFILL_SPLIT_KEYS = 9
 
 RPA_KERNEL_PREFILL = 0
 RPA_KERNEL_DECODE = 1
@@ -49,7 +50,8 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("num_prefill_items", ctypes.c_int32), ("num_decode_items", ctypes.c_int32),
                 ("num_split_groups", ctypes.c_int32), ("num_partials", ctypes.c_int32),
                 ("prefill_rows", ctypes.c_int32), ("decode_split_keys", ctypes.c_int32),
-                ("visible_pairs", ctypes.c_int64)]
+                ("visible_pairs", ctypes.c_int64), ("prefill_split_keys", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

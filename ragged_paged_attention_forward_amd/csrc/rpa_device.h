@@ -635,6 +635,96 @@ rpa_prefill_kernel(KernelArgs args) {
     __syncthreads();
   }
 
+  constexpr int OROWS = NB * 32;   // rows per wave
+  if (it.split_group >= 0) {
+    // ---- a split of a long item: normalised fp32 O and base-2 LSE per row ----
+    // Row r of split i sits at row i * ROWS of the group's partial block; the
+    // split that draws the group's last ticket merges the block (the same
+    // arithmetic and the same uncached workspace as the decode splits).
+    const int64_t prow = static_cast<int64_t>(it.partial_base) * 16 + static_cast<int64_t>(it.split_index) * C::ROWS;
+    float inv[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float l = l_run[nb] + __shfl_xor(l_run[nb], 32);
+      inv[nb] = l > 0.f ? 1.f / l : 0.f;
+      const float base = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
+      const int r = (rw * NB + nb) * 32 + n32;
+      if (lq2 == 0 && dh == 0 && r / G < it.q_count)
+        args.partial_lse[prow + r] = l > 0.f ? base + __builtin_log2f(l) : kNegInf;
+    }
+    // The fp32 rows go through LDS, in SP passes of CW columns, so that the
+    // stores write whole rows (16 contiguous bytes per lane, lanes along a
+    // row), as the bf16 epilogue does; the 16-byte row pad keeps the 16-byte
+    // LDS writes of 16 rows on distinct banks.  Tiles whose LDS cannot hold a
+    // 32-column pass store from registers instead.
+    constexpr int SP = (DH % 32 == 0 && NW * OROWS * (DH * 4 + 16) <= C::LDS_BYTES) ? 1
+                     : (DH % 64 == 0 && NW * OROWS * (DH * 2 + 16) <= C::LDS_BYTES) ? 2
+                     : (DH % 128 == 0 && NW * OROWS * (DH + 16) <= C::LDS_BYTES) ? 4 : 0;
+    if constexpr (SP > 0) {
+      constexpr int CW = DH / SP;          // columns per pass
+      constexpr int RP = CW * 4 + 16;      // LDS bytes per staged row
+      constexpr int CPF = CW * 4 / 16;     // 16-byte chunks per row per pass
+      constexpr int RPF = 64 / CPF;        // rows per store instruction
+      static_assert(CPF <= 64 && 64 % CPF == 0 && OROWS % RPF == 0, "whole rows per store");
+      char* fst = lds + wave * OROWS * RP;
+      const int fr = lane / CPF;
+      const int fc = lane - fr * CPF;
+#pragma unroll
+      for (int ps = 0; ps < SP; ++ps) {
+        if (ps > 0) __syncthreads();   // the previous pass's reads are done
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int db = ps * (CW / 32); db < (ps + 1) * (CW / 32); ++db)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const float* v = reinterpret_cast<const float*>(&o[db][nb]) + 4 * b;
+              *reinterpret_cast<f32x4*>(fst + (nb * 32 + n32) * RP + ((db - ps * (CW / 32)) * 32 + 8 * b + 4 * lq2) * 4) =
+                  f32x4{v[0] * inv[nb], v[1] * inv[nb], v[2] * inv[nb], v[3] * inv[nb]};
+            }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < OROWS / RPF; ++i) {
+          const int lr = i * RPF + fr;
+          const int r = rw * NB * 32 + lr;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(fst + lr * RP + fc * 16);
+          if (r / G < it.q_count)
+            *reinterpret_cast<f32x4*>(args.partial_o + (prow + r) * D + dh * DH + ps * CW + fc * 4) = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int r = (rw * NB + nb) * 32 + n32;
+        if (r / G < it.q_count) {
+          float* dst = args.partial_o + (prow + r) * D + dh * DH + lq2 * 4;
+#pragma unroll
+          for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const float* v = reinterpret_cast<const float*>(&o[db][nb]) + 4 * b;
+              *reinterpret_cast<f32x4*>(dst + db * 32 + b * 8) =
+                  f32x4{v[0] * inv[nb], v[1] * inv[nb], v[2] * inv[nb], v[3] * inv[nb]};
+            }
+        }
+      }
+    }
+    if (!args.fused_merge) return;   // the merge kernel follows
+    // every wave's stores are complete in memory before the group's ticket is drawn
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    int* flag = reinterpret_cast<int*>(lds);   // the tile buffers are free after the loop
+    if (tid == 0)
+      *flag = __hip_atomic_fetch_add(args.merge_tickets + it.split_group, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == it.num_splits - 1;
+    __syncthreads();
+    if (*flag == 0) return;
+    asm volatile("" ::: "memory");
+    merge_group<D>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, C::ROWS, tid, C::NT);
+    if (tid == 0) __hip_atomic_store(args.merge_tickets + it.split_group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+
   // ---- epilogue: O / l -> bf16, staged through LDS ----
   // A lane holds d = 32*db + 8*b + 4*lq2 + t of row n32, i.e. 8-byte pieces
   // strewn over 32 rows; stored directly, every store instruction would touch
@@ -646,7 +736,6 @@ rpa_prefill_kernel(KernelArgs args) {
   // The row pitch OP (8 bytes of pad) keeps the 8-byte LDS writes of 32 rows
   // on distinct banks.
   constexpr int OP = DH * 2 + 8;
-  constexpr int OROWS = NB * 32;
   constexpr int CPR = DH * 2 / 16;   // 16-byte chunks per row slice
   constexpr int RPS = 64 / CPR;      // rows per store instruction
   static_assert(NW * OROWS * OP <= C::LDS_BYTES, "output staging must fit the tile buffers");
@@ -695,9 +784,11 @@ struct MergeCfg {
 };
 // Merges the n partials of one split group (rows q_count * G of tokens from
 // q_start, KV head kv_head) into the bf16 output; threads tid of nthreads.
+// Split i's rows start at row i * rps of the group's block (rps = 16 for
+// decode splits, the tile's row count for prefill splits).
 template <int D>
 RPA_DEV void merge_group(const KernelArgs& args, int q_start, int q_count, int kv_head, int partial_base,
-                         int n, int tid, int nthreads) {
+                         int n, int rps, int tid, int nthreads) {
   constexpr int C4 = D / 4;
   constexpr int NB = 8;   // splits fetched per batch: every load of a batch is in flight at once
   const int rows = q_count * args.group;
@@ -714,8 +805,8 @@ RPA_DEV void merge_group(const KernelArgs& args, int q_start, int q_count, int k
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const bool ok = i0 + b < n;
-        l[b] = ok ? lse[(i0 + b) * 16 + r] : kNegInf;
-        v[b] = ok ? *reinterpret_cast<const f32x4*>(po + (static_cast<int64_t>(i0 + b) * 16 + r) * D + c * 4)
+        l[b] = ok ? lse[(i0 + b) * rps + r] : kNegInf;
+        v[b] = ok ? *reinterpret_cast<const f32x4*>(po + (static_cast<int64_t>(i0 + b) * rps + r) * D + c * 4)
                   : f32x4{0.f, 0.f, 0.f, 0.f};
       }
       float bm = mx;
@@ -746,7 +837,7 @@ template <int D>
 __global__ void __launch_bounds__(MergeCfg<D>::THREADS) rpa_merge_kernel(KernelArgs args) {
   const rpa_work_item grp = args.groups[blockIdx.x];
   merge_group<D>(args, grp.q_start, grp.q_count, grp.kv_head, grp.partial_base, grp.num_splits,
-                 threadIdx.x, blockDim.x);
+                 grp.kind == 0 ? args.prefill_rows : 16, threadIdx.x, blockDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1049,7 +1140,7 @@ rpa_decode_kernel(KernelArgs args) {
   __syncthreads();
   if (*lds_flag == 0) return;
   asm volatile("" ::: "memory");
-  merge_group<D>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, tid, C::NT);
+  merge_group<D>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, 16, tid, C::NT);
   if (tid == 0) __hip_atomic_store(args.merge_tickets + it.split_group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -58,6 +58,7 @@ static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
   a.max_pages = l.max_pages;
   a.window = l.window;
   a.scale_log2 = l.scale_log2;
+  a.prefill_rows = prefill_rows_for(l.head_dim);
   return a;
 }
 

@@ -15,7 +15,7 @@ struct KernelArgs {
   uint16_t* out;
   const rpa_work_item* items;
   const rpa_work_item* groups;
-  float* partial_o;      // [slot][16 rows][D]
+  float* partial_o;      // [slot][16 rows][D]; a prefill split uses prefill_rows / 16 slots
   float* partial_lse;    // [slot][16 rows], base-2 log-sum-exp
   int32_t* merge_tickets;  // [group] splits finished so far (0 between calls)
   int32_t fused_merge;   // 1: the last split of a group merges it (no merge kernel)
@@ -26,6 +26,7 @@ struct KernelArgs {
   int32_t max_pages;
   int32_t window;
   float scale_log2;      // scale * log2(e)
+  int32_t prefill_rows;  // rows of a prefill tile (rows of a prefill split's partial block)
 };
 
 }  // namespace rpa

@@ -118,6 +118,64 @@ int validate_metadata(const PlanParams& p, const int32_t* cu, const int32_t* kv,
   return RPA_OK;
 }
 
+// Long prefill items (the last query tiles of a long chunk) can outlast the
+// rest of the launch by far, with most compute units idle.  Such an item is
+// cut along its key range into splits that each write a partial result
+// (normalised O and log-sum-exp per row); the split that finishes last merges
+// them, as for decode.  Automatic mode splits only when the longest item
+// exceeds 1.5x the average work of a compute unit, into pieces of about that
+// average (smaller pieces measured slower: every split writes and re-reads
+// its rows' fp32 partials); boundaries sit on multiples of 64 keys so that no
+// key tile is shared by two splits.
+static void split_long_prefill_items(const PlanParams& p, Plan* out) {
+  out->prefill_split_keys = 0;
+  if (out->prefill.empty() || p.prefill_split_keys < 0) return;
+  int64_t total = 0, longest = 0;
+  for (const auto& it : out->prefill) {
+    const int64_t keys = it.kv_end - it.kv_begin;
+    total += keys;
+    longest = std::max(longest, keys);
+  }
+  int64_t piece = p.prefill_split_keys;
+  if (piece == 0) {
+    const int64_t avg = total / std::max(1, p.num_cus);
+    if (2 * longest <= 3 * avg) return;
+    piece = avg;
+  }
+  piece = std::max<int64_t>(512, (piece + 255) / 256 * 256);
+  if (2 * longest <= 3 * piece) return;
+  out->prefill_split_keys = static_cast<int>(piece);
+  const int slots = p.prefill_rows / 16;   // 16-row partial slots per split
+  std::vector<rpa_work_item> items;
+  items.reserve(out->prefill.size());
+  for (const auto& it : out->prefill) {
+    const int64_t keys = it.kv_end - it.kv_begin;
+    const int64_t n = (2 * keys <= 3 * piece) ? 1 : (keys + piece / 2) / piece;   // round(keys / piece)
+    if (n <= 1) {
+      items.push_back(it);
+      continue;
+    }
+    rpa_work_item base = it;
+    base.split_group = static_cast<int32_t>(out->groups.size());
+    base.num_splits = static_cast<int32_t>(n);
+    base.partial_base = out->num_partials;
+    out->num_partials += static_cast<int>(n) * slots;
+    out->groups.push_back(base);
+    int64_t lo = it.kv_begin;
+    for (int64_t i = 0; i < n; ++i) {
+      int64_t hi = it.kv_end;
+      if (i + 1 < n) hi = (it.kv_begin + (keys * (i + 1)) / n + 63) / 64 * 64;
+      rpa_work_item s = base;
+      s.split_index = static_cast<int32_t>(i);
+      s.kv_begin = static_cast<int32_t>(lo);
+      s.kv_end = static_cast<int32_t>(hi);
+      items.push_back(s);
+      lo = hi;
+    }
+  }
+  out->prefill.swap(items);
+}
+
 void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32_t num_seqs,
                 int32_t window, Plan* out) {
   out->prefill.clear();
@@ -169,6 +227,8 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
       }
     }
   }
+
+  split_long_prefill_items(p, out);
 
   // Longest first: the most expensive tiles start first so the tail is short.
   std::stable_sort(out->prefill.begin(), out->prefill.end(),

@@ -24,6 +24,7 @@ struct PlanParams {
   int decode_wave_keys = 32;   // keys one decode wave takes per step
   int decode_waves = 4;        // waves of one decode workgroup
   int64_t decode_split_keys = 0;  // 0: automatic
+  int64_t prefill_split_keys = 0; // 0: automatic, < 0: never, > 0: fixed
   int path_mode = 0;           // 0 auto, 1 all prefill kernel, 2 decode where it fits
   int num_cus = 256;           // compute units to fill
   int xcd_groups = 8;          // prefill order: workgroups b, b+X, b+2X, ... share a
@@ -35,7 +36,8 @@ struct Plan {
   std::vector<rpa_work_item> prefill;  // launch order
   std::vector<rpa_work_item> decode;   // launch order
   std::vector<rpa_work_item> groups;   // one entry per split group (its split 0)
-  int num_partials = 0;
+  int num_partials = 0;                // 16-row partial-result slots (a prefill split takes rows/16)
+  int prefill_split_keys = 0;          // keys per prefill split chosen (0: none split)
   int decode_split_keys = 0;
   int64_t visible_pairs = 0;
   int64_t total_q = 0;

@@ -257,6 +257,41 @@ def test_fused_merge_matches_merge_kernel_bitwise(window):
         compare(run_gpu(a, inp2), oracle_rows(inp2), label=f"fused d{d}")
 
 
+@pytest.mark.parametrize("hq,hkv,d,b,seqs,window", [
+    (8, 2, 128, 64, [(900, 2500), (5, 40), (1, 700), (300, 300)], 0),
+    (8, 1, 256, 128, [(600, 2000), (1, 500), (64, 64)], 0),
+    (8, 1, 256, 128, [(700, 2100)], 1400),
+    (16, 2, 512, 128, [(300, 1800), (2, 9)], 0),
+    (4, 1, 64, 16, [(500, 1500), (7, 7)], 0),
+])
+def test_prefill_splits(hq, hkv, d, b, seqs, window):
+    """Long prefill items cut along their key range: the partial results merged
+    by the last split (fused) match the oracle, give the same bits as the
+    separate merge kernel and as a repeated call (the tickets return to zero),
+    and agree with the unsplit kernel."""
+    w = wl.custom(seqs, hq, hkv, d, b, window, seed=d + window)
+    inp = wl.make_inputs(w, poison=True)
+    ref = oracle_rows(inp)
+    fused = make_attn(w)
+    fused.set_option(R.RPA_OPT_PREFILL_SPLIT_KEYS, 512)
+    info, items = fused.plan(inp.cu_q_lens, inp.kv_lens, window)
+    assert info["prefill_split_keys"] == 512
+    assert sum(1 for it in items if it["kind"] == 0 and it["split_group"] >= 0) >= 4
+    got = run_gpu(fused, inp).clone()
+    compare(got, ref, label="prefill splits, fused merge")
+    for _ in range(2):
+        assert torch.equal(run_gpu(fused, inp), got)
+    sep = make_attn(w)
+    sep.set_option(R.RPA_OPT_PREFILL_SPLIT_KEYS, 512)
+    sep.set_option(R.RPA_OPT_FUSED_MERGE, 0)
+    assert torch.equal(run_gpu(sep, inp), got)
+    whole = make_attn(w)
+    whole.set_option(R.RPA_OPT_PREFILL_SPLIT_KEYS, -1)
+    base = run_gpu(whole, inp)
+    compare(base, ref, label="unsplit")
+    assert (base.float() - got.float()).abs().max().item() <= 2e-2
+
+
 def test_long_contexts_sampled():
     """Decodes over 40K-key contexts (many splits per group) and a 2048-token
     chunk on a 30K prefix, with and without a window; sampled rows."""

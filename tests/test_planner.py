@@ -11,8 +11,8 @@ import pytest
 import oracle.rpa_oracle as ora
 import rpa_workloads as wl
 from ragged_paged_attention_forward_amd import (RPA_OPT_DECODE_MAX_ROWS, RPA_OPT_DECODE_SPLIT_KEYS,
-                                                RPA_OPT_PATH, RPA_OPT_XCD_GROUPS, RaggedPagedAttention,
-                                                metrics)
+                                                RPA_OPT_PATH, RPA_OPT_PREFILL_SPLIT_KEYS, RPA_OPT_XCD_GROUPS,
+                                                RaggedPagedAttention, metrics)
 
 
 def plan_for(w, options=()):
@@ -42,7 +42,7 @@ def check_plan(w, cu, kv, info, items):
         if it["kind"] == 1:
             assert it["q_count"] * g_ratio <= 16
         else:
-            assert it["split_group"] == -1
+            assert it["q_count"] * g_ratio <= info["prefill_rows"]
         for t in range(it["q_start"], it["q_start"] + it["q_count"]):
             cover.setdefault((t, g), []).append(it)
     for s in range(len(kv)):
@@ -61,6 +61,10 @@ def check_plan(w, cu, kv, info, items):
                     assert len(its) == n
                     assert sorted(it["split_index"] for it in its) == list(range(n))
                     assert len({it["partial_base"] for it in its}) == 1
+                    assert len({it["kind"] for it in its}) == 1
+                    if its[0]["kind"] == 0:   # prefill splits meet on 64-key boundaries
+                        cuts = sorted(it["kv_begin"] for it in its)[1:]
+                        assert all(c % 64 == 0 for c in cuts)
                 # union of the item key ranges, no overlap between splits
                 keys = []
                 for it in sorted(its, key=lambda x: x["kv_begin"]):
@@ -74,6 +78,15 @@ def check_plan(w, cu, kv, info, items):
                 rows = range(its[0]["q_start"] - cu[s], its[0]["q_start"] - cu[s] + its[0]["q_count"])
                 union = np.nonzero(vis[list(rows)].any(axis=0))[0]
                 assert lo == union.min() and hi == union.max() + 1
+    # partial-result slots: each group owns num_splits blocks of 16 rows (decode) or
+    # of prefill_rows rows (prefill), disjoint and within num_partials
+    used = []
+    for grp in {(it["split_group"], it["partial_base"], it["num_splits"], it["kind"])
+                for it in items if it["split_group"] >= 0}:
+        per = 1 if grp[3] == 1 else info["prefill_rows"] // 16
+        used.extend(range(grp[1], grp[1] + grp[2] * per))
+    assert len(used) == len(set(used))
+    assert all(0 <= u < info["num_partials"] for u in used)
 
 
 WORKLOADS = [
@@ -112,6 +125,42 @@ def test_plan_options_keep_coverage(options):
                 assert it["kv_end"] - it["kv_begin"] <= split
 
 
+def prefill_keys(items):
+    return [it["kv_end"] - it["kv_begin"] for it in items if it["kind"] == 0]
+
+
+def test_long_prefill_items_are_split_when_they_would_dominate():
+    """Mixed step, full causal: the last query tiles of the 4096-token chunk see
+    about twice the average key count of a compute unit, so they are cut along
+    their key range; the sliding-window and single-chunk workloads keep whole
+    items."""
+    w = wl.mixed(window=0)
+    cu, kv, info, items = plan_for(w)
+    check_plan(w, cu, kv, info, items)
+    piece = info["prefill_split_keys"]
+    assert piece > 0 and piece % 256 == 0
+    assert max(prefill_keys(items)) <= 1.5 * piece + 64
+    assert any(it["split_group"] >= 0 and it["kind"] == 0 for it in items)
+    unsplit = plan_for(w, [(RPA_OPT_PREFILL_SPLIT_KEYS, -1)])
+    assert unsplit[2]["prefill_split_keys"] == 0
+    assert max(prefill_keys(unsplit[3])) > 1.5 * piece
+    for w in [wl.mixed(window=1024), wl.swa_prefill(), wl.global_prefill()]:
+        info, items = plan_for(w)[2:]
+        assert info["prefill_split_keys"] == 0
+        assert all(it["split_group"] == -1 for it in items if it["kind"] == 0)
+
+
+@pytest.mark.parametrize("piece", [512, 700, 2000])
+def test_fixed_prefill_split_keeps_coverage(piece):
+    w = wl.custom([(1000, 3000), (3, 40), (700, 700), (1, 900)], 8, 2, 128, 16, 0, 5)
+    cu, kv, info, items = plan_for(w, [(RPA_OPT_PREFILL_SPLIT_KEYS, piece)])
+    check_plan(w, cu, kv, info, items)
+    rounded = -(-max(piece, 512) // 256) * 256
+    longest = max(prefill_keys(plan_for(w, [(RPA_OPT_PREFILL_SPLIT_KEYS, -1)])[3]))
+    assert info["prefill_split_keys"] == (rounded if longest > 1.5 * rounded else 0)
+    assert max(prefill_keys(items)) <= max(1.5 * rounded + 64, longest if longest <= 1.5 * rounded else 0)
+
+
 def test_decode_selection_rule():
     # q_len * G <= 16 -> decode kernel
     w = wl.custom([(1, 50), (2, 50), (3, 50)], 8, 1, 256, 128, 0, 9)
@@ -139,7 +188,7 @@ def test_chiplet_order_deals_short_runs(w, groups):
     consecutive items dealt to the chiplets 0..X-1, then X-1..0, and so on
     (exactly so when a round splits evenly), which keeps the chiplets' work
     within a few percent of each other."""
-    key = lambda it: (it["seq"], it["kv_head"], it["q_start"])
+    key = lambda it: (it["seq"], it["kv_head"], it["q_start"], it["split_index"])
     plain = [key(it) for it in plan_for(w, [(RPA_OPT_XCD_GROUPS, 0)])[3] if it["kind"] == 0]
     cu, kv, info, items = plan_for(w, [(RPA_OPT_XCD_GROUPS, groups)])
     check_plan(w, cu, kv, info, items)
