@@ -1087,56 +1087,60 @@ rpa_decode_kernel(KernelArgs args) {
     }
     if (half > 1) __syncthreads();
   }
-  // ---- wave 0 writes the output row (or the split's partial) from registers ----
-  const bool split = it.split_group >= 0;
-  if (!split) {
-    if (wave != 0 || !row_ok) return;
-    uint16_t* dst = args.out + q_off;
+  // ---- output rows (or the split's partial) through LDS, whole rows per store ----
+  // Wave 0 holds the combined rows; it writes them into slot 0 of the tree
+  // (row-major, rows padded to OSTRIDE floats) and every thread then stores
+  // 16 contiguous bytes of a row, consecutive threads along the row, instead
+  // of wave 0 storing 16-byte pieces strewn over 16 rows.
+  if (wave == 0 && row_ok) {
 #pragma unroll
     for (int u = 0; u < C::NU; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = u * 16 + lq * 4 + j;
-        if (c < C::NCH)
-          *reinterpret_cast<u32x4*>(dst + c * 8) =
-              u32x4{pack_bf16x2_split(o[u][0][j], o[u][1][j]), pack_bf16x2_split(o[u][2][j], o[u][3][j]),
-                    pack_bf16x2_split(o[u][4][j], o[u][5][j]), pack_bf16x2_split(o[u][6][j], o[u][7][j])};
-      }
+      for (int j = 0; j < 4; ++j)
+        if (u * 16 + lq * 4 + j < C::NCH) {
+          f32x4* dst = slot_ptr(0, u, j);
+          dst[0] = f32x4{o[u][0][j], o[u][1][j], o[u][2][j], o[u][3][j]};
+          dst[1] = f32x4{o[u][4][j], o[u][5][j], o[u][6][j], o[u][7][j]};
+        }
+  }
+  __syncthreads();
+  const bool split = it.split_group >= 0;
+  constexpr int C4 = D / 4;
+  if (!split) {
+    for (int idx = tid; idx < rows * C4; idx += C::NT) {
+      const int r = idx / C4;
+      const int c = idx - r * C4;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(lds_o + r * C::OSTRIDE + c * 4);
+      const int rt = r / G;
+      const int rh = r - rt * G;
+      *reinterpret_cast<u32x2*>(args.out + (static_cast<int64_t>(it.q_start + rt) * hq + g * G + rh) * D + c * 4) =
+          u32x2{pack_bf16x2_split(v[0], v[1]), pack_bf16x2_split(v[2], v[3])};
+    }
     return;
   }
-  if (wave == 0 && row_ok) {
-    const int64_t slot = static_cast<int64_t>(it.partial_base) + it.split_index;
-    float* dst = args.partial_o + (slot * 16 + ln) * D;
-#pragma unroll
-    for (int u = 0; u < C::NU; ++u)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = u * 16 + lq * 4 + j;
-        if (c < C::NCH) {
-          *reinterpret_cast<f32x4*>(dst + c * 8) = f32x4{o[u][0][j], o[u][1][j], o[u][2][j], o[u][3][j]};
-          *reinterpret_cast<f32x4*>(dst + c * 8 + 4) = f32x4{o[u][4][j], o[u][5][j], o[u][6][j], o[u][7][j]};
-        }
-      }
-    if (lq == 0) args.partial_lse[slot * 16 + ln] = (lsum > 0.f) ? base + __builtin_log2f(lsum) : kNegInf;
+  const int64_t slot = static_cast<int64_t>(it.partial_base) + it.split_index;
+  for (int idx = tid; idx < rows * C4; idx += C::NT) {
+    const int r = idx / C4;
+    const int c = idx - r * C4;
+    *reinterpret_cast<f32x4*>(args.partial_o + (slot * 16 + r) * D + c * 4) =
+        *reinterpret_cast<const f32x4*>(lds_o + r * C::OSTRIDE + c * 4);
   }
+  if (wave == 0 && row_ok && lq == 0)
+    args.partial_lse[slot * 16 + ln] = (lsum > 0.f) ? base + __builtin_log2f(lsum) : kNegInf;
   if (!args.fused_merge) return;
 
   // ---- last split of the group merges it (the group's ticket counts arrivals) ----
   // The workspace is uncached device memory: the stores above reach memory,
-  // where every workgroup's loads and the ticket atomic see them, once this
+  // where every workgroup's loads and the ticket atomic see them, once each
   // wave's vmcnt reaches zero.  The split that draws the last ticket then
   // reads all partials back (its own included) and merges them in split order
   // with the same arithmetic as the merge kernel, and resets the ticket for
   // the next call.
-  if (wave == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    int ticket = 0;
-    if (lane == 0)
-      ticket = __hip_atomic_fetch_add(args.merge_tickets + it.split_group, 1, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-    ticket = __shfl(ticket, 0);
-    if (lane == 0) *lds_flag = (ticket == it.num_splits - 1) ? 1 : 0;
-  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    *lds_flag = __hip_atomic_fetch_add(args.merge_tickets + it.split_group, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == it.num_splits - 1;
   __syncthreads();
   if (*lds_flag == 0) return;
   asm volatile("" ::: "memory");
