@@ -141,12 +141,18 @@ enum {
                                     that finishes last merges its group's
                                     partials; 0: a separate merge kernel does
                                     (same result)                               */
-  RPA_OPT_PREFILL_SPLIT_KEYS = 9  /* keys per split of a long prefill item: 0 =
+  RPA_OPT_PREFILL_SPLIT_KEYS = 9, /* keys per split of a long prefill item: 0 =
                                     automatic (split only when the longest item
                                     exceeds the average work of a compute unit
                                     by half), -1 = never split, > 0 = split every
                                     item longer than 1.5x this many keys (rounded
                                     up to 256); <= 2^30                         */
+  RPA_OPT_CONCURRENT = 10        /* 1 (default): when a step has decode items and
+                                    more prefill workgroups than compute units,
+                                    the decode kernel runs on a second stream of
+                                    the context, forked from and joined back
+                                    into the caller's stream; 0: both kernels
+                                    on the caller's stream                      */
 };
 /* Returns RPA_OK or RPA_ERR_INVALID_ARG (unknown option or bad value). */
 int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);

@@ -142,6 +142,9 @@ def test_set_option_validation():
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_KERNEL_TIMING, 65537) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_KERNEL_TIMING, 16) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_KERNEL_TIMING, 0) == _lib.RPA_OK
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_CONCURRENT, 2) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_CONCURRENT, 0) == _lib.RPA_OK
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_CONCURRENT, 1) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_PREFILL_SPLIT_KEYS, -2) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_PREFILL_SPLIT_KEYS, (1 << 30) + 1) == _lib.RPA_ERR_INVALID_ARG
     for v in (-1, 0, 512, 1 << 30):

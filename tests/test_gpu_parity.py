@@ -100,6 +100,10 @@ VARIANTS = [
     ("merge_kernel", {R.RPA_OPT_FUSED_MERGE: 0}),
     ("merge_kernel_split32", {R.RPA_OPT_FUSED_MERGE: 0, R.RPA_OPT_DECODE_SPLIT_KEYS: 32}),
     ("chiplets3", {R.RPA_OPT_XCD_GROUPS: 3}),
+    ("single_stream", {R.RPA_OPT_CONCURRENT: 0}),
+    ("prefill_split512", {R.RPA_OPT_PREFILL_SPLIT_KEYS: 512}),
+    ("prefill_split512_one_stream_merge_kernel", {R.RPA_OPT_PREFILL_SPLIT_KEYS: 512, R.RPA_OPT_CONCURRENT: 0,
+                                                  R.RPA_OPT_FUSED_MERGE: 0}),
 ]
 
 
@@ -290,6 +294,25 @@ def test_prefill_splits(hq, hkv, d, b, seqs, window):
     base = run_gpu(whole, inp)
     compare(base, ref, label="unsplit")
     assert (base.float() - got.float()).abs().max().item() <= 2e-2
+
+
+def test_concurrent_decode_stream():
+    """More prefill workgroups than compute units plus decodes: the decode kernel
+    runs on the context's second stream.  Same bits as one stream, over
+    repeated calls, and oracle parity."""
+    w = wl.custom([(20, 40 + (i % 7)) for i in range(300)] + [(1, 100 + i) for i in range(60)], 4, 1, 64, 16, 0,
+                  seed=31)
+    inp = wl.make_inputs(w, poison=True)
+    ref = oracle_rows(inp)
+    one = make_attn(w)
+    one.set_option(R.RPA_OPT_CONCURRENT, 0)
+    base = run_gpu(one, inp).clone()
+    compare(base, ref, label="one stream")
+    two = make_attn(w)
+    info, _ = two.plan(inp.cu_q_lens, inp.kv_lens, 0)
+    assert info["num_prefill_items"] > 256 and info["num_decode_items"] > 0
+    for _ in range(3):
+        assert torch.equal(run_gpu(two, inp), base)
 
 
 def test_long_contexts_sampled():
