@@ -79,8 +79,8 @@ def kernel_work(w, items, merge_kernel=True):
 
     A sequence belongs to the kernel kind of its work items.  Bytes count Q,
     the unique K/V rows its queries see and its page-table entries; O goes to
-    the kernel that writes it (the merge kernel for split decode sequences
-    when it runs, else the decode kernel, whose last split merges them).
+    the kernel that writes it (the merge kernel for split sequences when it
+    runs, else the prefill or decode kernel, whose last split merges them).
     """
     from ragged_paged_attention_forward_amd import metrics
     kind_of = {}
@@ -94,7 +94,7 @@ def kernel_work(w, items, merge_kernel=True):
         ids = [s for s, k in kind_of.items() if k == kind]
         seqs = [w.seqs[s] for s in ids]
         q_b = metrics.qo_bytes(seqs, w.num_q_heads, w.head_dim) // 2
-        o_ids = ids if (kind == "decode" and not merge_kernel) else [s for s in ids if s not in split]
+        o_ids = ids if not merge_kernel else [s for s in ids if s not in split]
         o_b = metrics.qo_bytes([w.seqs[s] for s in o_ids], w.num_q_heads, w.head_dim) // 2
         kv = metrics.kv_bytes(seqs, w.window, w.num_kv_heads, w.head_dim)
         pages = sum(-(-kvl // w.page_size) for _, kvl in seqs) * 4
@@ -262,7 +262,13 @@ def run(args):
     attn.set_option(R.RPA_OPT_KERNEL_TIMING, 0)
 
     work = kernel_work(w, items, merge_kernel="merge" in kernels)
-    dom = max(kernels, key=lambda k: kernels[k]["mean_ms"])
+    # The dominant kernel is the one with the largest roofline time (its
+    # algorithmic FLOPs at the MFMA peak or bytes at the HBM peak, whichever
+    # is larger): with the decode kernel on a second stream, durations overlap
+    # and the longest one need not be the one that bounds the step.
+    def roof_s(k):
+        return max(work[k]["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12), work[k]["bytes"] / (HBM_PEAK_GBS * 1e9))
+    dom = max(kernels, key=roof_s)
     kw = work[dom]
     k_ms = kernels[dom]["mean_ms"]
     t_mfma = kw["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
