@@ -43,6 +43,9 @@ def compile_flags():
         # packed fp32 VALU forms stay off: the compiler would otherwise emit them
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
+        # the five leading kernel arguments (work items, page table, Q, K, V:
+        # ten scalar registers) arrive preloaded in scalar registers
+        "-mllvm", "-amdgpu-kernarg-preload-count=5",
     ]
 
 

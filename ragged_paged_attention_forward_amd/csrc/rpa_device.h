@@ -116,6 +116,17 @@ RPA_DEV int32_t uniform_load(const int32_t* p, int idx) {
 }
 
 // KernelArgs: see rpa_kargs.h
+//
+// The pointers every work item needs first (its work item, the page table,
+// Q, K and V) are separate kernel arguments ahead of the argument block, so
+// that the build can preload them into scalar registers at wave launch
+// (kernel-argument preloading, gfx950): the work-item load then needs no
+// earlier load of the argument block, and the first K/V loads of a workgroup
+// wait on two dependent memory round trips instead of three.
+#define RPA_HOT_POINTERS                                                                  \
+  const rpa_work_item* __restrict__ items, const int32_t* __restrict__ page_table,        \
+      const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pages,               \
+      const uint16_t* __restrict__ v_pages
 
 RPA_DEV bool key_visible(int key, int pos, int kv_begin, int kv_end, int window) {
   return key >= kv_begin && key < kv_end && key <= pos && (window <= 0 || key > pos - window);
@@ -271,13 +282,16 @@ RPA_DEV int xor_v(int s) { return (s & 1) * 2; }
 
 template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI>
 __global__ void __launch_bounds__(NW * 64, 1)
-rpa_prefill_kernel(KernelArgs args) {
+rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   using C = PrefillCfg<D, BN, NW, NB, NS, DS>;
   constexpr int DH = C::DH;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   char* lds = reinterpret_cast<char*>(smem);
 
-  const rpa_work_item it = args.items[blockIdx.x];
+  const rpa_work_item it = items[blockIdx.x];
+  // the work item's load goes out before the argument block's: nothing is
+  // scheduled across this point, so the two loads are in flight together
+  __builtin_amdgcn_sched_barrier(0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -292,9 +306,9 @@ rpa_prefill_kernel(KernelArgs args) {
   const int hkv = args.num_kv_heads;
   const int G = args.group;
   const int g = it.kv_head;
-  const int32_t* __restrict__ pt_row = args.page_table + static_cast<int64_t>(it.seq) * args.max_pages;
-  const uint16_t* __restrict__ kbase = args.k;
-  const uint16_t* __restrict__ vbase = args.v;
+  const int32_t* __restrict__ pt_row = page_table + static_cast<int64_t>(it.seq) * args.max_pages;
+  const uint16_t* __restrict__ kbase = k_pages;
+  const uint16_t* __restrict__ vbase = v_pages;
   const int page_size = args.page_size;
   const int row_bytes = hkv * D * 2;   // bytes between consecutive key rows of a page
 
@@ -327,7 +341,7 @@ rpa_prefill_kernel(KernelArgs args) {
     const int64_t row_off = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
 #pragma unroll
     for (int kk = 0; kk < DH / 16; ++kk)
-      qf[nb][kk] = row_ok ? load16(args.q + row_off + dh * DH + kk * 16 + lq2 * 8) : u32x4{0, 0, 0, 0};
+      qf[nb][kk] = row_ok ? load16(q + row_off + dh * DH + kk * 16 + lq2 * 8) : u32x4{0, 0, 0, 0};
   }
   // positions spanned by this wave's valid rows (tile skipping / mask-free tiles)
   const int tk_lo = (rw * NB * 32) / G;
@@ -859,7 +873,7 @@ struct DecodeCfg {
 // workgroups of 4 waves; one for D = 512 whose fragments need the full file).
 template <int D, int NW, bool UNI>
 __global__ void __launch_bounds__(NW * 64, D >= 512 ? 1 : 2)
-rpa_decode_kernel(KernelArgs args) {
+rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   using C = DecodeCfg<D, NW>;
   extern __shared__ __attribute__((aligned(16))) float dsm[];
   float* lds_o = dsm;                     // [NW/2][16][OSTRIDE]
@@ -867,7 +881,10 @@ rpa_decode_kernel(KernelArgs args) {
   float* lds_l = lds_m + NW * 16;         // [NW][16]
   int* lds_flag = reinterpret_cast<int*>(lds_l + NW * 16);
 
-  const rpa_work_item it = args.items[blockIdx.x];
+  const rpa_work_item it = items[blockIdx.x];
+  // the work item's load goes out before the argument block's: nothing is
+  // scheduled across this point, so the two loads are in flight together
+  __builtin_amdgcn_sched_barrier(0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -878,9 +895,9 @@ rpa_decode_kernel(KernelArgs args) {
   const int G = args.group;
   const int g = it.kv_head;
   const int rows = it.q_count * G;
-  const int32_t* __restrict__ pt_row = args.page_table + static_cast<int64_t>(it.seq) * args.max_pages;
-  const uint16_t* __restrict__ kbase = args.k;
-  const uint16_t* __restrict__ vbase = args.v;
+  const int32_t* __restrict__ pt_row = page_table + static_cast<int64_t>(it.seq) * args.max_pages;
+  const uint16_t* __restrict__ kbase = k_pages;
+  const uint16_t* __restrict__ vbase = v_pages;
   const int page_size = args.page_size;
   const int64_t row_stride = static_cast<int64_t>(hkv) * D;
   const int kv_begin = it.kv_begin;
@@ -898,7 +915,7 @@ rpa_decode_kernel(KernelArgs args) {
   u32x4 qf[D / 32];
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk)
-    qf[kk] = row_ok ? load16(args.q + q_off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
+    qf[kk] = row_ok ? load16(q + q_off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
 
   f32x4 o[C::NU][8];
 #pragma unroll
@@ -1162,7 +1179,7 @@ static hipError_t launch_prefill_u(const KernelArgs& a, int n_items, hipStream_t
     attr_set = true;
   }
   hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, NS, DS, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
-                     stream, a);
+                     stream, a.items, a.page_table, a.q, a.k, a.v, a);
   return hipGetLastError();
 }
 
@@ -1177,7 +1194,8 @@ static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, hipStream_t
 template <int D, int NW, bool UNI>
 static hipError_t launch_decode_u(const KernelArgs& a, int n_items, hipStream_t stream) {
   using C = DecodeCfg<D, NW>;
-  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream, a);
+  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream, a.items,
+                     a.page_table, a.q, a.k, a.v, a);
   return hipGetLastError();
 }
 
