@@ -187,6 +187,50 @@ def copy_calibration(torch, dev):
     del a, b
 
 
+def measured_peak(torch, R, dev, bound: str, nbytes: int):
+    """What the device sustains for the dominant kernel's bound, measured here:
+    a plain streaming read of the same byte count from cold memory (best of
+    two grid sizes), or independent bf16 MFMA chains on every compute unit."""
+    stream = torch.cuda.current_stream(dev)
+
+    def time_launches(launch, n):
+        ts = []
+        for i in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch(i)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    if bound == "hbm":
+        nb = max(16, (int(nbytes) + 15) // 16 * 16)
+        slices = max(4, int(np.ceil(4 * LLC_BYTES / nb)))   # rotate so no read finds its slice in the LLC
+        pool = torch.empty(nb * slices, dtype=torch.uint8, device=dev)
+        pool.fill_(1)
+        best = None
+        for wgs in (512, 1024):
+            sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+            launch = lambda i: R.probe_read(pool[(i % slices) * nb:], nb, wgs, sink, stream)
+            time_launches(launch, 5)
+            ms = time_launches(launch, 40)
+            best = ms if best is None else min(best, ms)
+        del pool
+        return {"value": round(nb / (best * 1e-3) / 1e9, 1), "unit": "GB/s",
+                "probe": f"rpa_probe_read: plain streaming read of the same {nb} bytes, cold "
+                         f"(rotated over {slices} slices), median of 40 launches, best of 512/1024 workgroups"}
+    wgs, iters = 1024, 2048
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    flops = R.probe_mfma(wgs, iters, sink, stream)
+    launch = lambda i: R.probe_mfma(wgs, iters, sink, stream)
+    time_launches(launch, 2)
+    ms = time_launches(launch, 5)
+    return {"value": round(flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+            "probe": f"rpa_probe_mfma: {wgs} workgroups x 8 waves x {iters} x 4 independent "
+                     "v_mfma_f32_32x32x16_bf16, median of 5 launches"}
+
+
 def run(args):
     import torch
     import rpa_workloads as wl
@@ -277,8 +321,10 @@ def run(args):
         bound, achieved, peak, unit = "mfma", kw["flops"] / (k_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
         bound, achieved, peak, unit = "hbm", kw["bytes"] / (k_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    mp = measured_peak(torch, R, dev, bound, kw["bytes"])
+    mp["frac"] = round(achieved / mp["value"], 4)
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4),
+                "frac": round(achieved / peak, 4), "measured_peak": mp,
                 "traffic": load_traffic(args.workload, KERNEL_NAMES[dom]),
                 "kernel": KERNEL_NAMES[dom], "kernel_ms_mean": k_ms,
                 "algorithmic_bytes": kw["bytes"], "algorithmic_flops": kw["flops"],

@@ -175,6 +175,32 @@ enum { RPA_KERNEL_PREFILL = 0, RPA_KERNEL_DECODE = 1, RPA_KERNEL_MERGE = 2 };
 int rpa_kernel_times(rpa_ctx* ctx, int32_t kind, float* ms, int32_t capacity, int32_t* count);
 
 /*
+ * Measured-peak probes (diagnostics; no attention arithmetic).  The metric
+ * asks for each kernel's throughput against the published peaks and, as a
+ * diagnostic, against what the device measurably sustains: these two kernels
+ * measure that.  Both enqueue one launch on `stream` (a hipStream_t, NULL for
+ * the default stream) and return at once; time them with events on that stream.
+ *
+ * rpa_probe_read -- stream `bytes` bytes of device memory at `src` (16-byte
+ * aligned, bytes a positive multiple of 16) through the compute units: each
+ * of `workgroups` (1 .. 65536) workgroups of 256 threads reads one contiguous
+ * slice with 16-byte loads, and every thread writes one 32-bit fold of what it
+ * read to `sink` (device memory of workgroups * 256 uint32, caller-owned).
+ * The best case for moving that many bytes from HBM into the chip.
+ *
+ * rpa_probe_mfma -- `workgroups` (1 .. 65536) workgroups of 512 threads, each
+ * wave running 4 independent chains of `iterations` (>= 1)
+ * v_mfma_f32_32x32x16_bf16 (the prefill kernel's instruction) on register
+ * operands; work = workgroups * 8 * iterations * 4 * 32768 FLOP.  Every thread
+ * writes one float to `sink` (device memory of workgroups * 512 floats).
+ *
+ * Return RPA_OK, RPA_ERR_INVALID_ARG (bad pointer or size; nothing enqueued)
+ * or RPA_ERR_HIP (launch failure).
+ */
+int rpa_probe_read(const void* src, int64_t bytes, int32_t workgroups, void* sink, void* stream);
+int rpa_probe_mfma(int32_t workgroups, int32_t iterations, void* sink, void* stream);
+
+/*
  * Planner introspection (host only, no device call).  The host builds the
  * work list that the kernels consume: one item per (sequence, KV head, query
  * tile, key range), the GPU form of the per-sequence metadata the pages'

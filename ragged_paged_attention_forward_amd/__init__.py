@@ -31,7 +31,7 @@ __all__ = ["RaggedPagedAttention", "rpa_forward", "RpaError", "library_path", "R
            "RPA_ERR_INVALID_ARG", "RPA_ERR_UNSUPPORTED", "RPA_ERR_OOM", "RPA_ERR_HIP",
            "RPA_OPT_DECODE_SPLIT_KEYS", "RPA_OPT_PATH", "RPA_OPT_DECODE_MAX_ROWS",
            "RPA_OPT_DECODE_WAVES", "RPA_OPT_KERNEL_TIMING", "RPA_OPT_XCD_GROUPS", "RPA_OPT_FUSED_MERGE", "RPA_OPT_PREFILL_SPLIT_KEYS", "RPA_OPT_CONCURRENT", "RPA_KERNEL_PREFILL", "RPA_KERNEL_DECODE",
-           "RPA_KERNEL_MERGE", "KERNEL_KINDS"]
+           "RPA_KERNEL_MERGE", "KERNEL_KINDS", "probe_read", "probe_mfma"]
 
 KERNEL_KINDS = {"prefill": RPA_KERNEL_PREFILL, "decode": RPA_KERNEL_DECODE, "merge": RPA_KERNEL_MERGE}
 
@@ -190,3 +190,31 @@ def rpa_forward(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, window: int
         return res
     finally:
         attn.close()
+
+
+def probe_read(src: torch.Tensor, nbytes: int, workgroups: int, sink: torch.Tensor,
+               stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue the streaming-read probe over the first ``nbytes`` of ``src``
+    (``rpa_probe_read``); ``sink`` holds ``workgroups * 256`` int32."""
+    if not src.is_cuda or not sink.is_cuda or sink.numel() * sink.element_size() < workgroups * 256 * 4:
+        raise ValueError("src and sink must be CUDA tensors; sink needs workgroups * 256 words")
+    if nbytes > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds src")
+    stream = stream or torch.cuda.current_stream(src.device)
+    st = _lib.load().rpa_probe_read(src.data_ptr(), int(nbytes), int(workgroups), sink.data_ptr(),
+                                    ctypes.c_void_p(stream.cuda_stream))
+    if st != RPA_OK:
+        raise RpaError(st, "rpa_probe_read")
+
+
+def probe_mfma(workgroups: int, iterations: int, sink: torch.Tensor,
+               stream: Optional[torch.cuda.Stream] = None) -> int:
+    """Enqueue the MFMA-throughput probe (``rpa_probe_mfma``); returns its FLOP count."""
+    if not sink.is_cuda or sink.numel() * sink.element_size() < workgroups * 512 * 4:
+        raise ValueError("sink must be a CUDA tensor of workgroups * 512 floats")
+    stream = stream or torch.cuda.current_stream(sink.device)
+    st = _lib.load().rpa_probe_mfma(int(workgroups), int(iterations), sink.data_ptr(),
+                                    ctypes.c_void_p(stream.cuda_stream))
+    if st != RPA_OK:
+        raise RpaError(st, "rpa_probe_mfma")
+    return int(workgroups) * 8 * int(iterations) * 4 * 32768

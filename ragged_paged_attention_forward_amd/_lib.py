@@ -28,7 +28,7 @@ RPA_KERNEL_DECODE = 1
 RPA_KERNEL_MERGE = 2
 
 EXPORTED = ("rpa_create", "rpa_forward", "rpa_destroy", "rpa_status_string", "rpa_last_error",
-            "rpa_set_option", "rpa_plan", "rpa_kernel_times")
+            "rpa_set_option", "rpa_plan", "rpa_kernel_times", "rpa_probe_read", "rpa_probe_mfma")
 
 
 class Config(ctypes.Structure):
@@ -98,5 +98,9 @@ def load() -> ctypes.CDLL:
     lib.rpa_kernel_times.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
                                      i32p]
     lib.rpa_kernel_times.restype = ctypes.c_int
+    lib.rpa_probe_read.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp]
+    lib.rpa_probe_read.restype = ctypes.c_int
+    lib.rpa_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.rpa_probe_mfma.restype = ctypes.c_int
     _lib = lib
     return lib

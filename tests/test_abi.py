@@ -183,3 +183,18 @@ def test_status_strings():
     for code, name in ((0, b"RPA_OK"), (-1, b"RPA_ERR_INVALID_ARG"), (-2, b"RPA_ERR_UNSUPPORTED"),
                        (-3, b"RPA_ERR_OOM"), (-4, b"RPA_ERR_HIP"), (7, b"RPA_ERR_UNKNOWN")):
         assert lib.rpa_status_string(code) == name
+
+
+def test_probes_reject_bad_arguments_before_launch():
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(64)
+    addr = ctypes.addressof(buf)
+    assert lib.rpa_probe_read(None, 64, 1, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 64, 1, None, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 0, 1, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 24, 1, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 64, 0, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 64, 65537, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_mfma(0, 1, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_mfma(1, 0, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_mfma(1, 1, None, None) == _lib.RPA_ERR_INVALID_ARG
