@@ -126,9 +126,8 @@ enum {
                                     prefill kernel, 2 decode kernel wherever the
                                     rows of a sequence fit one decode item      */
   RPA_OPT_DECODE_MAX_ROWS = 4,   /* most q_len * G rows of a decode item (1..16)  */
-  RPA_OPT_DECODE_WAVES = 5,      /* waves per decode workgroup: 0 automatic (8
-                                    below head size 512, else 4), 4, 8 (head
-                                    size 512 always runs 4)                     */
+  RPA_OPT_DECODE_WAVES = 5,      /* waves per decode workgroup: 0 automatic
+                                    (4), 4, 8 (head size 512 always runs 4)     */
   RPA_OPT_KERNEL_TIMING = 6,     /* n > 0: time up to n launches per kernel kind
                                     (see rpa_kernel_times); 0 = off (default),
                                     n <= 65536                                  */

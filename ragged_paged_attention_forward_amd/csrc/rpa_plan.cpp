@@ -255,6 +255,30 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
   }
   out->decode_split_keys = static_cast<int>(split);
 
+  // Split boundaries: n = ceil(keys / split) pieces of about equal length, on
+  // multiples of the keys one wave takes per step (so that no wave chunk is
+  // read by two pieces), each at most `split` keys; where rounding would
+  // break that bound, fixed pieces of `split` keys and a remainder.  Equal
+  // pieces keep the split groups' pieces shorter than the longest unsplit
+  // items, so that their merge overlaps the streaming of the others.
+  std::vector<int64_t> bounds;
+  auto split_bounds = [&](int64_t kv_begin, int64_t kv_end, int32_t n) {
+    const int64_t keys = kv_end - kv_begin;
+    const int64_t w = std::max(1, p.decode_wave_keys);
+    bounds.assign(n + 1, kv_begin);
+    bounds[n] = kv_end;
+    bool ok = true;
+    for (int32_t i = 1; i < n; ++i) {
+      int64_t b = kv_begin + (keys * i + n / 2) / n;
+      b = (b + w / 2) / w * w;
+      bounds[i] = std::min(std::max(b, kv_begin), kv_end);
+    }
+    for (int32_t i = 0; i < n; ++i)
+      ok = ok && bounds[i + 1] > bounds[i] && bounds[i + 1] - bounds[i] <= split;
+    if (!ok)
+      for (int32_t i = 1; i < n; ++i) bounds[i] = kv_begin + int64_t(i) * split;
+  };
+
   for (const auto& d : dec) {
     const int64_t keys = d.kv_end - d.kv_begin;
     const int32_t n = static_cast<int32_t>(std::max<int64_t>(1, (keys + split - 1) / split));
@@ -279,11 +303,12 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
       base.split_group = static_cast<int32_t>(out->groups.size());
       base.partial_base = out->num_partials;
       out->num_partials += n;
+      split_bounds(d.kv_begin, d.kv_end, n);
       for (int32_t i = 0; i < n; ++i) {
         rpa_work_item it = base;
         it.split_index = i;
-        it.kv_begin = static_cast<int32_t>(d.kv_begin + int64_t(i) * split);
-        it.kv_end = static_cast<int32_t>(std::min<int64_t>(d.kv_end, d.kv_begin + int64_t(i + 1) * split));
+        it.kv_begin = static_cast<int32_t>(bounds[i]);
+        it.kv_end = static_cast<int32_t>(bounds[i + 1]);
         if (i == 0) {
           rpa_work_item grp = it;
           grp.kv_begin = d.kv_begin;
