@@ -253,12 +253,16 @@ struct PrefillCfg {
   // LDS layout of a tile: 1 KB blocks (one direct load each) followed by a
   // pad; inside a block, row s sits at s*ROW_B with its 16-byte chunk c at
   // position c ^ x(s).  K and V use different pads / XORs, chosen so that the
-  // K operand reads (16 consecutive rows, one chunk) and the transposing V
-  // reads (4 consecutive rows, two chunks) hit distinct banks, and so that the
-  // chunk index of an operand stays additive in the loop counter (the XOR
-  // only touches bit 0 for K and bits 0-1 for V).
+  // operand reads hit distinct banks of the 64 x 4-byte LDS banks: a 16-byte
+  // read serves 16 lanes per pass (K: 16 consecutive rows, one chunk), an
+  // 8-byte transposing read 32 lanes (V: 4 consecutive rows x 64 bytes, which
+  // must fall in the four distinct 64-byte bank windows of 256 bytes).  The
+  // XOR touches bit 0 of the chunk for K; for V it touches bit 1, or with two
+  // rows per block bit 2 (XV = 4: odd rows move to the neighbouring 64-byte
+  // window, so a V read's offset depends on the parity of its 64-byte d block).
   static constexpr int PAD_K = RPI == 1 ? 16 : RPI == 2 ? 32 : 64;
-  static constexpr int PAD_V = RPI == 1 ? 32 : 64;
+  static constexpr int PAD_V = RPI == 2 ? 128 : 64;
+  static constexpr int XV = RPI == 2 ? 4 : 2;       // chunk XOR of odd V rows
   static constexpr int BLK_K = 1024 + PAD_K;
   static constexpr int BLK_V = 1024 + PAD_V;
   static constexpr int TILE_K = BLOCKS * BLK_K;
@@ -278,7 +282,6 @@ struct PrefillCfg {
 };
 
 RPA_DEV int xor_k(int s) { return s & 1; }
-RPA_DEV int xor_v(int s) { return (s & 1) * 2; }
 
 template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI>
 __global__ void __launch_bounds__(NW * 64, 1)
@@ -396,7 +399,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     const int p = (in_blk % C::ROW_B) / 16;
     srow[i] = blk * C::RPI + sr;
     sgk[i] = (p ^ xor_k(sr)) * 16;
-    sgv[i] = (p ^ xor_v(sr)) * 16;
+    sgv[i] = (p ^ ((sr & 1) * C::XV)) * 16;
   }
   // Page and slot of the next tile to stage, advanced tile by tile (a tile
   // never crosses a page here) and reset when the order wraps to the start of
@@ -471,13 +474,22 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     const int sr = r % C::RPI;
     kaddr[kb] = (r / C::RPI) * C::BLK_K + sr * C::ROW_B + (lq2 ^ xor_k(sr)) * 16;
   }
-  int vaddr[2];
+  // vaddr[half][par]: V reads of the 64-byte d blocks of parity par (the odd
+  // rows' XOR on chunk bit 2 maps d block b to b ^ 1, i.e. +64 or -64 bytes)
+  int vaddr[2][2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int r = 4 * lq2 + (l16 >> 2) + 8 * half;
     const int sr = r % C::RPI;
     const int cl = 2 * (grp & 1) + ((l16 & 3) >> 1);
-    vaddr[half] = C::TILE_K + (r / C::RPI) * C::BLK_V + sr * C::ROW_B + ((cl ^ xor_v(sr)) * 16) + (l16 & 1) * 8;
+    const int xv = (sr & 1) * C::XV;
+    const int base = C::TILE_K + (r / C::RPI) * C::BLK_V + sr * C::ROW_B + (l16 & 1) * 8;
+    if constexpr (C::XV == 4) {
+      vaddr[half][0] = base + cl * 16 + (xv ? 64 : 0);
+      vaddr[half][1] = base + cl * 16 - (xv ? 64 : 0);
+    } else {
+      vaddr[half][0] = vaddr[half][1] = base + (cl ^ xv) * 16;
+    }
   }
 
   // tile starting at key kt fully masked for this wave's rows: nothing to add
@@ -575,8 +587,8 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       const char* vrow = ks + ks16 * (16 / C::RPI) * C::BLK_V;
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db) {
-        const u32x2 l2 = lds_read_tr16(vrow + vaddr[0] + dh * DH * 2 + db * 64);
-        const u32x2 h2 = lds_read_tr16(vrow + vaddr[1] + dh * DH * 2 + db * 64);
+        const u32x2 l2 = lds_read_tr16(vrow + vaddr[0][db & 1] + dh * DH * 2 + db * 64);
+        const u32x2 h2 = lds_read_tr16(vrow + vaddr[1][db & 1] + dh * DH * 2 + db * 64);
         const u32x4 a = u32x4{l2[0], l2[1], h2[0], h2[1]};
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) o[db][nb] = mfma32(a, pf[ks16][nb], o[db][nb]);
