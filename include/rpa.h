@@ -146,9 +146,9 @@ enum {
                                     by half), -1 = never split, > 0 = split every
                                     item longer than 1.5x this many keys (rounded
                                     up to 256); <= 2^30                         */
-  RPA_OPT_CONCURRENT = 10        /* 1 (default): when a step has decode items and
-                                    more prefill workgroups than compute units,
-                                    the decode kernel runs on a second stream of
+  RPA_OPT_CONCURRENT = 10        /* 1 (default): when a step has both decode
+                                    and prefill items, the decode kernel runs
+                                    on a second stream of
                                     the context, forked from and joined back
                                     into the caller's stream; 0: both kernels
                                     on the caller's stream                      */

@@ -296,12 +296,13 @@ def test_prefill_splits(hq, hkv, d, b, seqs, window):
     assert (base.float() - got.float()).abs().max().item() <= 2e-2
 
 
-def test_concurrent_decode_stream():
-    """More prefill workgroups than compute units plus decodes: the decode kernel
-    runs on the context's second stream.  Same bits as one stream, over
-    repeated calls, and oracle parity."""
-    w = wl.custom([(20, 40 + (i % 7)) for i in range(300)] + [(1, 100 + i) for i in range(60)], 4, 1, 64, 16, 0,
-                  seed=31)
+@pytest.mark.parametrize("n_prefill", [300, 12])
+def test_concurrent_decode_stream(n_prefill):
+    """Prefill items (more than the compute units, or a few) plus decodes: the
+    decode kernel runs on the context's second stream.  Same bits as one
+    stream, over repeated calls, and oracle parity."""
+    w = wl.custom([(20, 40 + (i % 7)) for i in range(n_prefill)] + [(1, 100 + i) for i in range(60)], 4, 1, 64,
+                  16, 0, seed=31)
     inp = wl.make_inputs(w, poison=True)
     ref = oracle_rows(inp)
     one = make_attn(w)
@@ -310,7 +311,7 @@ def test_concurrent_decode_stream():
     compare(base, ref, label="one stream")
     two = make_attn(w)
     info, _ = two.plan(inp.cu_q_lens, inp.kv_lens, 0)
-    assert info["num_prefill_items"] > 256 and info["num_decode_items"] > 0
+    assert info["num_prefill_items"] > 0 and info["num_decode_items"] > 0
     for _ in range(3):
         assert torch.equal(run_gpu(two, inp), base)
 
