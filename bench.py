@@ -258,9 +258,14 @@ def run(args):
 
     attn = R.RaggedPagedAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
                                   w.num_seqs, w.max_pages_per_seq, t_q)
-    t_plan = time.perf_counter()
     info, items = attn.plan(cu, kv, w.window)
-    planner_us = (time.perf_counter() - t_plan) * 1e6
+    # host metadata builder: one rpa_plan call (work list built, not copied out), best of 20
+    plan_s = []
+    for _ in range(20):
+        t_plan = time.perf_counter()
+        attn.plan_info(cu, kv, w.window)
+        plan_s.append(time.perf_counter() - t_plan)
+    planner_us = min(plan_s) * 1e6
     stream = torch.cuda.current_stream(dev)
 
     def step(i):

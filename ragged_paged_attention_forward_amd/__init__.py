@@ -97,6 +97,18 @@ class RaggedPagedAttention:
         if option == RPA_OPT_KERNEL_TIMING:
             self._timing_cap = int(value)
 
+    def plan_info(self, cu_q_lens, kv_lens, window: int = 0) -> dict:
+        """Build the work list on the host (``rpa_plan`` without copying items) and
+        return its summary."""
+        cu = _host_i32(cu_q_lens)
+        kv = _host_i32(kv_lens)
+        info = PlanInfo()
+        st = self._lib.rpa_plan(self._ctx, _i32p(cu), _i32p(kv), int(kv.shape[0]), int(window),
+                                ctypes.byref(info), None, 0)
+        if st != RPA_OK:
+            raise self._error(st, "rpa_plan")
+        return info.as_dict()
+
     def plan(self, cu_q_lens, kv_lens, window: int = 0) -> Tuple[dict, list]:
         cu = _host_i32(cu_q_lens)
         kv = _host_i32(kv_lens)
