@@ -103,6 +103,34 @@ int rpa_forward(rpa_ctx* ctx, const void* q, const void* k_pages, const void* v_
                 const int32_t* page_table, const int32_t* cu_q_lens, const int32_t* kv_lens,
                 int32_t num_seqs, int32_t window, float scale, void* out, void* stream);
 
+/*
+ * rpa_forward_append -- write the step's new keys and values into their
+ * pages, then the same attention as rpa_forward, in one call.  The pages'
+ * kernel takes the step's new tokens into the paged cache within the
+ * attention call ("TPU Deep Dive", chapter 8, ragged paged attention).
+ *
+ *   k_new, v_new  device, bf16 [T, Hkv, D] row-major (16-byte aligned): row t
+ *                 holds the new token at flattened query index t, i.e.
+ *                 position p = kv_len_s - q_len_s + (t - cu_q_lens[s]) of its
+ *                 sequence s; it is written to slot p % page_size of page
+ *                 page_table[s][p / page_size] of k_pages / v_pages
+ *   k_pages, v_pages  as for rpa_forward but written: the slots of the step's
+ *                 tokens are overwritten with k_new / v_new, every other byte
+ *                 is left as it was; the two must be distinct buffers, and
+ *                 k_new / v_new must not overlap them
+ *   all other arguments as for rpa_forward (kv_len counts the new tokens)
+ *
+ * The copy runs on `stream` before the attention kernels (which then see the
+ * new rows); page slots of different tokens must be distinct (a page table
+ * that maps two positions to one slot leaves either row there).  Errors as
+ * for rpa_forward, plus RPA_ERR_INVALID_ARG for a NULL k_new / v_new or
+ * k_pages == v_pages.
+ */
+int rpa_forward_append(rpa_ctx* ctx, const void* q, const void* k_new, const void* v_new, void* k_pages,
+                       void* v_pages, const int32_t* page_table, const int32_t* cu_q_lens,
+                       const int32_t* kv_lens, int32_t num_seqs, int32_t window, float scale, void* out,
+                       void* stream);
+
 /* rpa_destroy -- free a context (NULL-safe).  The caller must first make sure
  * no work enqueued with it is still running. */
 void rpa_destroy(rpa_ctx* ctx);
@@ -170,7 +198,7 @@ int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);
  * RPA_ERR_INVALID_ARG (null ctx/count, bad kind, negative capacity) or
  * RPA_ERR_HIP.
  */
-enum { RPA_KERNEL_PREFILL = 0, RPA_KERNEL_DECODE = 1, RPA_KERNEL_MERGE = 2 };
+enum { RPA_KERNEL_PREFILL = 0, RPA_KERNEL_DECODE = 1, RPA_KERNEL_MERGE = 2, RPA_KERNEL_APPEND = 3 };
 int rpa_kernel_times(rpa_ctx* ctx, int32_t kind, float* ms, int32_t capacity, int32_t* count);
 
 /*

@@ -174,6 +174,35 @@ def forward(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, window: int,
     return forward_rows(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, window, scale)
 
 
+def append_kv(k_pages, v_pages, page_table, cu_q_lens, kv_lens, k_new, v_new):
+    """The step's new keys and values written into their pages, as the pages'
+    kernel does within the attention call ("TPU Deep Dive", chapter 8: ragged
+    paged attention handles true lengths in the kernel, with a fused KV write).
+
+    Token t of sequence s (cu[s] <= t < cu[s+1]) is at position
+    p = kv_len_s - q_len_s + (t - cu[s]) (the step's tokens are the last q_len
+    positions); its rows k_new[t], v_new[t] (all KV heads) go to slot p mod B of
+    page page_table[s][p div B].  Works on numpy arrays or CPU torch tensors of
+    any dtype (bf16 included) and returns new arrays, the inputs untouched:
+    a pure copy, so every written value keeps its bits.
+    """
+    def copy(x):
+        return x.clone() if hasattr(x, "clone") else np.array(x, copy=True)
+
+    k_out, v_out = copy(k_pages), copy(v_pages)
+    cu, kv, table = as_i64(cu_q_lens), as_i64(kv_lens), as_i64(page_table)
+    page_size = k_pages.shape[1]
+    for s in range(len(kv)):
+        q_len = int(cu[s + 1] - cu[s])
+        for r in range(q_len):
+            t = int(cu[s]) + r
+            p = int(kv[s]) - q_len + r
+            page, slot = int(table[s, p // page_size]), p % page_size
+            k_out[page, slot] = k_new[t]
+            v_out[page, slot] = v_new[t]
+    return k_out, v_out
+
+
 def forward_inputs(inp, token_rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """Convenience wrapper over an ``rpa_workloads.Inputs`` bundle."""
     return forward_rows(inp.q, inp.k_pages, inp.v_pages, inp.page_table, inp.cu_q_lens,

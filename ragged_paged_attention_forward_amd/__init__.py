@@ -21,7 +21,7 @@ import torch
 
 from . import _lib
 from ._lib import (RPA_ERR_HIP, RPA_ERR_INVALID_ARG, RPA_ERR_OOM, RPA_ERR_UNSUPPORTED,
-                   RPA_KERNEL_DECODE, RPA_KERNEL_MERGE, RPA_KERNEL_PREFILL, RPA_OK,
+                   RPA_KERNEL_APPEND, RPA_KERNEL_DECODE, RPA_KERNEL_MERGE, RPA_KERNEL_PREFILL, RPA_OK,
                    RPA_OPT_DECODE_MAX_ROWS, RPA_OPT_DECODE_SPLIT_KEYS, RPA_OPT_DECODE_WAVES,
                    RPA_OPT_FUSED_MERGE, RPA_OPT_KERNEL_TIMING, RPA_OPT_PATH, RPA_OPT_XCD_GROUPS,
                    RPA_OPT_PREFILL_SPLIT_KEYS, RPA_OPT_CONCURRENT,
@@ -31,9 +31,10 @@ __all__ = ["RaggedPagedAttention", "rpa_forward", "RpaError", "library_path", "R
            "RPA_ERR_INVALID_ARG", "RPA_ERR_UNSUPPORTED", "RPA_ERR_OOM", "RPA_ERR_HIP",
            "RPA_OPT_DECODE_SPLIT_KEYS", "RPA_OPT_PATH", "RPA_OPT_DECODE_MAX_ROWS",
            "RPA_OPT_DECODE_WAVES", "RPA_OPT_KERNEL_TIMING", "RPA_OPT_XCD_GROUPS", "RPA_OPT_FUSED_MERGE", "RPA_OPT_PREFILL_SPLIT_KEYS", "RPA_OPT_CONCURRENT", "RPA_KERNEL_PREFILL", "RPA_KERNEL_DECODE",
-           "RPA_KERNEL_MERGE", "KERNEL_KINDS", "probe_read", "probe_mfma"]
+           "RPA_KERNEL_MERGE", "RPA_KERNEL_APPEND", "KERNEL_KINDS", "probe_read", "probe_mfma"]
 
-KERNEL_KINDS = {"prefill": RPA_KERNEL_PREFILL, "decode": RPA_KERNEL_DECODE, "merge": RPA_KERNEL_MERGE}
+KERNEL_KINDS = {"prefill": RPA_KERNEL_PREFILL, "decode": RPA_KERNEL_DECODE, "merge": RPA_KERNEL_MERGE,
+                "append": RPA_KERNEL_APPEND}
 
 
 def library_path() -> str:
@@ -141,13 +142,7 @@ class RaggedPagedAttention:
         return buf[:min(count.value, buf.shape[0])].copy()
 
     # -- forward --------------------------------------------------------------
-    def forward(self, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
-                page_table: torch.Tensor, cu_q_lens, kv_lens, window: int = 0,
-                scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-        """Enqueue one attention call on ``stream`` (default: torch's current stream)."""
-        if scale is None:
-            scale = float(self.head_dim) ** -0.5
+    def _checked(self, q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream):
         cu = _host_i32(cu_q_lens)
         kv = _host_i32(kv_lens)
         n = int(kv.shape[0])
@@ -175,16 +170,49 @@ class RaggedPagedAttention:
             stream = torch.cuda.current_stream(q.device)
         if stream is not self._stream_obj:
             self._stream_obj, self._stream_ptr = stream, ctypes.c_void_p(stream.cuda_stream)
-        args = (self._ctx, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), page_table.data_ptr(),
-                cu.ctypes.data, kv.ctypes.data, n, int(window), float(scale), out.data_ptr(),
-                self._stream_ptr)
-        if q.device.index == torch.cuda.current_device():
-            st = self._lib.rpa_forward(*args)
+        return cu, kv, n, out
+
+    def _call(self, fn, name, device, args):
+        if device.index == torch.cuda.current_device():
+            st = fn(*args)
         else:
-            with torch.cuda.device(q.device):
-                st = self._lib.rpa_forward(*args)
+            with torch.cuda.device(device):
+                st = fn(*args)
         if st != RPA_OK:
-            raise self._error(st, "rpa_forward")
+            raise self._error(st, name)
+
+    def forward(self, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                page_table: torch.Tensor, cu_q_lens, kv_lens, window: int = 0,
+                scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """Enqueue one attention call on ``stream`` (default: torch's current stream)."""
+        if scale is None:
+            scale = float(self.head_dim) ** -0.5
+        cu, kv, n, out = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream)
+        self._call(self._lib.rpa_forward, "rpa_forward", q.device,
+                   (self._ctx, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), page_table.data_ptr(),
+                    cu.ctypes.data, kv.ctypes.data, n, int(window), float(scale), out.data_ptr(),
+                    self._stream_ptr))
+        return out
+
+    def forward_append(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor, cu_q_lens,
+                       kv_lens, window: int = 0, scale: Optional[float] = None,
+                       out: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """Write the step's new K/V rows (``k_new`` / ``v_new``, [T, Hkv, D] bf16)
+        into their page slots, then the attention of ``forward``, in one call."""
+        if scale is None:
+            scale = float(self.head_dim) ** -0.5
+        cu, kv, n, out = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream)
+        shape = (q.shape[0], self.num_kv_heads, self.head_dim)
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor of shape {list(shape)}")
+        self._call(self._lib.rpa_forward_append, "rpa_forward_append", q.device,
+                   (self._ctx, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pages.data_ptr(),
+                    v_pages.data_ptr(), page_table.data_ptr(), cu.ctypes.data, kv.ctypes.data, n, int(window),
+                    float(scale), out.data_ptr(), self._stream_ptr))
         return out
 
     __call__ = forward

@@ -26,8 +26,9 @@ RPA_OPT_CONCURRENT = 10
 RPA_KERNEL_PREFILL = 0
 RPA_KERNEL_DECODE = 1
 RPA_KERNEL_MERGE = 2
+RPA_KERNEL_APPEND = 3
 
-EXPORTED = ("rpa_create", "rpa_forward", "rpa_destroy", "rpa_status_string", "rpa_last_error",
+EXPORTED = ("rpa_create", "rpa_forward", "rpa_forward_append", "rpa_destroy", "rpa_status_string", "rpa_last_error",
             "rpa_set_option", "rpa_plan", "rpa_kernel_times", "rpa_probe_read", "rpa_probe_mfma")
 
 
@@ -84,6 +85,9 @@ def load() -> ctypes.CDLL:
     lib.rpa_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
                                 ctypes.c_float, vp, vp]
     lib.rpa_forward.restype = ctypes.c_int
+    lib.rpa_forward_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_float, vp, vp]
+    lib.rpa_forward_append.restype = ctypes.c_int
     lib.rpa_destroy.argtypes = [vp]
     lib.rpa_destroy.restype = None
     lib.rpa_status_string.argtypes = [ctypes.c_int]

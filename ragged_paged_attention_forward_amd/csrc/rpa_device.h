@@ -1178,6 +1178,43 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 }
 
 // ---------------------------------------------------------------------------
+// KV append: the step's new keys and values into their pages, before the
+// attention kernels read them (the pages' kernel writes the new tokens' K/V
+// into the cache within the attention call: "TPU Deep Dive", chapter 8).
+// The new token at flattened index t of sequence s is at position
+// kv_len_s - q_len_s + (t - cu_q_lens[s]); its row of KV head g goes to slot
+// pos % page_size of page page_table[s][pos / page_size].  One workgroup per
+// work item; the items whose split index is 0 cover every (token, KV head)
+// pair of the step exactly once, and each copies its tokens' rows of its KV
+// head with 16-byte loads and stores, consecutive threads along a row.
+// ---------------------------------------------------------------------------
+constexpr int kAppendThreads = 256;
+
+template <int D>
+__global__ void __launch_bounds__(kAppendThreads)
+rpa_append_kernel(const rpa_work_item* __restrict__ items, const int32_t* __restrict__ page_table,
+                  const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                  uint16_t* __restrict__ k_dst, uint16_t* __restrict__ v_dst, KernelArgs args) {
+  const rpa_work_item it = items[blockIdx.x];
+  if (it.split_index != 0) return;
+  constexpr int CH = D / 8;   // 16-byte chunks per row
+  const int hkv = args.num_kv_heads;
+  const int ps = args.page_size;
+  const int32_t* pt_row = page_table + static_cast<int64_t>(it.seq) * args.max_pages;
+  const int n = it.q_count * CH;
+  for (int i = threadIdx.x; i < n; i += kAppendThreads) {
+    const int r = i / CH;
+    const int c = i - r * CH;
+    const int pos = it.q_pos0 + r;
+    const int64_t page = pt_row[pos / ps];
+    const int64_t src = (static_cast<int64_t>(it.q_start + r) * hkv + it.kv_head) * D + c * 8;
+    const int64_t dst = ((page * ps + pos % ps) * hkv + it.kv_head) * D + c * 8;
+    *reinterpret_cast<u32x4*>(k_dst + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
+    *reinterpret_cast<u32x4*>(v_dst + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI>
@@ -1224,6 +1261,15 @@ static hipError_t launch_decode_t(const KernelArgs& a, int n_items, int waves, h
 }
 
 template <int D>
+static hipError_t launch_append_t(const KernelArgs& a, int n_items, const void* k_new, const void* v_new,
+                                  void* k_dst, void* v_dst, hipStream_t stream) {
+  hipLaunchKernelGGL((rpa_append_kernel<D>), dim3(n_items), dim3(kAppendThreads), 0, stream, a.items, a.page_table,
+                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                     static_cast<uint16_t*>(k_dst), static_cast<uint16_t*>(v_dst), a);
+  return hipGetLastError();
+}
+
+template <int D>
 static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t stream) {
   hipLaunchKernelGGL((rpa_merge_kernel<D>), dim3(n_groups), dim3(MergeCfg<D>::THREADS), 0, stream, a);
   return hipGetLastError();
@@ -1247,6 +1293,10 @@ static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t 
   }                                                                                         \
   hipError_t launch_merge_d##D(const KernelArgs& a, int n, hipStream_t s) {                 \
     return launch_merge_t<D>(a, n, s);                                                      \
+  }                                                                                         \
+  hipError_t launch_append_d##D(const KernelArgs& a, int n, const void* kn, const void* vn, \
+                                void* kd, void* vd, hipStream_t s) {                        \
+    return launch_append_t<D>(a, n, kn, vn, kd, vd, s);                                     \
   }                                                                                         \
   int prefill_rows_d##D() { return PrefillCfg<RPA_PREFILL_SHAPE_##D>::ROWS; }
 

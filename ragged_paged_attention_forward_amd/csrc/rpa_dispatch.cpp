@@ -12,18 +12,26 @@ namespace rpa {
 hipError_t launch_prefill_d64(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, hipStream_t s);
 hipError_t launch_merge_d64(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
+                              hipStream_t s);
 int prefill_rows_d64();
 hipError_t launch_prefill_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, hipStream_t s);
 hipError_t launch_merge_d128(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
+                              hipStream_t s);
 int prefill_rows_d128();
 hipError_t launch_prefill_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, hipStream_t s);
 hipError_t launch_merge_d256(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
+                              hipStream_t s);
 int prefill_rows_d256();
 hipError_t launch_prefill_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, hipStream_t s);
 hipError_t launch_merge_d512(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_append_d512(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
+                              hipStream_t s);
 int prefill_rows_d512();
 
 int prefill_rows_for(int head_dim) {
@@ -85,6 +93,20 @@ hipError_t launch_decode(const LaunchArgs& l, const rpa_work_item* items, int n_
     case 128: return launch_decode_d128(a, n_items, w, s);
     case 256: return launch_decode_d256(a, n_items, w, s);
     case 512: return launch_decode_d512(a, n_items, w, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_append(const LaunchArgs& l, const rpa_work_item* items, int n_items, const void* k_new,
+                         const void* v_new, void* k_dst, void* v_dst) {
+  if (n_items <= 0) return hipSuccess;
+  const KernelArgs a = make_args(l, items);
+  hipStream_t s = static_cast<hipStream_t>(l.stream);
+  switch (l.head_dim) {
+    case 64: return launch_append_d64(a, n_items, k_new, v_new, k_dst, v_dst, s);
+    case 128: return launch_append_d128(a, n_items, k_new, v_new, k_dst, v_dst, s);
+    case 256: return launch_append_d256(a, n_items, k_new, v_new, k_dst, v_dst, s);
+    case 512: return launch_append_d512(a, n_items, k_new, v_new, k_dst, v_dst, s);
     default: return hipErrorInvalidValue;
   }
 }

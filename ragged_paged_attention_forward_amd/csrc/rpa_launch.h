@@ -38,5 +38,9 @@ bool head_dim_supported(int head_dim);
 hipError_t launch_prefill(const LaunchArgs& a, const rpa_work_item* items, int n_items);
 hipError_t launch_decode(const LaunchArgs& a, const rpa_work_item* items, int n_items);
 hipError_t launch_merge(const LaunchArgs& a, int n_groups);
+// Copies the step's new K/V rows (k_new / v_new, [T, Hkv, D]) into their page
+// slots of k_dst / v_dst, one workgroup per work item.
+hipError_t launch_append(const LaunchArgs& a, const rpa_work_item* items, int n_items, const void* k_new,
+                         const void* v_new, void* k_dst, void* v_dst);
 
 }  // namespace rpa

@@ -164,14 +164,14 @@ def test_kernel_times_validation_and_empty_read():
     count = ctypes.c_int32(-7)
     buf = (ctypes.c_float * 4)()
     assert lib.rpa_kernel_times(None, 0, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
-    assert lib.rpa_kernel_times(ctx, 3, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_kernel_times(ctx, 4, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_kernel_times(ctx, -1, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_kernel_times(ctx, 0, buf, -1, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_kernel_times(ctx, 0, None, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_kernel_times(ctx, 0, buf, 4, None) == _lib.RPA_ERR_INVALID_ARG
     # nothing recorded yet: count 0, no device call
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_KERNEL_TIMING, 4) == _lib.RPA_OK
-    for kind in (_lib.RPA_KERNEL_PREFILL, _lib.RPA_KERNEL_DECODE, _lib.RPA_KERNEL_MERGE):
+    for kind in (_lib.RPA_KERNEL_PREFILL, _lib.RPA_KERNEL_DECODE, _lib.RPA_KERNEL_MERGE, _lib.RPA_KERNEL_APPEND):
         assert lib.rpa_kernel_times(ctx, kind, buf, 4, ctypes.byref(count)) == _lib.RPA_OK
         assert count.value == 0
     assert lib.rpa_kernel_times(ctx, 1, None, 0, ctypes.byref(count)) == _lib.RPA_OK
@@ -198,3 +198,28 @@ def test_probes_reject_bad_arguments_before_launch():
     assert lib.rpa_probe_mfma(0, 1, addr, None) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_probe_mfma(1, 0, addr, None) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_probe_mfma(1, 1, None, None) == _lib.RPA_ERR_INVALID_ARG
+
+
+def test_forward_append_rejects_bad_pointers_before_launch():
+    lib, st, ctx = _ctx()
+    cu_a, cu_p = i32([0, 2])
+    kv_a, kv_p = i32([7])
+    other = ctypes.c_void_p(0x900000)
+    # q, k_new, v_new, k_pages, v_pages, page_table, out
+    for args in ((FAKE, None, FAKE, FAKE, other, FAKE, other), (FAKE, FAKE, None, FAKE, other, FAKE, other),
+                 (None, FAKE, FAKE, FAKE, other, FAKE, other), (FAKE, FAKE, FAKE, None, other, FAKE, other),
+                 (FAKE, FAKE, FAKE, FAKE, other, None, other), (FAKE, FAKE, FAKE, FAKE, other, FAKE, None)):
+        q, kn, vn, kp, vp, pt, out = args
+        st = lib.rpa_forward_append(ctx, q, kn, vn, kp, vp, pt, cu_p, kv_p, 1, 0, 1.0, out, None)
+        assert st == _lib.RPA_ERR_INVALID_ARG, args
+    # the same buffer for keys and values
+    st = lib.rpa_forward_append(ctx, FAKE, FAKE, FAKE, other, other, FAKE, cu_p, kv_p, 1, 0, 1.0,
+                                ctypes.c_void_p(0x7000000), None)
+    assert st == _lib.RPA_ERR_INVALID_ARG and "same buffer" in lib.rpa_last_error(ctx).decode()
+    # metadata checks as for rpa_forward
+    bad_kv_a, bad_kv_p = i32([1])   # q_len 2 > kv_len 1
+    st = lib.rpa_forward_append(ctx, FAKE, FAKE, FAKE, FAKE, other, FAKE, cu_p, bad_kv_p, 1, 0, 1.0, other, None)
+    assert st == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_forward_append(None, FAKE, FAKE, FAKE, FAKE, other, FAKE, cu_p, kv_p, 1, 0, 1.0, other,
+                                  None) == _lib.RPA_ERR_INVALID_ARG
+    lib.rpa_destroy(ctx)

@@ -23,6 +23,7 @@ import torch
 
 import oracle.rpa_oracle as ora
 import rpa_workloads as wl
+from append_common import new_token_slots, stale_pages_and_new_rows
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -450,3 +451,85 @@ def test_planted_gqa_mapping_is_caught(monkeypatch):
         return out[:, inv, :]
     monkeypatch.setattr(ora, "forward_rows", swapped)
     assert not _pins_pass()
+
+
+# ---------------------------------------------------------------------------
+# KV append (the step's new keys and values into their pages)
+# ---------------------------------------------------------------------------
+
+def test_append_golden_hand_worked():
+    g = json.load(open(os.path.join(GOLDEN, "append_hand_worked.json")))
+    shape = (g["num_pages"], g["page_size"], g["num_kv_heads"], g["head_dim"])
+    zeros = np.zeros(shape)
+    k_out, v_out = ora.append_kv(zeros, zeros, np.array(g["page_table"]), np.array(g["cu_q_lens"]),
+                                 np.array(g["kv_lens"]), np.array(g["k_new"], dtype=float),
+                                 np.array(g["v_new"], dtype=float))
+    want_k, want_v = np.zeros(shape), np.zeros(shape)
+    for w in g["expected_written"]:
+        want_k[w["page"], w["slot"], 0] = w["k"]
+        want_v[w["page"], w["slot"], 0] = w["v"]
+    np.testing.assert_array_equal(k_out, want_k)
+    np.testing.assert_array_equal(v_out, want_v)
+    assert not zeros.any()   # inputs untouched
+
+
+APPEND_CASES = [
+    wl.custom([(5, 40), (0, 7), (33, 33), (1, 90)], 8, 2, 32, 16, 17, seed=12),
+    wl.custom([(3, 11), (1, 1), (4, 9)], 4, 4, 8, 3, 0, seed=13),
+    wl.custom([(1, 300 + i) for i in range(7)] + [(64, 64)], 8, 1, 16, 128, 0, seed=14),
+    wl.custom([(2, 5), (7, 7)], 2, 1, 4, 1, 2, seed=15),
+]
+
+
+@pytest.mark.parametrize("w", APPEND_CASES, ids=lambda w: f"{w.num_seqs}seqs_B{w.page_size}")
+def test_append_restores_the_generated_pages(w):
+    """Take the new rows out of generated pages (slots set to NaN), append them
+    again: every byte of both pools is back as generated."""
+    inp = wl.make_inputs(w, poison=True)
+    k_new, k_stale, v_new, v_stale = stale_pages_and_new_rows(inp)
+    k_out, v_out = ora.append_kv(k_stale, v_stale, inp.page_table, inp.cu_q_lens, inp.kv_lens, k_new, v_new)
+    assert torch.equal(k_out.view(torch.int16), inp.k_pages.view(torch.int16))
+    assert torch.equal(v_out.view(torch.int16), inp.v_pages.view(torch.int16))
+    assert k_stale.float().isnan().sum() >= len(new_token_slots(inp))   # inputs untouched
+
+
+@pytest.mark.parametrize("w", APPEND_CASES, ids=lambda w: f"{w.num_seqs}seqs_B{w.page_size}")
+def test_append_puts_new_tokens_at_the_last_positions(w):
+    """After the append, the un-paged keys and values of every sequence end
+    with its new tokens' rows, in order, and attention over the appended pool
+    equals attention over the generated one."""
+    inp = wl.make_inputs(w)
+    k_new, k_stale, v_new, v_stale = stale_pages_and_new_rows(inp, fill=0.0)
+    k_out, v_out = ora.append_kv(k_stale, v_stale, inp.page_table, inp.cu_q_lens, inp.kv_lens, k_new, v_new)
+    cu, kv, table = inp.cu_q_lens.numpy(), inp.kv_lens.numpy(), inp.page_table.numpy()
+    b = inp.k_pages.shape[1]
+    for s in range(len(kv)):
+        q_len = int(cu[s + 1] - cu[s])
+        if q_len == 0:
+            continue
+        got_k = ora.unpage(ora.as_f64(k_out), table[s], int(kv[s]), b)[-q_len:]
+        got_v = ora.unpage(ora.as_f64(v_out), table[s], int(kv[s]), b)[-q_len:]
+        np.testing.assert_array_equal(got_k, ora.as_f64(k_new[cu[s]:cu[s + 1]]))
+        np.testing.assert_array_equal(got_v, ora.as_f64(v_new[cu[s]:cu[s + 1]]))
+    ref = ora.forward_inputs(inp)
+    got = ora.forward(inp.q, k_out, v_out, inp.page_table, inp.cu_q_lens, inp.kv_lens, inp.window, inp.scale)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_planted_append_position_mistake_is_caught(monkeypatch):
+    """An append that places token t at position kv_len - q_len + r - 1 (one
+    slot early) fails the hand-worked case."""
+    def early(k_pages, v_pages, page_table, cu_q_lens, kv_lens, k_new, v_new):
+        k_out, v_out = np.array(k_pages, copy=True), np.array(v_pages, copy=True)
+        cu, kv, table = ora.as_i64(cu_q_lens), ora.as_i64(kv_lens), ora.as_i64(page_table)
+        b = k_pages.shape[1]
+        for s in range(len(kv)):
+            q_len = int(cu[s + 1] - cu[s])
+            for r in range(q_len):
+                p = int(kv[s]) - q_len + r - 1
+                k_out[int(table[s, p // b]), p % b] = k_new[int(cu[s]) + r]
+                v_out[int(table[s, p // b]), p % b] = v_new[int(cu[s]) + r]
+        return k_out, v_out
+    monkeypatch.setattr(ora, "append_kv", early)
+    with pytest.raises(AssertionError):
+        test_append_golden_hand_worked()
