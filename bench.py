@@ -16,6 +16,10 @@ behind ``roofline.achieved``; the wall clock over the K timed steps gives
 ``value`` and ``ms_per_step``.  The oracle's CPU time on a bounded sample of
 the same workload is reported as ``cpu_baseline``.
 
+``--append`` makes every step call ``rpa_forward_append`` instead: the step's
+new K/V rows are written into their pages (the same bytes each step) before the
+attention kernels, and the append kernel is timed beside them.
+
 Prints ONE JSON line.
 
 Counter runs (HBM traffic of the dominant kernel):
@@ -49,7 +53,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 LLC_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "ragged_paged_attention_forward_amd", "csrc")
 COPY_BYTES = 1 << 30            # calibration buffer (read once, written once)
-KERNEL_NAMES = {"prefill": "rpa_prefill_kernel", "decode": "rpa_decode_kernel", "merge": "rpa_merge_kernel"}
+KERNEL_NAMES = {"prefill": "rpa_prefill_kernel", "decode": "rpa_decode_kernel", "merge": "rpa_merge_kernel",
+                "append": "rpa_append_kernel"}
 WORKLOADS = ("decode", "tiny", "swa_prefill", "global_prefill", "mixed", "mixed_swa")
 
 
@@ -104,7 +109,22 @@ def kernel_work(w, items, merge_kernel=True):
     seqs = [w.seqs[s] for s in sorted(split)]
     out["merge"] = {"flops": 0, "bytes": int(metrics.qo_bytes(seqs, w.num_q_heads, w.head_dim) // 2),
                     "seqs": len(seqs)}
+    # the KV append reads the step's new K and V rows and writes them into their pages
+    new_rows = w.total_q * w.num_kv_heads * w.head_dim * 2 * 2
+    out["append"] = {"flops": 0, "bytes": int(2 * new_rows), "seqs": w.num_seqs}
     return out
+
+
+def new_row_slots(w, cu, kv, page_table) -> np.ndarray:
+    """Flat page-slot index (page * page_size + slot) of each of the step's new
+    tokens, in token order: token r of sequence s is at position
+    kv_len - q_len + r (bench input construction for the append mode)."""
+    b = w.page_size
+    out = []
+    for s in range(w.num_seqs):
+        pos = np.arange(int(kv[s]) - int(cu[s + 1] - cu[s]), int(kv[s]))
+        out.append(page_table[s][pos // b].astype(np.int64) * b + pos % b)
+    return np.concatenate(out) if out else np.zeros(0, dtype=np.int64)
 
 
 def cpu_baseline(w, budget_s: float):
@@ -268,8 +288,22 @@ def run(args):
     planner_us = min(plan_s) * 1e6
     stream = torch.cuda.current_stream(dev)
 
+    if args.append:
+        # each step also writes its new K/V rows (already in the pages, so every
+        # step writes the same bytes) through rpa_forward_append
+        slots = torch.from_numpy(new_row_slots(w, cu, kv, host.page_table.numpy())).to(dev)
+        news = []
+        for d, _ in replicas:
+            flat = (w.num_kv_heads, w.head_dim)
+            news.append((d.k_pages.view(-1, *flat)[slots].contiguous(), d.v_pages.view(-1, *flat)[slots].contiguous()))
+
     def step(i):
         d, out = replicas[i % reps]
+        if args.append:
+            kn, vn = news[i % reps]
+            attn.forward_append(d.q, kn, vn, d.k_pages, d.v_pages, d.page_table, cu, kv, w.window, w.scale,
+                                out=out, stream=stream)
+            return
         attn.forward(d.q, d.k_pages, d.v_pages, d.page_table, cu, kv, w.window, w.scale, out=out,
                      stream=stream)
 
@@ -362,7 +396,7 @@ def run(args):
         "config": {"workload": args.workload, "description": w.description, "seed": w.seed,
                    "num_seqs": w.num_seqs, "q_tokens": t_q, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                   "page_size": w.page_size, "window": w.window, "replicas": reps,
+                   "page_size": w.page_size, "window": w.window, "replicas": reps, "append_kv": bool(args.append),
                    "parallelism": "single GPU"},
         "step_tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -453,6 +487,8 @@ def main(argv=None):
     ap.add_argument("--timing-steps", type=int, default=200,
                     help="steps of the event-timed pass (at most --steps)")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = >= 1 GiB total)")
+    ap.add_argument("--append", action="store_true",
+                    help="each step also writes its new K/V rows into the pages (rpa_forward_append)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the elementwise calibration kernel (for counter runs)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),

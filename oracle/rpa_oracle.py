@@ -39,7 +39,8 @@ most ``ROW_BLOCK`` only to bound memory, which is exact because rows of a
 softmax are independent.
 
 Every function below is pinned by ``tests/test_oracle.py`` (brute force, a
-library routine, closed forms and invariants); none is "parity unpinned".
+library routine, closed forms, invariants, and for ``append_kv`` a hand-worked
+case and a round trip through generated pages); none is "parity unpinned".
 """
 from __future__ import annotations
 
