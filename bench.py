@@ -251,6 +251,45 @@ def measured_peak(torch, R, dev, bound: str, nbytes: int):
                      "v_mfma_f32_32x32x16_bf16, median of 5 launches"}
 
 
+def graph_layers(torch, attn, replicas, w, cu, kv, layers: int, stream):
+    """The attention calls of `layers` layers of one step (same metadata, one
+    input replica per layer) launched eagerly and replayed as one captured HIP
+    graph: wall time per layer of each."""
+    n = min(layers, len(replicas))
+    outs = [torch.empty_like(replicas[i][0].q) for i in range(n)]
+
+    def calls():
+        for i in range(n):
+            d = replicas[i][0]
+            attn.forward(d.q, d.k_pages, d.v_pages, d.page_table, cu, kv, w.window, w.scale, out=outs[i])
+
+    calls()                      # the work list is on the device before the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    reps = max(20, 2000 // n)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps / n * 1e3
+
+    def eager():
+        with torch.cuda.stream(stream):
+            calls()
+    eager_ms = timed(eager)
+    graph_ms = timed(g.replay)
+    return {"layers": n, "eager_ms_per_layer": round(eager_ms, 6), "graph_ms_per_layer": round(graph_ms, 6),
+            "replays": reps}
+
+
 def run(args):
     import torch
     import rpa_workloads as wl
@@ -408,6 +447,8 @@ def run(args):
         "plan": info,
         "roofline": roofline,
     }
+    if args.graph_layers > 0:
+        res["graph"] = graph_layers(torch, attn, replicas, w, cu, kv, args.graph_layers, stream)
     if args.copy_calibration:
         copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
@@ -487,6 +528,8 @@ def main(argv=None):
     ap.add_argument("--timing-steps", type=int, default=200,
                     help="steps of the event-timed pass (at most --steps)")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = >= 1 GiB total)")
+    ap.add_argument("--graph-layers", type=int, default=0,
+                    help="also time L layers' calls eagerly and as one captured HIP graph")
     ap.add_argument("--append", action="store_true",
                     help="each step also writes its new K/V rows into the pages (rpa_forward_append)")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -98,6 +98,14 @@ int rpa_create(const rpa_config* cfg, rpa_ctx** out_ctx);
  * that returns an error has enqueued nothing.  Page-table *values* are device
  * data and are not checked.  Returns RPA_OK, RPA_ERR_INVALID_ARG, RPA_ERR_OOM
  * or RPA_ERR_HIP; rpa_last_error() then holds a message.
+ *
+ * Stream capture: a call may be captured into a HIP graph (for example the
+ * attention of every layer of a step, replayed as one graph) when the context
+ * has already run a call with the same cu_q_lens, kv_lens and window, so that
+ * its work list is on the device; the captured call enqueues only kernels
+ * (and, for a mixed step, the fork and join of its second stream) and records
+ * no kernel timing.  A capture that would need a new work list returns
+ * RPA_ERR_INVALID_ARG.  Replays read the device buffers given at capture time.
  */
 int rpa_forward(rpa_ctx* ctx, const void* q, const void* k_pages, const void* v_pages,
                 const int32_t* page_table, const int32_t* cu_q_lens, const int32_t* kv_lens,
