@@ -1275,6 +1275,17 @@ static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t 
   return hipGetLastError();
 }
 
+// Prefill workgroups one compute unit holds at once: by LDS (160 KB per
+// compute unit) and by waves (two per SIMD, the register budget the prefill
+// kernels are built for).
+template <typename C>
+constexpr int prefill_wgs_per_cu() {
+  const int by_lds = (160 * 1024) / C::LDS_BYTES;
+  const int by_waves = 8 * 64 / C::NT;
+  const int n = by_lds < by_waves ? by_lds : by_waves;
+  return n > 0 ? n : 1;
+}
+
 // Prefill tile shapes per head size:
 // (D, BN keys per tile, NW waves, NB 32-row blocks per wave, NS pipeline
 // stages, DS waves sharing a row block by splitting d).
@@ -1298,6 +1309,7 @@ static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t 
                                 void* kd, void* vd, hipStream_t s) {                        \
     return launch_append_t<D>(a, n, kn, vn, kd, vd, s);                                     \
   }                                                                                         \
-  int prefill_rows_d##D() { return PrefillCfg<RPA_PREFILL_SHAPE_##D>::ROWS; }
+  int prefill_rows_d##D() { return PrefillCfg<RPA_PREFILL_SHAPE_##D>::ROWS; }              \
+  int prefill_wgs_per_cu_d##D() { return prefill_wgs_per_cu<PrefillCfg<RPA_PREFILL_SHAPE_##D>>(); }
 
 }  // namespace rpa

@@ -15,24 +15,28 @@ hipError_t launch_merge_d64(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
 int prefill_rows_d64();
+int prefill_wgs_per_cu_d64();
 hipError_t launch_prefill_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, hipStream_t s);
 hipError_t launch_merge_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
 int prefill_rows_d128();
+int prefill_wgs_per_cu_d128();
 hipError_t launch_prefill_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, hipStream_t s);
 hipError_t launch_merge_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
 int prefill_rows_d256();
+int prefill_wgs_per_cu_d256();
 hipError_t launch_prefill_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, hipStream_t s);
 hipError_t launch_merge_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d512(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
 int prefill_rows_d512();
+int prefill_wgs_per_cu_d512();
 
 int prefill_rows_for(int head_dim) {
   switch (head_dim) {
@@ -45,6 +49,16 @@ int prefill_rows_for(int head_dim) {
 }
 
 bool head_dim_supported(int head_dim) { return prefill_rows_for(head_dim) > 0; }
+
+int prefill_wgs_per_cu_for(int head_dim) {
+  switch (head_dim) {
+    case 64: return prefill_wgs_per_cu_d64();
+    case 128: return prefill_wgs_per_cu_d128();
+    case 256: return prefill_wgs_per_cu_d256();
+    case 512: return prefill_wgs_per_cu_d512();
+    default: return 1;
+  }
+}
 
 static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
   KernelArgs a;

@@ -33,6 +33,8 @@ struct LaunchArgs {
 
 // Rows (tokens x grouped heads) per prefill workgroup for a head size, 0 if none.
 int prefill_rows_for(int head_dim);
+// Prefill workgroups one compute unit holds at once for a head size.
+int prefill_wgs_per_cu_for(int head_dim);
 bool head_dim_supported(int head_dim);
 
 hipError_t launch_prefill(const LaunchArgs& a, const rpa_work_item* items, int n_items);

@@ -20,6 +20,7 @@ struct PlanParams {
   int max_pages_per_seq = 0;
   int64_t max_q_tokens = 0;
   int prefill_rows = 128;      // query rows (tokens x grouped heads) per prefill tile
+  int prefill_wgs_per_cu = 1;  // prefill workgroups one compute unit holds at once
   int decode_max_rows = 16;    // most rows of one decode item
   int decode_wave_keys = 32;   // keys one decode wave takes per step
   int decode_waves = 4;        // waves of one decode workgroup

@@ -150,6 +150,24 @@ def test_long_prefill_items_are_split_when_they_would_dominate():
         assert all(it["split_group"] == -1 for it in items if it["kind"] == 0)
 
 
+def test_few_row_prefill_items_split_finer():
+    """Single tokens of 32 grouped heads (too many rows for a decode item) go to
+    the prefill kernel with a quarter of its tile's rows.  Their key ranges are
+    cut into pieces of the average per workgroup slot (two d = 128 prefill
+    workgroups per compute unit), rounded up to 128 keys, at least 128; items
+    with full tiles keep the 512-key floor (the mixed step above)."""
+    rng = np.random.default_rng(7)
+    w = wl.custom([(1, int(k)) for k in rng.integers(64, 2049, 128)], 32, 1, 128, 128, 0, seed=312)
+    cu, kv, info, items = plan_for(w)
+    check_plan(w, cu, kv, info, items)
+    assert info["num_decode_items"] == 0
+    piece = info["prefill_split_keys"]
+    per_slot = sum(k for _, k in w.seqs) / (256 * 2)
+    assert piece % 128 == 0 and 128 <= piece < 512
+    assert per_slot <= piece < per_slot + 128
+    assert max(prefill_keys(items)) <= 1.5 * piece + 64
+
+
 @pytest.mark.parametrize("piece", [512, 700, 2000])
 def test_fixed_prefill_split_keeps_coverage(piece):
     w = wl.custom([(1000, 3000), (3, 40), (700, 700), (1, 900)], 8, 2, 128, 16, 0, 5)
