@@ -38,6 +38,9 @@ CASES = {
     "mixed_small_w0": lambda: mixed_small(0),
     "mixed_small_w1024_pages16": lambda: mixed_small(1024, page_size=16),
     "gqa4_d128_chunks": lambda: wl.custom([(40, 100), (1, 17), (129, 129), (3, 1000)], 16, 4, 128, 32, 0, seed=42),
+    "with_empty_sequences": lambda: wl.custom([(0, 50), (3, 70), (0, 1), (1, 300), (0, 0), (17, 17)], 8, 2, 256, 64,
+                                              0, seed=43),
+    "mha_d64_window": lambda: wl.custom([(9, 200), (1, 65), (64, 64)], 4, 4, 64, 16, 33, seed=44),
 }
 
 
@@ -89,3 +92,47 @@ def test_append_kernel_is_timed():
     t = attn.kernel_times(R.RPA_KERNEL_APPEND)
     assert len(t) == 1 and t[0] > 0
     assert len(attn.kernel_times(R.RPA_KERNEL_DECODE)) == 1
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_append_through_one_kernel_kind(path):
+    """Every sequence through the prefill kernel (path 1: the append kernel
+    writes all rows), or decodes wherever their rows fit (path 2)."""
+    w = mixed_small(0)
+    attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_PATH, path)
+    inp, (k_new, k_stale, v_new, v_stale), kp, vp, out = run_append(w, attn)
+    want_k, want_v = ora.append_kv(k_stale, v_stale, inp.page_table, inp.cu_q_lens, inp.kv_lens, k_new, v_new)
+    assert torch.equal(kp.cpu().view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(vp.cpu().view(torch.int16), want_v.view(torch.int16))
+    compare(out, oracle_rows(inp), label=f"path {path}")
+
+
+def test_append_in_a_captured_graph():
+    """rpa_forward_append captured into a HIP graph (warm work list) and
+    replayed: each replay writes the same rows and gives the eager bits."""
+    w = mixed_small(1024)
+    inp = wl.make_inputs(w, poison=True)
+    k_new, k_stale, v_new, v_stale = stale_pages_and_new_rows(inp)
+    d = inp.to("cuda")
+    kn, vn = k_new.cuda(), v_new.cuda()
+    kp, vp = k_stale.cuda(), v_stale.cuda()
+    attn = make_attn(w)
+    eager = attn.forward_append(d.q, kn, vn, kp, vp, d.page_table, inp.cu_q_lens, inp.kv_lens, w.window,
+                                w.scale).clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        attn.forward_append(d.q, kn, vn, kp, vp, d.page_table, inp.cu_q_lens, inp.kv_lens, w.window, w.scale,
+                            out=out)
+    for _ in range(3):
+        kp.copy_(k_stale.cuda())
+        vp.copy_(v_stale.cuda())
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        assert torch.equal(kp.cpu().view(torch.int16), inp.k_pages.view(torch.int16))
+        assert torch.equal(vp.cpu().view(torch.int16), inp.v_pages.view(torch.int16))
