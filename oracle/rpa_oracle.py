@@ -38,6 +38,15 @@ Nothing here is blocked, fused or reordered: rows are processed in groups of at
 most ``ROW_BLOCK`` only to bound memory, which is exact because rows of a
 softmax are independent.
 
+An fp8 KV cache ("TPU Deep Dive", chapter 7, quantization levers: KV held in
+fp8 halves the dominant long-context read; "Pallas Kernel: vLLM on TPU ...",
+S5: a working cache quantization doubles the cache's token capacity) is read
+here as the pages leave it open: every stored K or V element is one byte in
+the OCP FP8 E4M3 format, and each KV head has one float32 scale for K and one
+for V; the value an element stands for is its E4M3 value times its head's
+scale.  ``forward_fp8_rows`` dequantizes exactly that way and then computes
+the same attention as ``forward_rows``.
+
 Every function below is pinned by ``tests/test_oracle.py`` (brute force, a
 library routine, closed forms, invariants, and for ``append_kv`` a hand-worked
 case and a round trip through generated pages); none is "parity unpinned".
@@ -202,6 +211,38 @@ def append_kv(k_pages, v_pages, page_table, cu_q_lens, kv_lens, k_new, v_new):
             k_out[page, slot] = k_new[t]
             v_out[page, slot] = v_new[t]
     return k_out, v_out
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """float64 value of each OCP FP8 E4M3 byte: 1 sign bit, 4 exponent bits
+    (bias 7), 3 mantissa bits.  Exponent field e > 0: (1 + m/8) * 2^(e - 7);
+    e = 0: subnormal, (m/8) * 2^-6.  The all-ones magnitude 0x7f (either sign)
+    is NaN and there is no infinity, so the largest finite value is
+    0x7e = 1.75 * 2^8 = 448."""
+    c = np.asarray(codes).astype(np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def dequantize_kv(pages, scales) -> np.ndarray:
+    """float64 values of an fp8 page pool: ``pages`` holds E4M3 bytes
+    [P, B, Hkv, D] (uint8 array or tensor), ``scales`` one float per KV head;
+    element (.., g, :) stands for e4m3_value(byte) * scales[g]."""
+    codes = pages.detach().cpu().numpy() if hasattr(pages, "detach") else np.asarray(pages)
+    sc = as_f64(scales).reshape(1, 1, -1, 1)
+    return e4m3_value(codes) * sc
+
+
+def forward_fp8_rows(q, k_pages, v_pages, k_scales, v_scales, page_table, cu_q_lens, kv_lens,
+                     window: int, scale: float, token_rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Attention over an fp8 KV cache: the pools are dequantized (``dequantize_kv``)
+    and the result is ``forward_rows`` of those values."""
+    return forward_rows(q, dequantize_kv(k_pages, k_scales), dequantize_kv(v_pages, v_scales), page_table,
+                        cu_q_lens, kv_lens, window, scale, token_rows)
 
 
 def forward_inputs(inp, token_rows: Optional[Sequence[int]] = None) -> np.ndarray:

@@ -221,6 +221,65 @@ def make_inputs(w: Workload, seed: Optional[int] = None, poison: bool = False,
                   torch.from_numpy(kv), trap, w.window, w.scale, poison)
 
 
+@dataclass
+class Fp8Inputs:
+    """An fp8 KV cache drawn from a bf16 call's tensors: the pools hold OCP FP8
+    E4M3 bytes [P, B, Hkv, D] (uint8) and each KV head has one float32 scale
+    for K and one for V.  ``base`` keeps the bf16 tensors (q, page table,
+    lengths) the call shares."""
+
+    base: Inputs
+    k_pages: torch.Tensor   # [P, B, Hkv, D] uint8
+    v_pages: torch.Tensor   # [P, B, Hkv, D] uint8
+    k_scales: torch.Tensor  # [Hkv] float32
+    v_scales: torch.Tensor  # [Hkv] float32
+
+    def to(self, device) -> "Fp8Inputs":
+        return Fp8Inputs(self.base.to(device), self.k_pages.to(device), self.v_pages.to(device),
+                         self.k_scales.to(device), self.v_scales.to(device))
+
+
+NAN_E4M3 = 0x7F   # the E4M3 NaN byte
+
+
+def _to_e4m3(pool: torch.Tensor, rng: np.random.Generator) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Bytes and per-KV-head scales of a [P, B, Hkv, D] pool: head g gets the
+    scale max|x_g| / 448 times a factor drawn from [1, 4) (so heads differ and
+    no value saturates); bytes are torch's round-to-nearest E4M3 of x / scale."""
+    x = pool.to(torch.float32)
+    amax = x.abs().amax(dim=(0, 1, 3)).clamp_min(1e-3)
+    factor = torch.from_numpy(rng.uniform(1.0, 4.0, size=x.shape[2]).astype(np.float32))
+    scales = (amax / 448.0 * factor).to(torch.float32)
+    codes = (x / scales.view(1, 1, -1, 1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scales
+
+
+def make_fp8_inputs(w: Workload, seed: Optional[int] = None, poison: bool = False,
+                    shuffle: bool = True) -> Fp8Inputs:
+    """The tensors of ``make_inputs`` with the K and V pools held in fp8.
+
+    ``poison`` fills every page slot past a sequence's kv_len and the whole trap
+    page with the E4M3 NaN byte."""
+    base = make_inputs(w, seed, poison=False, shuffle=shuffle)
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 104729)
+    k8, ks = _to_e4m3(base.k_pages, rng)
+    v8, vs = _to_e4m3(base.v_pages, rng)
+    if poison:
+        k8[base.trap_page] = NAN_E4M3
+        v8[base.trap_page] = NAN_E4M3
+        need = w.pages_needed()
+        for s, (_, kl) in enumerate(w.seqs):
+            n = need[s]
+            if n == 0:
+                continue
+            tail = kl - (n - 1) * w.page_size
+            last = int(base.page_table[s, n - 1])
+            k8[last, tail:] = NAN_E4M3
+            v8[last, tail:] = NAN_E4M3
+        base.poisoned = True
+    return Fp8Inputs(base, k8, v8, ks, vs)
+
+
 def custom(seqs: Sequence[Tuple[int, int]], num_q_heads: int, num_kv_heads: int,
            head_dim: int, page_size: int, window: int = 0, seed: int = 0,
            extra_pages_per_seq: int = 0, name: str = "custom") -> Workload:

@@ -533,3 +533,113 @@ def test_planted_append_position_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(ora, "append_kv", early)
     with pytest.raises(AssertionError):
         test_append_golden_hand_worked()
+
+
+# ---------------------------------------------------------------------------
+# fp8 (OCP E4M3) KV cache with per-KV-head scales
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3(codes) -> np.ndarray:
+    """torch's own E4M3 decoding (the library routine), as float64."""
+    t = codes if isinstance(codes, torch.Tensor) else torch.from_numpy(np.asarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _fp8_pins_pass() -> bool:
+    try:
+        test_e4m3_matches_torch_for_every_byte()
+        test_e4m3_closed_forms()
+        test_e4m3_is_monotone_and_symmetric()
+        test_fp8_head_scales_fold_into_score_scale_and_output()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_e4m3_matches_torch_for_every_byte():
+    codes = np.arange(256, dtype=np.uint8)
+    np.testing.assert_array_equal(ora.e4m3_value(codes), _torch_e4m3(codes))
+
+
+def test_e4m3_closed_forms():
+    """Values fixed by the format: bias 7, subnormals m/8 * 2^-6, NaN at 0x7f
+    and 0xff, largest finite 448."""
+    v = ora.e4m3_value(np.arange(256, dtype=np.uint8))
+    expect = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+              0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+    for code, val in expect.items():
+        assert v[code] == val, hex(code)
+    assert math.copysign(1.0, v[0x80]) < 0 and v[0x80] == 0.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.isfinite(v[np.r_[0:0x7F, 0x80:0xFF]]).all()
+
+
+def test_e4m3_is_monotone_and_symmetric():
+    v = ora.e4m3_value(np.arange(256, dtype=np.uint8))
+    assert np.all(np.diff(v[:0x7F]) > 0)
+    np.testing.assert_array_equal(v[0x80:0xFF], -v[:0x7F])
+
+
+def _fp8_case(seqs, hq, hkv, d, b, window, seed):
+    w = wl.custom(seqs, hq, hkv, d, b, window=window, seed=seed)
+    return wl.make_fp8_inputs(w, poison=True)
+
+
+def test_fp8_head_scales_fold_into_score_scale_and_output():
+    """A K scale c_g multiplies every score of KV head g, so it equals the
+    bf16-style forward with scale * c_g; a V scale multiplies that head
+    group's output.  The reference side decodes the bytes with torch."""
+    f = _fp8_case([(5, 9), (1, 40), (12, 12)], 4, 2, 32, 8, 0, 11)
+    b = f.base
+    k_val, v_val = _torch_e4m3(f.k_pages), _torch_e4m3(f.v_pages)
+    got = ora.forward_fp8_rows(b.q, f.k_pages, f.v_pages, f.k_scales, f.v_scales, b.page_table, b.cu_q_lens,
+                               b.kv_lens, b.window, b.scale)
+    group = 2
+    for g in range(2):
+        ks, vs = float(f.k_scales[g]), float(f.v_scales[g])
+        assert ks != vs
+        ref = brute_force(b.q, torch.from_numpy(k_val), torch.from_numpy(v_val), b.page_table, b.cu_q_lens,
+                          b.kv_lens, b.window, b.scale * ks)
+        heads = slice(g * group, (g + 1) * group)
+        np.testing.assert_allclose(got[:, heads], vs * np.asarray(ref)[:, heads], rtol=1e-11, atol=1e-13)
+
+
+def test_fp8_nan_bytes_past_kv_len_never_contribute():
+    f = _fp8_case([(3, 21), (1, 17), (7, 30)], 2, 1, 16, 8, 6, 12)
+    b = f.base
+    assert (f.k_pages == wl.NAN_E4M3).any()
+    got = ora.forward_fp8_rows(b.q, f.k_pages, f.v_pages, f.k_scales, f.v_scales, b.page_table, b.cu_q_lens,
+                               b.kv_lens, b.window, b.scale)
+    assert np.isfinite(got).all()
+
+
+def test_fp8_pins_pass_on_the_real_oracle():
+    assert _fp8_pins_pass()
+
+
+def _mut_e4m3_no_subnormals(codes):
+    c = np.asarray(codes).astype(np.int64)
+    e, m = (c >> 3) & 0xF, (c & 7) / 8.0
+    mag = (1.0 + m) * np.exp2(e - 7.0)            # treats exponent 0 as normal
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+
+@pytest.mark.parametrize("name", ["no subnormals", "scale of query head", "k and v scales swapped"])
+def test_planted_fp8_mistake_is_caught(monkeypatch, name):
+    real_dq = ora.dequantize_kv
+    if name == "no subnormals":
+        monkeypatch.setattr(ora, "e4m3_value", _mut_e4m3_no_subnormals)
+    elif name == "scale of query head":
+        def dq(pages, scales):   # scale index taken from a wrong (query-head-like) position
+            sc = np.asarray(ora.as_f64(scales))[::-1].copy()
+            return real_dq(pages, sc)
+        monkeypatch.setattr(ora, "dequantize_kv", dq)
+    else:
+        real_fwd = ora.forward_fp8_rows
+
+        def swapped(q, kp, vp, ks, vs, *a, **k):
+            return real_fwd(q, kp, vp, vs, ks, *a, **k)
+        monkeypatch.setattr(ora, "forward_fp8_rows", swapped)
+    assert not _fp8_pins_pass(), f"planted mistake not caught: {name}"
