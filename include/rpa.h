@@ -139,6 +139,35 @@ int rpa_forward_append(rpa_ctx* ctx, const void* q, const void* k_new, const voi
                        const int32_t* kv_lens, int32_t num_seqs, int32_t window, float scale, void* out,
                        void* stream);
 
+/*
+ * rpa_forward_fp8 -- rpa_forward over a KV cache held in fp8.  Holding KV in
+ * fp8 halves the cache read that dominates decode and long contexts ("TPU
+ * Deep Dive", chapter 7, quantization levers) and doubles the tokens a cache
+ * holds ("Pallas Kernel: vLLM on TPU ...", S5).  The pages fix neither the
+ * fp8 format nor the scale layout; here every element is one byte in the OCP
+ * FP8 E4M3 format (sign, 4 exponent bits of bias 7, 3 mantissa bits,
+ * subnormals, NaN at 0x7f / 0xff, no infinity; largest value 448), and K and
+ * V each have one float32 scale per KV head: element (page, slot, g, i)
+ * stands for e4m3(byte) * scale[g].
+ *
+ *   k_pages, v_pages  device, uint8 [P, page_size, Hkv, D] row-major (16-byte
+ *                 aligned), E4M3 bytes; bytes past a sequence's kv_len and
+ *                 pages it does not reach are never read into the result
+ *   k_scales, v_scales  device, float32 [Hkv], finite (read by the kernels;
+ *                 the caller keeps them valid until the work is done)
+ *   all other arguments as for rpa_forward (q and out stay bf16)
+ *
+ * Every query token is computed by the split-KV decode kernel (sequences
+ * longer than 16 / G tokens in chunks of that many tokens), which converts
+ * the bytes to bf16 exactly in registers before its bf16 matrix products.
+ * Errors as for rpa_forward, plus RPA_ERR_INVALID_ARG for a NULL scale
+ * array and RPA_ERR_UNSUPPORTED when G = Hq / Hkv exceeds 16.
+ */
+int rpa_forward_fp8(rpa_ctx* ctx, const void* q, const void* k_pages, const void* v_pages, const float* k_scales,
+                    const float* v_scales, const int32_t* page_table, const int32_t* cu_q_lens,
+                    const int32_t* kv_lens, int32_t num_seqs, int32_t window, float scale, void* out,
+                    void* stream);
+
 /* rpa_destroy -- free a context (NULL-safe).  The caller must first make sure
  * no work enqueued with it is still running. */
 void rpa_destroy(rpa_ctx* ctx);
@@ -160,7 +189,11 @@ enum {
                                     (a positive value is rounded up to 32)      */
   RPA_OPT_PATH = 2,              /* 0 automatic, 1 every sequence through the
                                     prefill kernel, 2 decode kernel wherever the
-                                    rows of a sequence fit one decode item      */
+                                    rows of a sequence fit one decode item,
+                                    3 every token through the decode kernel
+                                    (longer sequences in chunks of
+                                    decode-item rows; the path fp8 calls take,
+                                    whatever this option says)                  */
   RPA_OPT_DECODE_MAX_ROWS = 4,   /* most q_len * G rows of a decode item (1..16)  */
   RPA_OPT_DECODE_WAVES = 5,      /* waves per decode workgroup: 0 automatic
                                     (4), 4, 8 (head size 512 always runs 4)     */
@@ -234,6 +267,16 @@ int rpa_kernel_times(rpa_ctx* ctx, int32_t kind, float* ms, int32_t capacity, in
  */
 int rpa_probe_read(const void* src, int64_t bytes, int32_t workgroups, void* sink, void* stream);
 int rpa_probe_mfma(int32_t workgroups, int32_t iterations, void* sink, void* stream);
+
+/*
+ * rpa_probe_e4m3 -- convert `count` (a multiple of 8, 8 .. 2^30) OCP FP8 E4M3
+ * bytes at device `src` to bf16 at device `dst` (2 * count bytes), with the
+ * conversion rpa_forward_fp8's kernel applies to the cache bytes, on
+ * `stream`, asynchronously.  A check of that conversion on its own: every
+ * E4M3 value is exact in bf16.  Returns RPA_ERR_INVALID_ARG for NULL pointers
+ * or a bad count, RPA_ERR_HIP if the launch fails.
+ */
+int rpa_probe_e4m3(const void* src, void* dst, int64_t count, void* stream);
 
 /*
  * Planner introspection (host only, no device call).  The host builds the

@@ -142,15 +142,18 @@ class RaggedPagedAttention:
         return buf[:min(count.value, buf.shape[0])].copy()
 
     # -- forward --------------------------------------------------------------
-    def _checked(self, q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream):
+    def _checked(self, q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream,
+                 kv_dtype=torch.bfloat16):
         cu = _host_i32(cu_q_lens)
         kv = _host_i32(kv_lens)
         n = int(kv.shape[0])
         if cu.shape[0] != n + 1:
             raise ValueError("cu_q_lens must have num_seqs + 1 entries")
-        for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
-            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+        if q.dtype != torch.bfloat16 or not q.is_cuda or not q.is_contiguous():
+            raise ValueError("q must be a contiguous bf16 CUDA tensor")
+        for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+            if t.dtype != kv_dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {kv_dtype} CUDA tensor")
         if page_table.dtype != torch.int32 or not page_table.is_cuda or not page_table.is_contiguous():
             raise ValueError("page_table must be a contiguous int32 CUDA tensor")
         if q.dim() != 3 or q.shape[1] != self.num_q_heads or q.shape[2] != self.head_dim:
@@ -215,6 +218,29 @@ class RaggedPagedAttention:
                     float(scale), out.data_ptr(), self._stream_ptr))
         return out
 
+    def forward_fp8(self, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                    k_scales: torch.Tensor, v_scales: torch.Tensor, page_table: torch.Tensor, cu_q_lens,
+                    kv_lens, window: int = 0, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None,
+                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """``forward`` over an fp8 KV cache: ``k_pages`` / ``v_pages`` hold OCP
+        FP8 E4M3 bytes (uint8, [P, page_size, Hkv, D]) and ``k_scales`` /
+        ``v_scales`` one float32 per KV head (CUDA tensors); element bytes
+        stand for their E4M3 value times their head's scale."""
+        if scale is None:
+            scale = float(self.head_dim) ** -0.5
+        cu, kv, n, out = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream,
+                                       kv_dtype=torch.uint8)
+        for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+            if (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()
+                    or tuple(t.shape) != (self.num_kv_heads,)):
+                raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape [{self.num_kv_heads}]")
+        self._call(self._lib.rpa_forward_fp8, "rpa_forward_fp8", q.device,
+                   (self._ctx, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), k_scales.data_ptr(),
+                    v_scales.data_ptr(), page_table.data_ptr(), cu.ctypes.data, kv.ctypes.data, n, int(window),
+                    float(scale), out.data_ptr(), self._stream_ptr))
+        return out
+
     __call__ = forward
 
 
@@ -258,3 +284,18 @@ def probe_mfma(workgroups: int, iterations: int, sink: torch.Tensor,
     if st != RPA_OK:
         raise RpaError(st, "rpa_probe_mfma")
     return int(workgroups) * 8 * int(iterations) * 4 * 32768
+
+
+def probe_e4m3(src: torch.Tensor, dst: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 values of the E4M3 bytes ``src`` (uint8 CUDA tensor, size a
+    multiple of 8), converted by the fp8 decode kernel's own conversion."""
+    if src.dtype != torch.uint8 or not src.is_cuda or not src.is_contiguous() or src.numel() % 8:
+        raise ValueError("src must be a contiguous uint8 CUDA tensor with a multiple of 8 elements")
+    if dst is None:
+        dst = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(src.device)
+    st = lib.rpa_probe_e4m3(src.data_ptr(), dst.data_ptr(), src.numel(), ctypes.c_void_p(stream.cuda_stream))
+    if st != RPA_OK:
+        raise RpaError(st, "rpa_probe_e4m3")
+    return dst

@@ -28,8 +28,9 @@ RPA_KERNEL_DECODE = 1
 RPA_KERNEL_MERGE = 2
 RPA_KERNEL_APPEND = 3
 
-EXPORTED = ("rpa_create", "rpa_forward", "rpa_forward_append", "rpa_destroy", "rpa_status_string", "rpa_last_error",
-            "rpa_set_option", "rpa_plan", "rpa_kernel_times", "rpa_probe_read", "rpa_probe_mfma")
+EXPORTED = ("rpa_create", "rpa_forward", "rpa_forward_append", "rpa_forward_fp8", "rpa_destroy", "rpa_status_string",
+            "rpa_last_error", "rpa_set_option", "rpa_plan", "rpa_kernel_times", "rpa_probe_read", "rpa_probe_mfma",
+            "rpa_probe_e4m3")
 
 
 class Config(ctypes.Structure):
@@ -88,6 +89,9 @@ def load() -> ctypes.CDLL:
     lib.rpa_forward_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_float, vp, vp]
     lib.rpa_forward_append.restype = ctypes.c_int
+    lib.rpa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_float, vp, vp]
+    lib.rpa_forward_fp8.restype = ctypes.c_int
     lib.rpa_destroy.argtypes = [vp]
     lib.rpa_destroy.restype = None
     lib.rpa_status_string.argtypes = [ctypes.c_int]
@@ -105,6 +109,8 @@ def load() -> ctypes.CDLL:
     lib.rpa_probe_read.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp]
     lib.rpa_probe_read.restype = ctypes.c_int
     lib.rpa_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.rpa_probe_e4m3.argtypes = [vp, vp, ctypes.c_int64, vp]
+    lib.rpa_probe_e4m3.restype = ctypes.c_int
     lib.rpa_probe_mfma.restype = ctypes.c_int
     _lib = lib
     return lib

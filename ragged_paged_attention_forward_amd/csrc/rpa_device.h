@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rpa.h"
 #include "rpa_launch.h"
 #include "rpa_kargs.h"
@@ -108,11 +110,32 @@ RPA_DEV u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
 }
 
+RPA_DEV u32x2 load8(const uint8_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+RPA_DEV u32x2 buffer_load8(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, byte_off, 0, 0));
+}
+
+// Eight OCP FP8 E4M3 bytes (two little-endian words) to the eight bf16 a
+// 16-byte load of bf16 elements would give (element i in half-word i).
+// Every E4M3 value is exact in bf16; v_cvt_scalef32_pk_bf16_fp8 with scale
+// 1.0 converts the low or the high byte pair of a word, the lower byte into
+// the lower half-word.
+RPA_DEV u32x4 e4m3x8_to_bf16x8(const u32x2& w) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true))};
+}
+
 // Wave-uniform load through the constant address space, so it becomes a
 // scalar load that does not wait behind the vector loads in flight.
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
 RPA_DEV int32_t uniform_load(const int32_t* p, int idx) {
   return ((const_i32_ptr)(p))[idx];
+}
+typedef const float __attribute__((address_space(4)))* const_f32_ptr;
+RPA_DEV float uniform_load(const float* p, int idx) {
+  return ((const_f32_ptr)(p))[idx];
 }
 
 // KernelArgs: see rpa_kargs.h
@@ -883,7 +906,12 @@ struct DecodeCfg {
 
 // Second launch bound: waves per SIMD to fit (two, so a compute unit holds two
 // workgroups of 4 waves; one for D = 512 whose fragments need the full file).
-template <int D, int NW, bool UNI>
+// KV8: the pools hold OCP FP8 E4M3 bytes with one K and one V scale per KV
+// head; each lane loads 8 bytes where the bf16 form loads 16 and converts
+// them to the same bf16 operand layout.  The K scale joins the score scale
+// and the V scale the output weight (both are per KV head, so they factor
+// out of the dot products).
+template <int D, int NW, bool UNI, bool KV8>
 __global__ void __launch_bounds__(NW * 64, D >= 512 ? 1 : 2)
 rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   using C = DecodeCfg<D, NW>;
@@ -908,14 +936,21 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   const int g = it.kv_head;
   const int rows = it.q_count * G;
   const int32_t* __restrict__ pt_row = page_table + static_cast<int64_t>(it.seq) * args.max_pages;
-  const uint16_t* __restrict__ kbase = k_pages;
-  const uint16_t* __restrict__ vbase = v_pages;
+  using KVT = typename std::conditional<KV8, uint8_t, uint16_t>::type;
+  constexpr int ESZ = sizeof(KVT);
+  const KVT* __restrict__ kbase = reinterpret_cast<const KVT*>(k_pages);
+  const KVT* __restrict__ vbase = reinterpret_cast<const KVT*>(v_pages);
   const int page_size = args.page_size;
   const int64_t row_stride = static_cast<int64_t>(hkv) * D;
   const int kv_begin = it.kv_begin;
   const int kv_end = it.kv_end;
   const int window = args.window;
-  const float sl2 = args.scale_log2;
+  float sl2 = args.scale_log2;
+  float vscale = 1.f;
+  if constexpr (KV8) {
+    sl2 *= uniform_load(args.k_scales, g);
+    vscale = uniform_load(args.v_scales, g);
+  }
 
   // query row n = ln: token ln / G, head ln % G
   const int tk = ln / G;
@@ -939,7 +974,7 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   // 32-key chunks aligned to 32 keys; with UNI a chunk never crosses a page.
   const int chunk0 = (kv_begin / 32) * 32;
   const int n_chunks = (kv_end - chunk0 + 31) / 32;
-  const int row_bytes = static_cast<int>(row_stride) * 2;   // bytes between key rows of a page
+  const int row_bytes = static_cast<int>(row_stride) * ESZ;   // bytes between key rows of a page
   int next_page = 0;
   if constexpr (UNI) {
     if (wave < n_chunks) next_page = uniform_load(pt_row, (chunk0 + wave * 32) / page_size);
@@ -949,6 +984,8 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     // keys of this lane: K rows k0 + 16*kb + ln; V rows k0 + 4*lq + j and k0 + 16 + 4*lq + j
     u32x4 kf[2][D / 32];
     u32x4 vf[C::NU][8];
+    [[maybe_unused]] u32x2 kr[2][D / 32];   // KV8: the raw bytes of kf / vf
+    [[maybe_unused]] u32x2 vr[C::NU][8];
     if constexpr (UNI) {
       // One page holds the whole chunk: buffer loads against the chunk's valid
       // key rows [lo, hi); rows outside read as zero (negative offsets wrap
@@ -958,15 +995,18 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       const int lo = k0 > kv_begin ? k0 : kv_begin;
       const int hi = k0 + 32 < kv_end ? k0 + 32 : kv_end;
       const int64_t lo_off = ((static_cast<int64_t>(page) * page_size + (lo - (lo / page_size) * page_size)) * hkv + g) * D;
-      const uint32_t nbytes = static_cast<uint32_t>((hi - lo - 1) * row_bytes + D * 2);
+      const uint32_t nbytes = static_cast<uint32_t>((hi - lo - 1) * row_bytes + D * ESZ);
       const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + lo_off, nbytes);
       const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + lo_off, nbytes);
       const int rel = k0 - lo;   // <= 0
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int off = (rel + kb * 16 + ln) * row_bytes + lq * 16;
+        const int off = (rel + kb * 16 + ln) * row_bytes + lq * 8 * ESZ;
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) kf[kb][kk] = buffer_load16(krs, off + kk * 64);
+        for (int kk = 0; kk < D / 32; ++kk) {
+          if constexpr (KV8) kr[kb][kk] = buffer_load8(krs, off + kk * 32);
+          else kf[kb][kk] = buffer_load16(krs, off + kk * 64);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -974,7 +1014,8 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 #pragma unroll
         for (int u = 0; u < C::NU; ++u) {
           const int c = u * 16 + ln;
-          vf[u][j] = c < C::NCH ? buffer_load16(vrs, key_rel * row_bytes + c * 16) : u32x4{0, 0, 0, 0};
+          if constexpr (KV8) vr[u][j] = c < C::NCH ? buffer_load8(vrs, key_rel * row_bytes + c * 8) : u32x2{0, 0};
+          else vf[u][j] = c < C::NCH ? buffer_load16(vrs, key_rel * row_bytes + c * 16) : u32x4{0, 0, 0, 0};
         }
       }
     } else {
@@ -1000,8 +1041,10 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
         const bool ok = kkey[kb] >= kv_begin && kkey[kb] < kv_end;
         const int64_t off = kv_row(kkey[kb], kpid[kb]);
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-          kf[kb][kk] = ok ? load16(kbase + off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
+        for (int kk = 0; kk < D / 32; ++kk) {
+          if constexpr (KV8) kr[kb][kk] = ok ? load8(kbase + off + kk * 32 + lq * 8) : u32x2{0, 0};
+          else kf[kb][kk] = ok ? load16(kbase + off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
+        }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -1010,9 +1053,20 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 #pragma unroll
         for (int u = 0; u < C::NU; ++u) {
           const int c = u * 16 + ln;
-          vf[u][j] = (ok && c < C::NCH) ? load16(vbase + off + c * 8) : u32x4{0, 0, 0, 0};
+          if constexpr (KV8) vr[u][j] = (ok && c < C::NCH) ? load8(vbase + off + c * 8) : u32x2{0, 0};
+          else vf[u][j] = (ok && c < C::NCH) ? load16(vbase + off + c * 8) : u32x4{0, 0, 0, 0};
         }
       }
+    }
+    if constexpr (KV8) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) kf[kb][kk] = e4m3x8_to_bf16x8(kr[kb][kk]);
+#pragma unroll
+      for (int u = 0; u < C::NU; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vf[u][j] = e4m3x8_to_bf16x8(vr[u][j]);
     }
 
     f32x4 s[2];
@@ -1076,7 +1130,7 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 #pragma unroll
   for (int w = 0; w < NW; ++w) lsum += fast_exp2(lds_m[w * 16 + ln] - base) * lds_l[w * 16 + ln];
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  const float wscale = fast_exp2(m_run - base) * inv;   // this wave's share, normalised
+  const float wscale = fast_exp2(m_run - base) * inv * vscale;   // this wave's share, normalised
 #pragma unroll
   for (int u = 0; u < C::NU; ++u)
 #pragma unroll
@@ -1240,19 +1294,22 @@ static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, hipStream_t
   return launch_prefill_u<D, BN, NW, NB, NS, DS, false>(a, n_items, stream);
 }
 
-template <int D, int NW, bool UNI>
+template <int D, int NW, bool UNI, bool KV8 = false>
 static hipError_t launch_decode_u(const KernelArgs& a, int n_items, hipStream_t stream) {
   using C = DecodeCfg<D, NW>;
-  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream, a.items,
-                     a.page_table, a.q, a.k, a.v, a);
+  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, UNI, KV8>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream,
+                     a.items, a.page_table, a.q, a.k, a.v, a);
   return hipGetLastError();
 }
 
 // Eight-wave workgroups are not used for D = 512: two waves per SIMD cannot
-// hold its fragments.
+// hold its fragments.  The fp8 form is built with four waves only.
 template <int D>
-static hipError_t launch_decode_t(const KernelArgs& a, int n_items, int waves, hipStream_t stream) {
+static hipError_t launch_decode_t(const KernelArgs& a, int n_items, int waves, bool kv8, hipStream_t stream) {
   const bool uni = a.page_size % 32 == 0;
+  if (kv8)
+    return uni ? launch_decode_u<D, 4, true, true>(a, n_items, stream)
+               : launch_decode_u<D, 4, false, true>(a, n_items, stream);
   if constexpr (D < 512) {
     if (waves == 8) return uni ? launch_decode_u<D, 8, true>(a, n_items, stream)
                                : launch_decode_u<D, 8, false>(a, n_items, stream);
@@ -1299,8 +1356,8 @@ constexpr int prefill_wgs_per_cu() {
   hipError_t launch_prefill_d##D(const KernelArgs& a, int n, hipStream_t s) {               \
     return launch_prefill_t<RPA_PREFILL_SHAPE_##D>(a, n, s);                               \
   }                                                                                         \
-  hipError_t launch_decode_d##D(const KernelArgs& a, int n, int waves, hipStream_t s) {     \
-    return launch_decode_t<D>(a, n, waves, s);                                              \
+  hipError_t launch_decode_d##D(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s) { \
+    return launch_decode_t<D>(a, n, waves, kv8, s);                                         \
   }                                                                                         \
   hipError_t launch_merge_d##D(const KernelArgs& a, int n, hipStream_t s) {                 \
     return launch_merge_t<D>(a, n, s);                                                      \

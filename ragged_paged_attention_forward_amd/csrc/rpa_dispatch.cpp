@@ -10,28 +10,28 @@
 namespace rpa {
 
 hipError_t launch_prefill_d64(const KernelArgs& a, int n, hipStream_t s);
-hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, hipStream_t s);
+hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
 hipError_t launch_merge_d64(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
 int prefill_rows_d64();
 int prefill_wgs_per_cu_d64();
 hipError_t launch_prefill_d128(const KernelArgs& a, int n, hipStream_t s);
-hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, hipStream_t s);
+hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
 hipError_t launch_merge_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
 int prefill_rows_d128();
 int prefill_wgs_per_cu_d128();
 hipError_t launch_prefill_d256(const KernelArgs& a, int n, hipStream_t s);
-hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, hipStream_t s);
+hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
 hipError_t launch_merge_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
 int prefill_rows_d256();
 int prefill_wgs_per_cu_d256();
 hipError_t launch_prefill_d512(const KernelArgs& a, int n, hipStream_t s);
-hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, hipStream_t s);
+hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
 hipError_t launch_merge_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d512(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
@@ -81,6 +81,8 @@ static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
   a.window = l.window;
   a.scale_log2 = l.scale_log2;
   a.prefill_rows = prefill_rows_for(l.head_dim);
+  a.k_scales = l.k_scales;
+  a.v_scales = l.v_scales;
   return a;
 }
 
@@ -102,11 +104,12 @@ hipError_t launch_decode(const LaunchArgs& l, const rpa_work_item* items, int n_
   const KernelArgs a = make_args(l, items);
   hipStream_t s = static_cast<hipStream_t>(l.stream);
   const int w = l.decode_waves;
+  const bool kv8 = l.kv_fp8 != 0;
   switch (l.head_dim) {
-    case 64: return launch_decode_d64(a, n_items, w, s);
-    case 128: return launch_decode_d128(a, n_items, w, s);
-    case 256: return launch_decode_d256(a, n_items, w, s);
-    case 512: return launch_decode_d512(a, n_items, w, s);
+    case 64: return launch_decode_d64(a, n_items, w, kv8, s);
+    case 128: return launch_decode_d128(a, n_items, w, kv8, s);
+    case 256: return launch_decode_d256(a, n_items, w, kv8, s);
+    case 512: return launch_decode_d512(a, n_items, w, kv8, s);
     default: return hipErrorInvalidValue;
   }
 }

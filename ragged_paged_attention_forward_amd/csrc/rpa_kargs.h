@@ -27,6 +27,8 @@ struct KernelArgs {
   int32_t window;
   float scale_log2;      // scale * log2(e)
   int32_t prefill_rows;  // rows of a prefill tile (rows of a prefill split's partial block)
+  const float* k_scales; // fp8 pools: K scale per KV head (else unused)
+  const float* v_scales; // fp8 pools: V scale per KV head (else unused)
 };
 
 }  // namespace rpa

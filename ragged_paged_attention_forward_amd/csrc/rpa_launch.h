@@ -28,6 +28,9 @@ struct LaunchArgs {
   int32_t window;
   float scale_log2;
   int32_t decode_waves;  // waves per decode workgroup: 4 or 8
+  int32_t kv_fp8;        // 1: k / v hold OCP FP8 E4M3 bytes with per-KV-head scales
+  const float* k_scales; // device [Hkv] (fp8 only)
+  const float* v_scales; // device [Hkv] (fp8 only)
   void* stream;
 };
 

@@ -223,6 +223,16 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
       dec.push_back({s, cu[s], q_len, pos_first, range_begin(pos_first, window), kv_len});
       continue;
     }
+    if (p.path_mode == 3 && dec_tokens > 0) {
+      // every token through the decode kernel: consecutive chunks of
+      // dec_tokens tokens, each with the key range its rows see
+      for (int32_t t = 0; t < q_len; t += dec_tokens) {
+        const int32_t count = std::min(dec_tokens, q_len - t);
+        const int32_t pos0 = pos_first + t;
+        dec.push_back({s, cu[s] + t, count, pos0, range_begin(pos0, window), pos0 + count});
+      }
+      continue;
+    }
     for (int32_t g = 0; g < p.num_kv_heads; ++g) {
       for (int32_t t = 0; t < q_len; t += tile_tokens) {
         const int32_t count = std::min(tile_tokens, q_len - t);

@@ -26,7 +26,8 @@ struct PlanParams {
   int decode_waves = 4;        // waves of one decode workgroup
   int64_t decode_split_keys = 0;  // 0: automatic
   int64_t prefill_split_keys = 0; // 0: automatic, < 0: never, > 0: fixed
-  int path_mode = 0;           // 0 auto, 1 all prefill kernel, 2 decode where it fits
+  int path_mode = 0;           // 0 auto, 1 all prefill kernel, 2 decode where it fits,
+                               // 3 every token through decode items (long sequences in chunks)
   int num_cus = 256;           // compute units to fill
   int xcd_groups = 8;          // prefill order: workgroups b, b+X, b+2X, ... share a
                                // chiplet (and its L2); <= 1 keeps the plain order

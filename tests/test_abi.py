@@ -130,7 +130,8 @@ def test_empty_call_returns_ok_without_device_work():
 
 def test_set_option_validation():
     lib, st, ctx = _ctx()
-    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_PATH, 3) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_PATH, 4) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_PATH, 3) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_WAVES, 6) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_WAVES, 8) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_MAX_ROWS, 17) == _lib.RPA_ERR_INVALID_ARG
@@ -223,3 +224,38 @@ def test_forward_append_rejects_bad_pointers_before_launch():
     assert lib.rpa_forward_append(None, FAKE, FAKE, FAKE, FAKE, other, FAKE, cu_p, kv_p, 1, 0, 1.0, other,
                                   None) == _lib.RPA_ERR_INVALID_ARG
     lib.rpa_destroy(ctx)
+
+
+def test_forward_fp8_rejects_bad_arguments_before_launch():
+    lib, st, ctx = _ctx()
+    cu_a, cu_p = i32([0, 2])
+    kv_a, kv_p = i32([7])
+    other = ctypes.c_void_p(0x900000)
+    # q, k_pages, v_pages, k_scales, v_scales, page_table, out
+    for args in ((FAKE, FAKE, FAKE, None, FAKE, FAKE, other), (FAKE, FAKE, FAKE, FAKE, None, FAKE, other),
+                 (None, FAKE, FAKE, FAKE, FAKE, FAKE, other), (FAKE, None, FAKE, FAKE, FAKE, FAKE, other),
+                 (FAKE, FAKE, FAKE, FAKE, FAKE, None, other), (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)):
+        q, kp, vp, ks, vs, pt, out = args
+        st = lib.rpa_forward_fp8(ctx, q, kp, vp, ks, vs, pt, cu_p, kv_p, 1, 0, 1.0, out, None)
+        assert st == _lib.RPA_ERR_INVALID_ARG, args
+    bad_kv_a, bad_kv_p = i32([1])   # q_len 2 > kv_len 1
+    st = lib.rpa_forward_fp8(ctx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cu_p, bad_kv_p, 1, 0, 1.0, other, None)
+    assert st == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_forward_fp8(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cu_p, kv_p, 1, 0, 1.0, other,
+                               None) == _lib.RPA_ERR_INVALID_ARG
+    lib.rpa_destroy(ctx)
+    # more than 16 query heads per KV head: no decode item holds one token
+    lib, st, ctx = _ctx(hq=32, hkv=1)
+    assert st == _lib.RPA_OK
+    st = lib.rpa_forward_fp8(ctx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cu_p, kv_p, 1, 0, 1.0, other, None)
+    assert st == _lib.RPA_ERR_UNSUPPORTED
+    lib.rpa_destroy(ctx)
+
+
+def test_probe_e4m3_rejects_bad_arguments():
+    lib = _lib.load()
+    addr = ctypes.c_void_p(0x800000)
+    assert lib.rpa_probe_e4m3(None, addr, 64, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_e4m3(addr, None, 64, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_e4m3(addr, addr, 0, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_e4m3(addr, addr, 12, None) == _lib.RPA_ERR_INVALID_ARG

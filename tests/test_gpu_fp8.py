@@ -1,0 +1,119 @@
+"""GPU checks of rpa_forward_fp8 (through the C ABI): attention over a KV
+cache held as OCP FP8 E4M3 bytes with per-KV-head K and V scales matches the
+oracle's fp8 forward (max-abs <= 2e-2, mean-abs <= 2e-3, no NaN), and the
+kernel's byte conversion matches torch's E4M3 decoding for every byte.  Page
+slots past kv_len and the trap page hold the E4M3 NaN byte, so a kernel that
+reads them shows it in its output."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.rpa_oracle as ora
+import rpa_workloads as wl
+from gpu_common import compare, gpu_available, make_attn
+
+pytestmark = pytest.mark.gpu
+
+if not gpu_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import ragged_paged_attention_forward_amd as R  # noqa: E402
+
+
+def mixed_small(window, seed=205, page_size=128):
+    rng = np.random.default_rng(seed)
+    kv = rng.integers(64, 1500, 64)
+    chunks = [(300, 300), (150, 230), (70, 400), (33, 80)]
+    return wl.Workload(f"mixed_small_w{window}", chunks + [(1, int(k)) for k in kv], 8, 1, 256, page_size,
+                       window, seed, length_draw=(64, 1500, 64))
+
+
+CASES = {
+    "tiny": lambda: wl.tiny(),
+    "decode": lambda: wl.decode(),
+    "decode_pages16": lambda: wl.custom([(1, 64 + 37 * i) for i in range(40)], 8, 1, 256, 16, 0, seed=41),
+    "swa_prefill_1100": lambda: wl.swa_prefill(tokens=1100),
+    "global_prefill_300": lambda: wl.global_prefill(tokens=300),
+    "mixed_small_w0": lambda: mixed_small(0),
+    "mixed_small_w1024_pages16": lambda: mixed_small(1024, page_size=16),
+    "gqa4_d128_chunks": lambda: wl.custom([(40, 100), (1, 17), (129, 129), (3, 1000)], 16, 4, 128, 32, 0, seed=42),
+    "with_empty_sequences": lambda: wl.custom([(0, 50), (3, 70), (0, 1), (1, 300), (0, 0), (17, 17)], 8, 2, 256, 64,
+                                              0, seed=43),
+    "mha_d64_window": lambda: wl.custom([(9, 200), (1, 65), (64, 64)], 4, 4, 64, 16, 33, seed=44),
+    "g16_d128": lambda: wl.custom([(5, 90), (1, 400)], 16, 1, 128, 64, 0, seed=45),
+}
+
+
+def run_fp8(f: wl.Fp8Inputs, attn=None):
+    d = f.to("cuda")
+    b = f.base
+    attn = attn or make_attn(b.workload)
+    out = attn.forward_fp8(d.base.q, d.k_pages, d.v_pages, d.k_scales, d.v_scales, d.base.page_table,
+                           b.cu_q_lens, b.kv_lens, b.window, b.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_fp8(f: wl.Fp8Inputs, rows=None):
+    b = f.base
+    return ora.forward_fp8_rows(b.q, f.k_pages, f.v_pages, f.k_scales, f.v_scales, b.page_table, b.cu_q_lens,
+                                b.kv_lens, b.window, b.scale, rows)
+
+
+def test_e4m3_conversion_matches_torch_for_every_byte():
+    rng = np.random.default_rng(7)
+    codes = np.concatenate([np.arange(256), rng.integers(0, 256, 4096)]).astype(np.uint8)
+    src = torch.from_numpy(codes)
+    got = R.probe_e4m3(src.cuda())
+    torch.cuda.synchronize()
+    want = src.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    g, w = got.cpu().view(torch.int16), want.view(torch.int16)
+    nan = torch.isnan(want)
+    assert torch.equal(torch.isnan(got.cpu()), nan)
+    assert torch.equal(g[~nan], w[~nan])
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fp8_parity(name):
+    w = CASES[name]()
+    print(f"fp8 parity {name}: seqs={w.num_seqs} T={w.total_q} d={w.head_dim} B={w.page_size} W={w.window}",
+          flush=True)
+    f = wl.make_fp8_inputs(w, poison=True)
+    out = run_fp8(f)
+    compare(out, oracle_fp8(f), label=name)
+
+
+@pytest.mark.parametrize("window", [0, 1024])
+def test_fp8_mixed_full_size_sampled(window):
+    w = wl.mixed(window=window)
+    print(f"fp8 mixed full size W={window}: T={w.total_q}", flush=True)
+    f = wl.make_fp8_inputs(w, poison=True)
+    out = run_fp8(f)
+    t_q = w.total_q
+    rows = wl.sample_rows(t_q, 48, seed=window + 3, must=[0, 4095, 4096, t_q - 513, t_q - 1])
+    compare(out, oracle_fp8(f, rows), rows=rows, label=f"mixed_w{window}")
+
+
+def test_fp8_is_bitwise_reproducible():
+    f = wl.make_fp8_inputs(mixed_small(0), poison=True)
+    attn = make_attn(f.base.workload)
+    a = run_fp8(f, attn).clone()
+    b = run_fp8(f, attn)
+    assert torch.equal(a, b)
+
+
+def test_fp8_and_bf16_calls_alternate_on_one_context():
+    """The cached plan of an fp8 call (every token in decode items) is not the
+    bf16 one for the same metadata: alternating calls each get their own."""
+    w = wl.custom([(40, 100), (1, 300), (70, 70)], 8, 2, 128, 32, 0, seed=46)
+    f = wl.make_fp8_inputs(w, poison=True)
+    b = f.base
+    attn = make_attn(w)
+    d = b.to("cuda")
+    ref16 = ora.forward_inputs(b)
+    ref8 = oracle_fp8(f)
+    for _ in range(2):
+        out16 = attn.forward(d.q, d.k_pages, d.v_pages, d.page_table, b.cu_q_lens, b.kv_lens, b.window, b.scale)
+        torch.cuda.synchronize()
+        compare(out16, ref16, label="bf16")
+        compare(run_fp8(f, attn), ref8, label="fp8")

@@ -125,6 +125,27 @@ def test_plan_options_keep_coverage(options):
                 assert it["kv_end"] - it["kv_begin"] <= split
 
 
+@pytest.mark.parametrize("w", WORKLOADS, ids=lambda w: w.name + f"_w{w.window}_g{w.num_q_heads // w.num_kv_heads}")
+def test_all_decode_path_chunks_every_sequence(w):
+    """Path 3 (the path of fp8 calls): every token in decode items of at most
+    16 rows, long sequences in consecutive chunks; with G > 16 no decode item
+    fits and the prefill kernel keeps the sequences."""
+    cu, kv, info, items = plan_for(w, [(RPA_OPT_PATH, 3)])
+    check_plan(w, cu, kv, info, items)
+    g_ratio = w.num_q_heads // w.num_kv_heads
+    if g_ratio <= 16:
+        assert info["num_prefill_items"] == 0
+        per = 16 // g_ratio
+        for it in items:
+            if it["split_index"] == 0:
+                s = it["seq"]
+                # chunks start at multiples of 16 / G tokens of their sequence
+                assert (it["q_start"] - cu[s]) % per == 0
+                assert it["q_count"] == min(per, cu[s + 1] - it["q_start"])
+    else:
+        assert info["num_decode_items"] == 0
+
+
 def prefill_keys(items):
     return [it["kv_end"] - it["kv_begin"] for it in items if it["kind"] == 0]
 
