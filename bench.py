@@ -20,6 +20,10 @@ the same workload is reported as ``cpu_baseline``.
 new K/V rows are written into their pages (the same bytes each step) before the
 attention kernels, and the append kernel is timed beside them.
 
+``--kv fp8`` holds the K/V pools as OCP FP8 E4M3 bytes with per-KV-head scales
+(drawn from the same bf16 values) and calls ``rpa_forward_fp8``; the K/V bytes
+of the roofline are then one byte per element.
+
 Prints ONE JSON line.
 
 Counter runs (HBM traffic of the dominant kernel):
@@ -67,9 +71,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, kernel: str):
+def load_traffic(workload: str, kernel: str, kv: str = "bf16"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    tag = workload if kv == "bf16" else f"{workload}_{kv}"
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -79,7 +84,7 @@ def load_traffic(workload: str, kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def kernel_work(w, items, merge_kernel=True):
+def kernel_work(w, items, merge_kernel=True, kv_elem_bytes=2):
     """Algorithmic FLOPs and bytes of each kernel kind for the planned step.
 
     A sequence belongs to the kernel kind of its work items.  Bytes count Q,
@@ -101,7 +106,7 @@ def kernel_work(w, items, merge_kernel=True):
         q_b = metrics.qo_bytes(seqs, w.num_q_heads, w.head_dim) // 2
         o_ids = ids if not merge_kernel else [s for s in ids if s not in split]
         o_b = metrics.qo_bytes([w.seqs[s] for s in o_ids], w.num_q_heads, w.head_dim) // 2
-        kv = metrics.kv_bytes(seqs, w.window, w.num_kv_heads, w.head_dim)
+        kv = metrics.kv_bytes(seqs, w.window, w.num_kv_heads, w.head_dim) * kv_elem_bytes // 2
         pages = sum(-(-kvl // w.page_size) for _, kvl in seqs) * 4
         out[kind] = {"flops": int(metrics.flops(seqs, w.window, w.num_q_heads, w.head_dim)),
                      "bytes": int(q_b + o_b + kv + pages), "seqs": len(seqs)}
@@ -302,7 +307,13 @@ def run(args):
     torch.cuda.set_device(dev)
 
     w = wl.by_name(args.workload)
-    host = wl.make_inputs(w)
+    fp8 = args.kv == "fp8"
+    if fp8:
+        host8 = wl.make_fp8_inputs(w)
+        host = host8.base
+        host.k_pages, host.v_pages = host8.k_pages, host8.v_pages   # the pools the steps read
+    else:
+        host = wl.make_inputs(w)
     t_q = w.total_q
     per_replica = sum(t.numel() * t.element_size() for t in (host.q, host.k_pages, host.v_pages)) * 2
     # enough replicas that the set exceeds the last-level cache four times,
@@ -312,11 +323,15 @@ def run(args):
     for _ in range(reps):
         d = host.to(dev)
         replicas.append((d, torch.empty_like(d.q)))
+    if fp8:
+        k_scales, v_scales = host8.k_scales.to(dev), host8.v_scales.to(dev)
     cu = np.ascontiguousarray(host.cu_q_lens.numpy().astype(np.int32))
     kv = np.ascontiguousarray(host.kv_lens.numpy().astype(np.int32))
 
     attn = R.RaggedPagedAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
                                   w.num_seqs, w.max_pages_per_seq, t_q)
+    if fp8:
+        attn.set_option(R.RPA_OPT_PATH, 3)   # the plan fp8 calls build (for the work accounting)
     info, items = attn.plan(cu, kv, w.window)
     # host metadata builder: one rpa_plan call (work list built, not copied out), best of 20
     plan_s = []
@@ -342,6 +357,10 @@ def run(args):
             kn, vn = news[i % reps]
             attn.forward_append(d.q, kn, vn, d.k_pages, d.v_pages, d.page_table, cu, kv, w.window, w.scale,
                                 out=out, stream=stream)
+            return
+        if fp8:
+            attn.forward_fp8(d.q, d.k_pages, d.v_pages, k_scales, v_scales, d.page_table, cu, kv, w.window,
+                             w.scale, out=out, stream=stream)
             return
         attn.forward(d.q, d.k_pages, d.v_pages, d.page_table, cu, kv, w.window, w.scale, out=out,
                      stream=stream)
@@ -383,7 +402,8 @@ def run(args):
             kernels[name] = st
     attn.set_option(R.RPA_OPT_KERNEL_TIMING, 0)
 
-    work = kernel_work(w, items, merge_kernel="merge" in kernels)
+    kv_elem = 1 if fp8 else 2
+    work = kernel_work(w, items, merge_kernel="merge" in kernels, kv_elem_bytes=kv_elem)
     # The dominant kernel is the one with the largest roofline time (its
     # algorithmic FLOPs at the MFMA peak or bytes at the HBM peak, whichever
     # is larger): with the decode kernel on a second stream, durations overlap
@@ -403,16 +423,17 @@ def run(args):
     mp["frac"] = round(achieved / mp["value"], 4)
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "measured_peak": mp,
-                "traffic": load_traffic(args.workload, KERNEL_NAMES[dom]),
+                "traffic": load_traffic(args.workload, KERNEL_NAMES[dom], args.kv),
                 "kernel": KERNEL_NAMES[dom], "kernel_ms_mean": k_ms,
                 "algorithmic_bytes": kw["bytes"], "algorithmic_flops": kw["flops"],
                 "source_sha256_16": kernel_source_hash()}
 
     from ragged_paged_attention_forward_amd import metrics
     step_flops = metrics.flops(w.seqs, w.window, w.num_q_heads, w.head_dim)
+    kv_b = metrics.kv_bytes(w.seqs, w.window, w.num_kv_heads, w.head_dim) * kv_elem // 2
     step_bytes = metrics.total_bytes(w.seqs, w.window, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                     w.page_size)
-    kv_b = metrics.kv_bytes(w.seqs, w.window, w.num_kv_heads, w.head_dim)
+                                     w.page_size) - metrics.kv_bytes(w.seqs, w.window, w.num_kv_heads,
+                                                                     w.head_dim) + kv_b
     assert info["visible_pairs"] == metrics.visible_pairs(w.seqs, w.window)
     ms_per_step = wall * 1e3 / args.steps
     for name in kernels:
@@ -436,6 +457,7 @@ def run(args):
                    "num_seqs": w.num_seqs, "q_tokens": t_q, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "window": w.window, "replicas": reps, "append_kv": bool(args.append),
+                   "kv_dtype": "fp8_e4m3" if fp8 else "bf16",
                    "parallelism": "single GPU"},
         "step_tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -451,7 +473,7 @@ def run(args):
         res["graph"] = graph_layers(torch, attn, replicas, w, cu, kv, args.graph_layers, stream)
     if args.copy_calibration:
         copy_calibration(torch, dev)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(res), flush=True)
     attn.close()
@@ -498,7 +520,7 @@ def pmc_summary(args):
     kf, nf = pick(fetch, kernel)
     kwr, nw = pick(write, kernel)
     rec = {
-        "workload": args.workload, "kernel": kernel,
+        "workload": args.workload, "kv_dtype": args.kv, "kernel": kernel,
         "kernel_source_sha256_16": kernel_source_hash(),
         "fetch_kib_per_dispatch": round(kf, 1), "write_kib_per_dispatch": round(kwr, 1),
         "dispatches": [nf, nw],
@@ -509,7 +531,8 @@ def pmc_summary(args):
         "commands": args.pmc_commands or [],
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    out = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    tag = args.workload if args.kv == "bf16" else f"{args.workload}_{args.kv}"
+    out = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -530,6 +553,8 @@ def main(argv=None):
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = >= 1 GiB total)")
     ap.add_argument("--graph-layers", type=int, default=0,
                     help="also time L layers' calls eagerly and as one captured HIP graph")
+    ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8"),
+                    help="K/V pool format: bf16, or OCP FP8 E4M3 with per-KV-head scales (rpa_forward_fp8)")
     ap.add_argument("--append", action="store_true",
                     help="each step also writes its new K/V rows into the pages (rpa_forward_append)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -546,6 +571,9 @@ def main(argv=None):
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(how it would shard is described in the design notes); run with --gpus 1.",
               file=sys.stderr)
+        return 2
+    if args.kv == "fp8" and args.append:
+        print("--append writes bf16 rows; it does not combine with --kv fp8", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
