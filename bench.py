@@ -58,7 +58,7 @@ LLC_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "ragged_paged_attention_forward_amd", "csrc")
 COPY_BYTES = 1 << 30            # calibration buffer (read once, written once)
 KERNEL_NAMES = {"prefill": "rpa_prefill_kernel", "decode": "rpa_decode_kernel", "merge": "rpa_merge_kernel",
-                "append": "rpa_append_kernel"}
+                "append": "rpa_append_kernel", "stage": "rpa_stage_kernel"}
 WORKLOADS = ("decode", "tiny", "swa_prefill", "global_prefill", "mixed", "mixed_swa")
 
 
@@ -117,6 +117,10 @@ def kernel_work(w, items, merge_kernel=True, kv_elem_bytes=2):
     # the KV append reads the step's new K and V rows and writes them into their pages
     new_rows = w.total_q * w.num_kv_heads * w.head_dim * 2 * 2
     out["append"] = {"flops": 0, "bytes": int(2 * new_rows), "seqs": w.num_seqs}
+    # fp8 staging: the prefill sequences' pages read as bytes, written as bf16
+    pre = [w.seqs[s] for s, k in kind_of.items() if k == "prefill"]
+    staged = sum(-(-kvl // w.page_size) for _, kvl in pre) * w.page_size * w.num_kv_heads * w.head_dim * 2
+    out["stage"] = {"flops": 0, "bytes": int(3 * staged), "seqs": len(pre)}
     return out
 
 
@@ -330,8 +334,6 @@ def run(args):
 
     attn = R.RaggedPagedAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
                                   w.num_seqs, w.max_pages_per_seq, t_q)
-    if fp8:
-        attn.set_option(R.RPA_OPT_PATH, 3)   # the plan fp8 calls build (for the work accounting)
     info, items = attn.plan(cu, kv, w.window)
     # host metadata builder: one rpa_plan call (work list built, not copied out), best of 20
     plan_s = []

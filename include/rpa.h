@@ -157,11 +157,16 @@ int rpa_forward_append(rpa_ctx* ctx, const void* q, const void* k_new, const voi
  *                 the caller keeps them valid until the work is done)
  *   all other arguments as for rpa_forward (q and out stay bf16)
  *
- * Every query token is computed by the split-KV decode kernel (sequences
- * longer than 16 / G tokens in chunks of that many tokens), which converts
- * the bytes to bf16 exactly in registers before its bf16 matrix products.
- * Errors as for rpa_forward, plus RPA_ERR_INVALID_ARG for a NULL scale
- * array and RPA_ERR_UNSUPPORTED when G = Hq / Hkv exceeds 16.
+ * The work is planned as for rpa_forward.  The split-KV decode kernel reads
+ * the bytes itself and converts them to bf16 exactly in registers (the K
+ * scale joins the score scale, the V scale the output weight).  For the
+ * sequences the prefill kernel serves, a staging kernel first converts
+ * their pages to bf16 (value times scale, rounded to nearest even) in a
+ * pool the context owns (grown on demand, like the split workspace), which
+ * the prefill kernel then reads through the pool's own page table; both run
+ * on `stream`.  With RPA_OPT_PATH = 3 every token goes through the decode
+ * kernel instead (no staging).  Errors as for rpa_forward, plus
+ * RPA_ERR_INVALID_ARG for a NULL scale array.
  */
 int rpa_forward_fp8(rpa_ctx* ctx, const void* q, const void* k_pages, const void* v_pages, const float* k_scales,
                     const float* v_scales, const int32_t* page_table, const int32_t* cu_q_lens,
@@ -192,8 +197,8 @@ enum {
                                     rows of a sequence fit one decode item,
                                     3 every token through the decode kernel
                                     (longer sequences in chunks of
-                                    decode-item rows; the path fp8 calls take,
-                                    whatever this option says)                  */
+                                    decode-item rows; with G > 16 the
+                                    prefill kernel keeps them)                  */
   RPA_OPT_DECODE_MAX_ROWS = 4,   /* most q_len * G rows of a decode item (1..16)  */
   RPA_OPT_DECODE_WAVES = 5,      /* waves per decode workgroup: 0 automatic
                                     (4), 4, 8 (head size 512 always runs 4)     */
@@ -239,7 +244,8 @@ int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);
  * RPA_ERR_INVALID_ARG (null ctx/count, bad kind, negative capacity) or
  * RPA_ERR_HIP.
  */
-enum { RPA_KERNEL_PREFILL = 0, RPA_KERNEL_DECODE = 1, RPA_KERNEL_MERGE = 2, RPA_KERNEL_APPEND = 3 };
+enum { RPA_KERNEL_PREFILL = 0, RPA_KERNEL_DECODE = 1, RPA_KERNEL_MERGE = 2, RPA_KERNEL_APPEND = 3,
+       RPA_KERNEL_STAGE = 4 /* rpa_forward_fp8: fp8 pages converted for the prefill kernel */ };
 int rpa_kernel_times(rpa_ctx* ctx, int32_t kind, float* ms, int32_t capacity, int32_t* count);
 
 /*

@@ -1269,6 +1269,60 @@ rpa_append_kernel(const rpa_work_item* __restrict__ items, const int32_t* __rest
 }
 
 // ---------------------------------------------------------------------------
+// fp8 staging: the pages of the sequences that the prefill kernel serves in an
+// fp8 call, converted to bf16 (E4M3 value times the KV head's scale, rounded
+// to nearest even) into pages of a bf16 pool, which the prefill kernel then
+// reads through the pool's own page table.  Workgroup (b, y) converts part y
+// of staged page b (kStageChunks 16-byte chunks per part, so that a launch
+// has enough workgroups when pages are large); stage[3b .. 3b+2] =
+// (sequence, page of the sequence, page of the pool).  Each thread converts
+// 16 bytes at a time (one KV head's row segment, as D is a multiple of 16)
+// into 32 bytes.
+// ---------------------------------------------------------------------------
+constexpr int kStageThreads = 256;
+constexpr int kStageChunks = 4 * kStageThreads;
+
+RPA_DEV uint32_t scale_bf16x2(uint32_t w, float sc) {
+  const float lo = __builtin_bit_cast(float, w << 16);
+  const float hi = __builtin_bit_cast(float, w & 0xffff0000u);
+  return pack_bf16x2(lo * sc, hi * sc);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kStageThreads)
+rpa_stage_kernel(const int32_t* __restrict__ stage, const int32_t* __restrict__ page_table,
+                 const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8, uint16_t* __restrict__ k_dst,
+                 uint16_t* __restrict__ v_dst, KernelArgs args) {
+  const int seq = stage[blockIdx.x * 3];
+  const int lp = stage[blockIdx.x * 3 + 1];
+  const int slot = stage[blockIdx.x * 3 + 2];
+  const int hkv = args.num_kv_heads;
+  const int64_t page_elems = static_cast<int64_t>(args.page_size) * hkv * D;
+  const int64_t src = static_cast<int64_t>(page_table[static_cast<int64_t>(seq) * args.max_pages + lp]) * page_elems;
+  const int64_t dst = static_cast<int64_t>(slot) * page_elems;
+  const int n16 = static_cast<int>(page_elems / 16);
+  const int first = blockIdx.y * kStageChunks;
+  const int last = first + kStageChunks < n16 ? first + kStageChunks : n16;
+  for (int i = first + threadIdx.x; i < last; i += kStageThreads) {
+    const int g = ((i * 16) / D) % hkv;
+    const float ks = args.k_scales[g];
+    const float vs = args.v_scales[g];
+    const u32x4 kr = *reinterpret_cast<const u32x4*>(k8 + src + i * 16);
+    const u32x4 vr = *reinterpret_cast<const u32x4*>(v8 + src + i * 16);
+    const u32x4 ka = e4m3x8_to_bf16x8(u32x2{kr[0], kr[1]});
+    const u32x4 kb = e4m3x8_to_bf16x8(u32x2{kr[2], kr[3]});
+    const u32x4 va = e4m3x8_to_bf16x8(u32x2{vr[0], vr[1]});
+    const u32x4 vb = e4m3x8_to_bf16x8(u32x2{vr[2], vr[3]});
+    u32x4* kd = reinterpret_cast<u32x4*>(k_dst + dst + i * 16);
+    u32x4* vd = reinterpret_cast<u32x4*>(v_dst + dst + i * 16);
+    kd[0] = u32x4{scale_bf16x2(ka[0], ks), scale_bf16x2(ka[1], ks), scale_bf16x2(ka[2], ks), scale_bf16x2(ka[3], ks)};
+    kd[1] = u32x4{scale_bf16x2(kb[0], ks), scale_bf16x2(kb[1], ks), scale_bf16x2(kb[2], ks), scale_bf16x2(kb[3], ks)};
+    vd[0] = u32x4{scale_bf16x2(va[0], vs), scale_bf16x2(va[1], vs), scale_bf16x2(va[2], vs), scale_bf16x2(va[3], vs)};
+    vd[1] = u32x4{scale_bf16x2(vb[0], vs), scale_bf16x2(vb[1], vs), scale_bf16x2(vb[2], vs), scale_bf16x2(vb[3], vs)};
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI>
@@ -1327,6 +1381,17 @@ static hipError_t launch_append_t(const KernelArgs& a, int n_items, const void* 
 }
 
 template <int D>
+static hipError_t launch_stage_t(const KernelArgs& a, const int32_t* stage, int n_pages, void* k_dst, void* v_dst,
+                                 hipStream_t stream) {
+  const int64_t n16 = int64_t(a.page_size) * a.num_kv_heads * D / 16;
+  const int parts = static_cast<int>((n16 + kStageChunks - 1) / kStageChunks);
+  hipLaunchKernelGGL((rpa_stage_kernel<D>), dim3(n_pages, parts), dim3(kStageThreads), 0, stream, stage, a.page_table,
+                     reinterpret_cast<const uint8_t*>(a.k), reinterpret_cast<const uint8_t*>(a.v),
+                     static_cast<uint16_t*>(k_dst), static_cast<uint16_t*>(v_dst), a);
+  return hipGetLastError();
+}
+
+template <int D>
 static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t stream) {
   hipLaunchKernelGGL((rpa_merge_kernel<D>), dim3(n_groups), dim3(MergeCfg<D>::THREADS), 0, stream, a);
   return hipGetLastError();
@@ -1365,6 +1430,10 @@ constexpr int prefill_wgs_per_cu() {
   hipError_t launch_append_d##D(const KernelArgs& a, int n, const void* kn, const void* vn, \
                                 void* kd, void* vd, hipStream_t s) {                        \
     return launch_append_t<D>(a, n, kn, vn, kd, vd, s);                                     \
+  }                                                                                         \
+  hipError_t launch_stage_d##D(const KernelArgs& a, const int32_t* st, int n, void* kd,     \
+                               void* vd, hipStream_t s) {                                   \
+    return launch_stage_t<D>(a, st, n, kd, vd, s);                                          \
   }                                                                                         \
   int prefill_rows_d##D() { return PrefillCfg<RPA_PREFILL_SHAPE_##D>::ROWS; }              \
   int prefill_wgs_per_cu_d##D() { return prefill_wgs_per_cu<PrefillCfg<RPA_PREFILL_SHAPE_##D>>(); }

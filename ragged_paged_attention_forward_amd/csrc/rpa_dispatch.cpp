@@ -14,6 +14,7 @@ hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, bool kv8, hi
 hipError_t launch_merge_d64(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
+hipError_t launch_stage_d64(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d64();
 int prefill_wgs_per_cu_d64();
 hipError_t launch_prefill_d128(const KernelArgs& a, int n, hipStream_t s);
@@ -21,6 +22,7 @@ hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, bool kv8, h
 hipError_t launch_merge_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
+hipError_t launch_stage_d128(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d128();
 int prefill_wgs_per_cu_d128();
 hipError_t launch_prefill_d256(const KernelArgs& a, int n, hipStream_t s);
@@ -28,6 +30,7 @@ hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, bool kv8, h
 hipError_t launch_merge_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
+hipError_t launch_stage_d256(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d256();
 int prefill_wgs_per_cu_d256();
 hipError_t launch_prefill_d512(const KernelArgs& a, int n, hipStream_t s);
@@ -35,6 +38,7 @@ hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, bool kv8, h
 hipError_t launch_merge_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d512(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               hipStream_t s);
+hipError_t launch_stage_d512(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d512();
 int prefill_wgs_per_cu_d512();
 
@@ -124,6 +128,19 @@ hipError_t launch_append(const LaunchArgs& l, const rpa_work_item* items, int n_
     case 128: return launch_append_d128(a, n_items, k_new, v_new, k_dst, v_dst, s);
     case 256: return launch_append_d256(a, n_items, k_new, v_new, k_dst, v_dst, s);
     case 512: return launch_append_d512(a, n_items, k_new, v_new, k_dst, v_dst, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_stage(const LaunchArgs& l, const int32_t* stage, int n_pages, void* k_dst, void* v_dst) {
+  if (n_pages <= 0) return hipSuccess;
+  const KernelArgs a = make_args(l, nullptr);
+  hipStream_t s = static_cast<hipStream_t>(l.stream);
+  switch (l.head_dim) {
+    case 64: return launch_stage_d64(a, stage, n_pages, k_dst, v_dst, s);
+    case 128: return launch_stage_d128(a, stage, n_pages, k_dst, v_dst, s);
+    case 256: return launch_stage_d256(a, stage, n_pages, k_dst, v_dst, s);
+    case 512: return launch_stage_d512(a, stage, n_pages, k_dst, v_dst, s);
     default: return hipErrorInvalidValue;
   }
 }

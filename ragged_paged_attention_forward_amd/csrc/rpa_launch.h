@@ -47,5 +47,9 @@ hipError_t launch_merge(const LaunchArgs& a, int n_groups);
 // slots of k_dst / v_dst, one workgroup per work item.
 hipError_t launch_append(const LaunchArgs& a, const rpa_work_item* items, int n_items, const void* k_new,
                          const void* v_new, void* k_dst, void* v_dst);
+// fp8 calls: converts the staged pages (stage: 3 ints per page, device) of
+// the fp8 pools a.k / a.v (page ids from a.page_table) to bf16 pages of
+// k_dst / v_dst, scaled by a.k_scales / a.v_scales.
+hipError_t launch_stage(const LaunchArgs& a, const int32_t* stage, int n_pages, void* k_dst, void* v_dst);
 
 }  // namespace rpa

@@ -198,6 +198,9 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
   out->decode.clear();
   out->groups.clear();
   out->num_partials = 0;
+  out->stage.clear();
+  out->stage_table.clear();
+  out->stage_pages = 0;
   out->visible_pairs = 0;
   out->total_q = num_seqs > 0 ? cu[num_seqs] : 0;
 
@@ -250,6 +253,26 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
         it.partial_base = 0;
         it.kind = 0;
         out->prefill.push_back(it);
+      }
+    }
+  }
+
+  // Every page of a sequence with prefill items gets a page of the bf16
+  // staging pool (pool pages in sequence order), and the pool's page table
+  // maps the sequence's pages to them.
+  if (p.stage_prefill && !out->prefill.empty()) {
+    out->stage_table.assign(static_cast<size_t>(num_seqs) * p.max_pages_per_seq, 0);
+    int32_t last = -1;
+    for (const auto& it : out->prefill) {
+      if (it.seq == last) continue;
+      last = it.seq;
+      const int32_t n = (kv[it.seq] + p.page_size - 1) / p.page_size;
+      for (int32_t lp = 0; lp < n; ++lp) {
+        out->stage.push_back(it.seq);
+        out->stage.push_back(lp);
+        out->stage.push_back(out->stage_pages);
+        out->stage_table[static_cast<size_t>(it.seq) * p.max_pages_per_seq + lp] = out->stage_pages;
+        ++out->stage_pages;
       }
     }
   }

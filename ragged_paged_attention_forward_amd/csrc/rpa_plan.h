@@ -32,6 +32,8 @@ struct PlanParams {
   int xcd_groups = 8;          // prefill order: workgroups b, b+X, b+2X, ... share a
                                // chiplet (and its L2); <= 1 keeps the plain order
   int xcd_run = 4;             // consecutive items dealt to one chiplet at a time
+  bool stage_prefill = false;  // fp8 calls: the pages of sequences with prefill items are
+                               // staged into a bf16 pool that the prefill kernel reads
 };
 
 struct Plan {
@@ -43,6 +45,12 @@ struct Plan {
   int decode_split_keys = 0;
   int64_t visible_pairs = 0;
   int64_t total_q = 0;
+  // Staging (stage_prefill): three ints per staged page (sequence, page of
+  // the sequence, page of the bf16 pool), and the bf16 pool's page table
+  // [num_seqs * max_pages_per_seq] (rows of staged sequences; 0 elsewhere).
+  std::vector<int32_t> stage;
+  std::vector<int32_t> stage_table;
+  int32_t stage_pages = 0;
 };
 
 // Checks the metadata of one call.  Returns RPA_OK or RPA_ERR_INVALID_ARG with *err set.

@@ -41,13 +41,16 @@ CASES = {
                                               0, seed=43),
     "mha_d64_window": lambda: wl.custom([(9, 200), (1, 65), (64, 64)], 4, 4, 64, 16, 33, seed=44),
     "g16_d128": lambda: wl.custom([(5, 90), (1, 400)], 16, 1, 128, 64, 0, seed=45),
+    "g32_d128_prefill_only": lambda: wl.custom([(5, 90), (33, 400), (1, 70)], 32, 1, 128, 64, 0, seed=47),
 }
 
 
-def run_fp8(f: wl.Fp8Inputs, attn=None):
+def run_fp8(f: wl.Fp8Inputs, attn=None, path=0):
     d = f.to("cuda")
     b = f.base
-    attn = attn or make_attn(b.workload)
+    if attn is None:
+        attn = make_attn(b.workload)
+        attn.set_option(R.RPA_OPT_PATH, path)
     out = attn.forward_fp8(d.base.q, d.k_pages, d.v_pages, d.k_scales, d.v_scales, d.base.page_table,
                            b.cu_q_lens, b.kv_lens, b.window, b.scale)
     torch.cuda.synchronize()
@@ -73,13 +76,17 @@ def test_e4m3_conversion_matches_torch_for_every_byte():
     assert torch.equal(g[~nan], w[~nan])
 
 
+@pytest.mark.parametrize("path", [0, 3], ids=["staged_prefill", "all_decode"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_fp8_parity(name):
+def test_fp8_parity(name, path):
+    """Path 0: prefill sequences through the staged bf16 pool and the prefill
+    kernel, the rest through the decode kernel; path 3: every token through
+    the decode kernel (G <= 16)."""
     w = CASES[name]()
-    print(f"fp8 parity {name}: seqs={w.num_seqs} T={w.total_q} d={w.head_dim} B={w.page_size} W={w.window}",
-          flush=True)
+    print(f"fp8 parity {name} path {path}: seqs={w.num_seqs} T={w.total_q} d={w.head_dim} B={w.page_size} "
+          f"W={w.window}", flush=True)
     f = wl.make_fp8_inputs(w, poison=True)
-    out = run_fp8(f)
+    out = run_fp8(f, path=path)
     compare(out, oracle_fp8(f), label=name)
 
 
@@ -92,6 +99,28 @@ def test_fp8_mixed_full_size_sampled(window):
     t_q = w.total_q
     rows = wl.sample_rows(t_q, 48, seed=window + 3, must=[0, 4095, 4096, t_q - 513, t_q - 1])
     compare(out, oracle_fp8(f, rows), rows=rows, label=f"mixed_w{window}")
+
+
+@pytest.mark.parametrize("name", ["swa_prefill", "global_prefill"])
+def test_fp8_prefill_full_size_sampled(name):
+    w = wl.by_name(name)
+    print(f"fp8 {name} full size: T={w.total_q} d={w.head_dim}", flush=True)
+    f = wl.make_fp8_inputs(w, poison=True)
+    out = run_fp8(f)
+    t_q = w.total_q
+    rows = wl.sample_rows(t_q, 24, seed=11, must=[0, 127, 128, 1023, 1024, t_q - 1])
+    compare(out, oracle_fp8(f, rows), rows=rows, label=name)
+
+
+def test_fp8_staging_kernel_is_timed():
+    w = CASES["mixed_small_w0"]()
+    f = wl.make_fp8_inputs(w, poison=True)
+    attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
+    run_fp8(f, attn)
+    assert len(attn.kernel_times(R.RPA_KERNEL_STAGE)) == 1
+    assert len(attn.kernel_times(R.RPA_KERNEL_PREFILL)) == 1
+    assert len(attn.kernel_times(R.RPA_KERNEL_DECODE)) == 1
 
 
 def test_fp8_is_bitwise_reproducible():
