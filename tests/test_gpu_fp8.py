@@ -146,3 +146,35 @@ def test_fp8_and_bf16_calls_alternate_on_one_context():
         torch.cuda.synchronize()
         compare(out16, ref16, label="bf16")
         compare(run_fp8(f, attn), ref8, label="fp8")
+
+
+def test_fp8_graph_of_layers_replays_bitwise():
+    """Four layers of one fp8 mixed step (their own pools and scales, one work
+    list and one staging pool) captured into one graph: every replay equals
+    the eager calls bit for bit."""
+    w = mixed_small(1024)
+    layers = 4
+    host = [wl.make_fp8_inputs(w, seed=w.seed + 7 * i, poison=True) for i in range(layers)]
+    dev = [h.to("cuda") for h in host]
+    cu, kv = host[0].base.cu_q_lens, host[0].base.kv_lens
+    attn = make_attn(w)
+
+    def call(d, out=None):
+        return attn.forward_fp8(d.base.q, d.k_pages, d.v_pages, d.k_scales, d.v_scales, d.base.page_table, cu, kv,
+                                w.window, w.scale, out=out)
+    eager = [call(d).clone() for d in dev]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(d.base.q) for d in dev]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for d, o in zip(dev, outs):
+            call(d, o)
+    for _ in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), f"layer {i}"
+    compare(eager[3], oracle_fp8(host[3]), label="layer 3")
