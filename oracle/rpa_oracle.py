@@ -237,6 +237,42 @@ def dequantize_kv(pages, scales) -> np.ndarray:
     return e4m3_value(codes) * sc
 
 
+def quantize_e4m3(x) -> np.ndarray:
+    """E4M3 byte of each float32 value: the finite code nearest to x, ties to
+    the code with an even last mantissa bit; values beyond +-448 take +-448
+    (the largest finite code), NaN gives 0x7f; the sign of zero is kept.
+    Done by search over the code values, not by bit manipulation."""
+    xs = np.asarray(x, dtype=np.float32).astype(np.float64).ravel()
+    pos_codes = np.arange(0x7F)                       # 0x00 .. 0x7e: 0 .. 448
+    pos_vals = e4m3_value(pos_codes)
+    out = np.empty(xs.shape, dtype=np.uint8)
+    for i, v in enumerate(xs):
+        if np.isnan(v):
+            out[i] = 0x7F
+            continue
+        a = min(abs(v), 448.0)
+        d = np.abs(pos_vals - a)
+        best = np.nonzero(d == d.min())[0]
+        c = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+        neg = v < 0 or (v == 0 and np.signbit(v))
+        out[i] = c | (0x80 if neg else 0)
+    return out.reshape(np.shape(x))
+
+
+def append_kv_fp8(k_pages, v_pages, k_scales, v_scales, page_table, cu_q_lens, kv_lens, k_new, v_new):
+    """The step's new keys and values written into an fp8 cache: each new
+    element is divided by its KV head's scale in float32 and stored as
+    ``quantize_e4m3`` of that quotient, at the slots ``append_kv`` uses.
+    k_pages / v_pages are uint8 arrays or tensors; returns new uint8 arrays."""
+    def codes(new, scales):
+        x = as_f64(new).astype(np.float32)
+        sc = as_f64(scales).astype(np.float32).reshape(1, -1, 1)
+        return quantize_e4m3(x / sc)
+    kp = k_pages.cpu().numpy() if hasattr(k_pages, "cpu") else np.asarray(k_pages)
+    vp = v_pages.cpu().numpy() if hasattr(v_pages, "cpu") else np.asarray(v_pages)
+    return append_kv(kp, vp, page_table, cu_q_lens, kv_lens, codes(k_new, k_scales), codes(v_new, v_scales))
+
+
 def forward_fp8_rows(q, k_pages, v_pages, k_scales, v_scales, page_table, cu_q_lens, kv_lens,
                      window: int, scale: float, token_rows: Optional[Iterable[int]] = None) -> np.ndarray:
     """Attention over an fp8 KV cache: the pools are dequantized (``dequantize_kv``)

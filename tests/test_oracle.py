@@ -643,3 +643,71 @@ def test_planted_fp8_mistake_is_caught(monkeypatch, name):
             return real_fwd(q, kp, vp, vs, ks, *a, **k)
         monkeypatch.setattr(ora, "forward_fp8_rows", swapped)
     assert not _fp8_pins_pass(), f"planted mistake not caught: {name}"
+
+
+# ---------------------------------------------------------------------------
+# fp8 KV append: the new rows quantized to E4M3 with the per-head scales
+# ---------------------------------------------------------------------------
+
+def _e4m3_midpoints():
+    v = ora.e4m3_value(np.arange(0x7F))
+    return ((v[:-1] + v[1:]) / 2).astype(np.float32)
+
+
+def test_quantize_e4m3_matches_torch_rounding():
+    """torch's float32 -> E4M3 conversion (round to nearest even) on random
+    values inside +-448 and on every midpoint between adjacent codes."""
+    rng = np.random.default_rng(5)
+    mids = _e4m3_midpoints()
+    x = np.concatenate([rng.standard_normal(4000) * 40, rng.standard_normal(2000) * 0.02, mids, -mids,
+                        [0.0, 1e-30, -1e-30]]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ora.quantize_e4m3(x), want)
+
+
+def test_quantize_e4m3_closed_forms():
+    q = ora.quantize_e4m3
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    np.testing.assert_array_equal(q(ora.e4m3_value(finite).astype(np.float32)), finite)   # every code round-trips
+    assert list(q(np.float32([2.0 ** -10, 1.5 * 2.0 ** -10, 3 * 2.0 ** -10]))) == [0x00, 0x01, 0x02]  # ties to even
+    assert list(q(np.float32([448.0, 460.0, 1e9, -1e9]))) == [0x7E, 0x7E, 0x7E, 0xFE]                  # saturation
+    assert q(np.float32([-0.0]))[0] == 0x80 and q(np.float32([np.nan]))[0] == 0x7F
+
+
+def test_append_fp8_round_trip_with_power_of_two_scales():
+    """New rows that are code value x scale with power-of-two scales divide
+    back exactly, so appending them restores the generated bytes."""
+    w = wl.custom([(3, 40), (1, 9), (12, 12), (0, 5)], 4, 2, 16, 8, seed=21)
+    f = wl.make_fp8_inputs(w)
+    b = f.base
+    ks = torch.tensor([0.25, 2.0], dtype=torch.float32)
+    vs = torch.tensor([0.0625, 1.0], dtype=torch.float32)
+    bsz = w.page_size
+    slots = [(t, int(fl) // bsz, int(fl) % bsz) for t, fl in enumerate(new_token_slots(b))]
+    kval, vval = ora.e4m3_value(f.k_pages.numpy()), ora.e4m3_value(f.v_pages.numpy())
+    t_q = b.q.shape[0]
+    k_new = np.zeros((t_q, 2, 16)); v_new = np.zeros((t_q, 2, 16))
+    for t, page, slot in slots:
+        k_new[t] = kval[page, slot] * ks.numpy()[:, None]
+        v_new[t] = vval[page, slot] * vs.numpy()[:, None]
+    k_stale, v_stale = f.k_pages.clone(), f.v_pages.clone()
+    for t, page, slot in slots:
+        k_stale[page, slot] = 0x7F
+        v_stale[page, slot] = 0x7F
+    k_out, v_out = ora.append_kv_fp8(k_stale, v_stale, ks, vs, b.page_table, b.cu_q_lens, b.kv_lens,
+                                     torch.from_numpy(k_new).to(torch.bfloat16), torch.from_numpy(v_new).to(torch.bfloat16))
+    np.testing.assert_array_equal(k_out, f.k_pages.numpy())
+    np.testing.assert_array_equal(v_out, f.v_pages.numpy())
+
+
+def test_planted_quantize_ties_away_is_caught(monkeypatch):
+    real = ora.quantize_e4m3
+
+    def away(x):
+        x = np.asarray(x, dtype=np.float32)
+        return real(np.nextafter(x, np.where(x >= 0, np.float32(np.inf), np.float32(-np.inf))))
+    monkeypatch.setattr(ora, "quantize_e4m3", away)
+    with pytest.raises(AssertionError):
+        test_quantize_e4m3_matches_torch_rounding()
