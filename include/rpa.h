@@ -173,6 +173,22 @@ int rpa_forward_fp8(rpa_ctx* ctx, const void* q, const void* k_pages, const void
                     const int32_t* kv_lens, int32_t num_seqs, int32_t window, float scale, void* out,
                     void* stream);
 
+/*
+ * rpa_forward_fp8_append -- rpa_forward_append for an fp8 cache: the step's
+ * new keys and values (bf16, as for rpa_forward_append) are quantized into
+ * their page slots, then the attention of rpa_forward_fp8 runs, in one call
+ * (the pages' kernel writes the new tokens' K/V within the attention call:
+ * "TPU Deep Dive", chapter 8).  Each new element x of KV head g is stored
+ * as the E4M3 byte nearest to x / scale[g] (the division in float32; ties to
+ * an even last mantissa bit; magnitudes beyond 448 stored as +-448; NaN as
+ * 0x7f).  Arguments as for rpa_forward_fp8 plus k_new / v_new; errors as for
+ * rpa_forward_append and rpa_forward_fp8.
+ */
+int rpa_forward_fp8_append(rpa_ctx* ctx, const void* q, const void* k_new, const void* v_new, void* k_pages,
+                           void* v_pages, const float* k_scales, const float* v_scales, const int32_t* page_table,
+                           const int32_t* cu_q_lens, const int32_t* kv_lens, int32_t num_seqs, int32_t window,
+                           float scale, void* out, void* stream);
+
 /* rpa_destroy -- free a context (NULL-safe).  The caller must first make sure
  * no work enqueued with it is still running. */
 void rpa_destroy(rpa_ctx* ctx);

@@ -243,6 +243,31 @@ class RaggedPagedAttention:
                     float(scale), out.data_ptr(), self._stream_ptr))
         return out
 
+    def forward_fp8_append(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                           k_pages: torch.Tensor, v_pages: torch.Tensor, k_scales: torch.Tensor,
+                           v_scales: torch.Tensor, page_table: torch.Tensor, cu_q_lens, kv_lens, window: int = 0,
+                           scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """Quantize the step's new K/V rows (bf16 ``[T, Hkv, D]``) into their
+        slots of the fp8 pools, then the attention of ``forward_fp8``."""
+        if scale is None:
+            scale = float(self.head_dim) ** -0.5
+        cu, kv, n, out = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream,
+                                       kv_dtype=torch.uint8)
+        shape = (q.shape[0], self.num_kv_heads, self.head_dim)
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor of shape {list(shape)}")
+        for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+            if (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()
+                    or tuple(t.shape) != (self.num_kv_heads,)):
+                raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape [{self.num_kv_heads}]")
+        self._call(self._lib.rpa_forward_fp8_append, "rpa_forward_fp8_append", q.device,
+                   (self._ctx, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pages.data_ptr(),
+                    v_pages.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(), page_table.data_ptr(),
+                    cu.ctypes.data, kv.ctypes.data, n, int(window), float(scale), out.data_ptr(), self._stream_ptr))
+        return out
+
     __call__ = forward
 
 

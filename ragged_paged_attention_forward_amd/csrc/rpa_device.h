@@ -127,6 +127,42 @@ RPA_DEV u32x4 e4m3x8_to_bf16x8(const u32x2& w) {
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true))};
 }
 
+// float -> OCP E4M3 byte: the finite code nearest to x, ties to an even last
+// mantissa bit; |x| is clamped to 448 (the largest finite code) first, NaN
+// gives 0x7f, the sign of zero is kept.  Every step is exact: the exponent
+// comes from the float's bits, the mantissa grid is a power-of-two scaling,
+// and rintf rounds half to even.
+RPA_DEV uint32_t f32_to_e4m3(float x) {
+  const uint32_t bits = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  if ((bits & 0x7fffffffu) > 0x7f800000u) return 0x7fu;
+  const float a = fminf(__builtin_fabsf(x), 448.f);
+  if (a < 0.015625f) {   // below 2^-6: multiples of 2^-9; q = 8 is the smallest normal code 0x08
+    return sign | static_cast<uint32_t>(rintf(a * 512.f));
+  }
+  const int e = static_cast<int>((__builtin_bit_cast(uint32_t, a) >> 23) & 0xffu) - 127;   // -6 .. 8
+  uint32_t q = static_cast<uint32_t>(rintf(ldexpf(a, 3 - e)));                            // 8 .. 16
+  int biased = e + 7;
+  if (q == 16) {
+    q = 8;
+    ++biased;
+  }
+  return sign | (static_cast<uint32_t>(biased) << 3) | (q - 8);
+}
+
+// Eight bf16 (a 16-byte load) divided by `sc` in float32 and quantized to
+// eight E4M3 bytes, element i in byte i.
+RPA_DEV u32x2 bf16x8_to_e4m3x8(const u32x4& w, float sc) {
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = f32_to_e4m3(__builtin_bit_cast(float, w[j] << 16) / sc);
+    const uint32_t hi = f32_to_e4m3(__builtin_bit_cast(float, w[j] & 0xffff0000u) / sc);
+    out[j / 2] |= (lo | (hi << 8)) << (16 * (j % 2));
+  }
+  return u32x2{out[0], out[1]};
+}
+
 // Wave-uniform load through the constant address space, so it becomes a
 // scalar load that does not wait behind the vector loads in flight.
 typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
@@ -1244,7 +1280,9 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 // ---------------------------------------------------------------------------
 constexpr int kAppendThreads = 256;
 
-template <int D>
+// KV8: the pools hold E4M3 bytes; each new element is divided by its KV
+// head's scale and quantized (f32_to_e4m3), 8 bytes written per 16 read.
+template <int D, bool KV8>
 __global__ void __launch_bounds__(kAppendThreads)
 rpa_append_kernel(const rpa_work_item* __restrict__ items, const int32_t* __restrict__ page_table,
                   const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -1263,8 +1301,17 @@ rpa_append_kernel(const rpa_work_item* __restrict__ items, const int32_t* __rest
     const int64_t page = pt_row[pos / ps];
     const int64_t src = (static_cast<int64_t>(it.q_start + r) * hkv + it.kv_head) * D + c * 8;
     const int64_t dst = ((page * ps + pos % ps) * hkv + it.kv_head) * D + c * 8;
-    *reinterpret_cast<u32x4*>(k_dst + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
-    *reinterpret_cast<u32x4*>(v_dst + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+    if constexpr (KV8) {
+      const float ks = args.k_scales[it.kv_head];
+      const float vs = args.v_scales[it.kv_head];
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(k_dst) + dst) =
+          bf16x8_to_e4m3x8(*reinterpret_cast<const u32x4*>(k_new + src), ks);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(v_dst) + dst) =
+          bf16x8_to_e4m3x8(*reinterpret_cast<const u32x4*>(v_new + src), vs);
+    } else {
+      *reinterpret_cast<u32x4*>(k_dst + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
+      *reinterpret_cast<u32x4*>(v_dst + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+    }
   }
 }
 
@@ -1373,10 +1420,15 @@ static hipError_t launch_decode_t(const KernelArgs& a, int n_items, int waves, b
 
 template <int D>
 static hipError_t launch_append_t(const KernelArgs& a, int n_items, const void* k_new, const void* v_new,
-                                  void* k_dst, void* v_dst, hipStream_t stream) {
-  hipLaunchKernelGGL((rpa_append_kernel<D>), dim3(n_items), dim3(kAppendThreads), 0, stream, a.items, a.page_table,
-                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                     static_cast<uint16_t*>(k_dst), static_cast<uint16_t*>(v_dst), a);
+                                  void* k_dst, void* v_dst, bool kv8, hipStream_t stream) {
+  if (kv8)
+    hipLaunchKernelGGL((rpa_append_kernel<D, true>), dim3(n_items), dim3(kAppendThreads), 0, stream, a.items,
+                       a.page_table, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       static_cast<uint16_t*>(k_dst), static_cast<uint16_t*>(v_dst), a);
+  else
+    hipLaunchKernelGGL((rpa_append_kernel<D, false>), dim3(n_items), dim3(kAppendThreads), 0, stream, a.items,
+                       a.page_table, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       static_cast<uint16_t*>(k_dst), static_cast<uint16_t*>(v_dst), a);
   return hipGetLastError();
 }
 
@@ -1428,8 +1480,8 @@ constexpr int prefill_wgs_per_cu() {
     return launch_merge_t<D>(a, n, s);                                                      \
   }                                                                                         \
   hipError_t launch_append_d##D(const KernelArgs& a, int n, const void* kn, const void* vn, \
-                                void* kd, void* vd, hipStream_t s) {                        \
-    return launch_append_t<D>(a, n, kn, vn, kd, vd, s);                                     \
+                                void* kd, void* vd, bool kv8, hipStream_t s) {              \
+    return launch_append_t<D>(a, n, kn, vn, kd, vd, kv8, s);                                \
   }                                                                                         \
   hipError_t launch_stage_d##D(const KernelArgs& a, const int32_t* st, int n, void* kd,     \
                                void* vd, hipStream_t s) {                                   \

@@ -13,7 +13,7 @@ hipError_t launch_prefill_d64(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
 hipError_t launch_merge_d64(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
-                              hipStream_t s);
+                              bool kv8, hipStream_t s);
 hipError_t launch_stage_d64(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d64();
 int prefill_wgs_per_cu_d64();
@@ -21,7 +21,7 @@ hipError_t launch_prefill_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
 hipError_t launch_merge_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
-                              hipStream_t s);
+                              bool kv8, hipStream_t s);
 hipError_t launch_stage_d128(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d128();
 int prefill_wgs_per_cu_d128();
@@ -29,7 +29,7 @@ hipError_t launch_prefill_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
 hipError_t launch_merge_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
-                              hipStream_t s);
+                              bool kv8, hipStream_t s);
 hipError_t launch_stage_d256(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d256();
 int prefill_wgs_per_cu_d256();
@@ -37,7 +37,7 @@ hipError_t launch_prefill_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
 hipError_t launch_merge_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d512(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
-                              hipStream_t s);
+                              bool kv8, hipStream_t s);
 hipError_t launch_stage_d512(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d512();
 int prefill_wgs_per_cu_d512();
@@ -124,10 +124,10 @@ hipError_t launch_append(const LaunchArgs& l, const rpa_work_item* items, int n_
   const KernelArgs a = make_args(l, items);
   hipStream_t s = static_cast<hipStream_t>(l.stream);
   switch (l.head_dim) {
-    case 64: return launch_append_d64(a, n_items, k_new, v_new, k_dst, v_dst, s);
-    case 128: return launch_append_d128(a, n_items, k_new, v_new, k_dst, v_dst, s);
-    case 256: return launch_append_d256(a, n_items, k_new, v_new, k_dst, v_dst, s);
-    case 512: return launch_append_d512(a, n_items, k_new, v_new, k_dst, v_dst, s);
+    case 64: return launch_append_d64(a, n_items, k_new, v_new, k_dst, v_dst, l.kv_fp8 != 0, s);
+    case 128: return launch_append_d128(a, n_items, k_new, v_new, k_dst, v_dst, l.kv_fp8 != 0, s);
+    case 256: return launch_append_d256(a, n_items, k_new, v_new, k_dst, v_dst, l.kv_fp8 != 0, s);
+    case 512: return launch_append_d512(a, n_items, k_new, v_new, k_dst, v_dst, l.kv_fp8 != 0, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -254,3 +254,24 @@ def test_probe_e4m3_rejects_bad_arguments():
     assert lib.rpa_probe_e4m3(addr, None, 64, None) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_probe_e4m3(addr, addr, 0, None) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_probe_e4m3(addr, addr, 12, None) == _lib.RPA_ERR_INVALID_ARG
+
+
+def test_forward_fp8_append_rejects_bad_arguments_before_launch():
+    lib, st, ctx = _ctx()
+    cu_a, cu_p = i32([0, 2])
+    kv_a, kv_p = i32([7])
+    other = ctypes.c_void_p(0x900000)
+    # q, k_new, v_new, k_pages, v_pages, k_scales, v_scales, page_table, out
+    for args in ((FAKE, None, FAKE, FAKE, other, FAKE, FAKE, FAKE, other),
+                 (FAKE, FAKE, None, FAKE, other, FAKE, FAKE, FAKE, other),
+                 (FAKE, FAKE, FAKE, FAKE, other, None, FAKE, FAKE, other),
+                 (FAKE, FAKE, FAKE, FAKE, other, FAKE, None, FAKE, other),
+                 (None, FAKE, FAKE, FAKE, other, FAKE, FAKE, FAKE, other),
+                 (FAKE, FAKE, FAKE, FAKE, other, FAKE, FAKE, None, other)):
+        q, kn, vn, kp, vp, ks, vs, pt, out = args
+        st = lib.rpa_forward_fp8_append(ctx, q, kn, vn, kp, vp, ks, vs, pt, cu_p, kv_p, 1, 0, 1.0, out, None)
+        assert st == _lib.RPA_ERR_INVALID_ARG, args
+    st = lib.rpa_forward_fp8_append(ctx, FAKE, FAKE, FAKE, other, other, FAKE, FAKE, FAKE, cu_p, kv_p, 1, 0, 1.0,
+                                    ctypes.c_void_p(0x7000000), None)
+    assert st == _lib.RPA_ERR_INVALID_ARG and "same buffer" in lib.rpa_last_error(ctx).decode()
+    lib.rpa_destroy(ctx)

@@ -178,3 +178,40 @@ def test_fp8_graph_of_layers_replays_bitwise():
         for i, (o, e) in enumerate(zip(outs, eager)):
             assert torch.equal(o, e), f"layer {i}"
     compare(eager[3], oracle_fp8(host[3]), label="layer 3")
+
+
+APPEND_CASES = ["tiny", "decode", "decode_pages16", "mixed_small_w0", "gqa4_d128_chunks", "with_empty_sequences",
+                "mha_d64_window", "g32_d128_prefill_only"]
+
+
+@pytest.mark.parametrize("name", APPEND_CASES)
+def test_fp8_append_then_attend(name):
+    """rpa_forward_fp8_append: the new tokens' bf16 K/V rows (the bf16 pools'
+    rows at their slots) are quantized into slots that start as the E4M3 NaN
+    byte; every byte of both pools must equal the oracle's fp8 append, and the
+    attention that follows must match the oracle on the oracle's pools."""
+    from append_common import new_token_slots
+    w = CASES[name]()
+    print(f"fp8 append {name}", flush=True)
+    f = wl.make_fp8_inputs(w, poison=True)
+    b = f.base
+    flat = torch.from_numpy(new_token_slots(b))
+    hd = (w.num_kv_heads, w.head_dim)
+    k_new = b.k_pages.reshape(-1, *hd)[flat].contiguous()
+    v_new = b.v_pages.reshape(-1, *hd)[flat].contiguous()
+    k_stale, v_stale = f.k_pages.clone(), f.v_pages.clone()
+    k_stale.reshape(-1, *hd)[flat] = wl.NAN_E4M3
+    v_stale.reshape(-1, *hd)[flat] = wl.NAN_E4M3
+    want_k, want_v = ora.append_kv_fp8(k_stale, v_stale, f.k_scales, f.v_scales, b.page_table, b.cu_q_lens,
+                                       b.kv_lens, k_new, v_new)
+    d = b.to("cuda")
+    kp, vp = k_stale.cuda(), v_stale.cuda()
+    attn = make_attn(w)
+    out = attn.forward_fp8_append(d.q, k_new.cuda(), v_new.cuda(), kp, vp, f.k_scales.cuda(), f.v_scales.cuda(),
+                                  d.page_table, b.cu_q_lens, b.kv_lens, w.window, w.scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kp.cpu().numpy(), want_k)
+    np.testing.assert_array_equal(vp.cpu().numpy(), want_v)
+    ref = ora.forward_fp8_rows(b.q, want_k, want_v, f.k_scales, f.v_scales, b.page_table, b.cu_q_lens, b.kv_lens,
+                               w.window, w.scale)
+    compare(out, ref, label=name)
