@@ -21,8 +21,9 @@ new K/V rows are written into their pages (the same bytes each step) before the
 attention kernels, and the append kernel is timed beside them.
 
 ``--kv fp8`` holds the K/V pools as OCP FP8 E4M3 bytes with per-KV-head scales
-(drawn from the same bf16 values) and calls ``rpa_forward_fp8``; the K/V bytes
-of the roofline are then one byte per element.
+(drawn from the same bf16 values) and calls ``rpa_forward_fp8`` (with
+``--append``: ``rpa_forward_fp8_append``, which quantizes the new rows); the
+K/V bytes of the roofline are then one byte per element.
 
 Prints ONE JSON line.
 
@@ -115,8 +116,8 @@ def kernel_work(w, items, merge_kernel=True, kv_elem_bytes=2):
     out["merge"] = {"flops": 0, "bytes": int(metrics.qo_bytes(seqs, w.num_q_heads, w.head_dim) // 2),
                     "seqs": len(seqs)}
     # the KV append reads the step's new K and V rows and writes them into their pages
-    new_rows = w.total_q * w.num_kv_heads * w.head_dim * 2 * 2
-    out["append"] = {"flops": 0, "bytes": int(2 * new_rows), "seqs": w.num_seqs}
+    new_elems = w.total_q * w.num_kv_heads * w.head_dim * 2   # K and V
+    out["append"] = {"flops": 0, "bytes": int(new_elems * (2 + kv_elem_bytes)), "seqs": w.num_seqs}
     # fp8 staging: the prefill sequences' pages read as bytes, written as bf16
     pre = [w.seqs[s] for s, k in kind_of.items() if k == "prefill"]
     staged = sum(-(-kvl // w.page_size) for _, kvl in pre) * w.page_size * w.num_kv_heads * w.head_dim * 2
@@ -315,6 +316,7 @@ def run(args):
     if fp8:
         host8 = wl.make_fp8_inputs(w)
         host = host8.base
+        k16, v16 = host.k_pages, host.v_pages                      # bf16 rows the fp8 append writes
         host.k_pages, host.v_pages = host8.k_pages, host8.v_pages   # the pools the steps read
     else:
         host = wl.make_inputs(w)
@@ -349,12 +351,22 @@ def run(args):
         # step writes the same bytes) through rpa_forward_append
         slots = torch.from_numpy(new_row_slots(w, cu, kv, host.page_table.numpy())).to(dev)
         news = []
+        flat = (w.num_kv_heads, w.head_dim)
         for d, _ in replicas:
-            flat = (w.num_kv_heads, w.head_dim)
-            news.append((d.k_pages.view(-1, *flat)[slots].contiguous(), d.v_pages.view(-1, *flat)[slots].contiguous()))
+            if fp8:   # the bf16 rows whose quantized bytes the pools already hold
+                news.append((k16.reshape(-1, *flat)[slots.cpu()].contiguous().to(dev),
+                             v16.reshape(-1, *flat)[slots.cpu()].contiguous().to(dev)))
+            else:
+                news.append((d.k_pages.view(-1, *flat)[slots].contiguous(),
+                             d.v_pages.view(-1, *flat)[slots].contiguous()))
 
     def step(i):
         d, out = replicas[i % reps]
+        if args.append and fp8:
+            kn, vn = news[i % reps]
+            attn.forward_fp8_append(d.q, kn, vn, d.k_pages, d.v_pages, k_scales, v_scales, d.page_table, cu, kv,
+                                    w.window, w.scale, out=out, stream=stream)
+            return
         if args.append:
             kn, vn = news[i % reps]
             attn.forward_append(d.q, kn, vn, d.k_pages, d.v_pages, d.page_table, cu, kv, w.window, w.scale,
@@ -573,9 +585,6 @@ def main(argv=None):
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(how it would shard is described in the design notes); run with --gpus 1.",
               file=sys.stderr)
-        return 2
-    if args.kv == "fp8" and args.append:
-        print("--append writes bf16 rows; it does not combine with --kv fp8", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
