@@ -45,7 +45,9 @@ here as the pages leave it open: every stored K or V element is one byte in
 the OCP FP8 E4M3 format, and each KV head has one float32 scale for K and one
 for V; the value an element stands for is its E4M3 value times its head's
 scale.  ``forward_fp8_rows`` dequantizes exactly that way and then computes
-the same attention as ``forward_rows``.
+the same attention as ``forward_rows``.  New tokens enter such a cache as
+``quantize_e4m3`` of their value divided by the head's scale in float32 (the
+nearest code, ties to even, saturating at 448): ``append_kv_fp8``.
 
 Every function below is pinned by ``tests/test_oracle.py`` (brute force, a
 library routine, closed forms, invariants, and for ``append_kv`` a hand-worked
