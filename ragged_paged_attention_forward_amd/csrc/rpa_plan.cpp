@@ -257,21 +257,24 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
     }
   }
 
-  // Every page of a sequence with prefill items gets a page of the bf16
+  // Every page that the prefill items of a sequence read (from the page of
+  // their first key to the sequence's last page) gets a page of the bf16
   // staging pool (pool pages in sequence order), and the pool's page table
-  // maps the sequence's pages to them.
+  // maps the sequence's pages to them.  A sequence's items are consecutive
+  // here (before splitting and sorting).
   if (p.stage_prefill && !out->prefill.empty()) {
     out->stage_table.assign(static_cast<size_t>(num_seqs) * p.max_pages_per_seq, 0);
-    int32_t last = -1;
-    for (const auto& it : out->prefill) {
-      if (it.seq == last) continue;
-      last = it.seq;
-      const int32_t n = (kv[it.seq] + p.page_size - 1) / p.page_size;
-      for (int32_t lp = 0; lp < n; ++lp) {
-        out->stage.push_back(it.seq);
+    for (size_t i = 0; i < out->prefill.size();) {
+      const int32_t seq = out->prefill[i].seq;
+      int32_t first_key = out->prefill[i].kv_begin;
+      for (; i < out->prefill.size() && out->prefill[i].seq == seq; ++i)
+        first_key = std::min(first_key, out->prefill[i].kv_begin);
+      const int32_t n = (kv[seq] + p.page_size - 1) / p.page_size;
+      for (int32_t lp = first_key / p.page_size; lp < n; ++lp) {
+        out->stage.push_back(seq);
         out->stage.push_back(lp);
         out->stage.push_back(out->stage_pages);
-        out->stage_table[static_cast<size_t>(it.seq) * p.max_pages_per_seq + lp] = out->stage_pages;
+        out->stage_table[static_cast<size_t>(seq) * p.max_pages_per_seq + lp] = out->stage_pages;
         ++out->stage_pages;
       }
     }
