@@ -1,0 +1,73 @@
+// Invariants of the fp8 staging list built by the host planner, on random
+// ragged batches (run by tests/test_planner.py): every page that a prefill
+// item reads has a staged pool page that maps back to that (sequence, page);
+// pool pages are numbered 0.. in list order; no staging without prefill
+// items.  Exit status 0 when every check holds.
+#include <algorithm>
+#include <cstdio>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "rpa_plan.h"
+
+int main() {
+  std::mt19937 rng(1);
+  int bad = 0, planned = 0;
+  for (int trial = 0; trial < 400; ++trial) {
+    rpa::PlanParams p;
+    const int group = 1 << (rng() % 6);
+    p.num_kv_heads = 1 + rng() % 3;
+    p.num_q_heads = group * p.num_kv_heads;
+    p.head_dim = 256;
+    p.page_size = std::vector<int>{16, 32, 64, 128}[rng() % 4];
+    const int num_seqs = 1 + rng() % 20;
+    p.max_num_seqs = num_seqs;
+    p.prefill_rows = 256;
+    p.stage_prefill = true;
+    p.path_mode = rng() % 4;
+    std::vector<int32_t> cu(num_seqs + 1, 0), kv(num_seqs);
+    int max_pages = 1;
+    for (int s = 0; s < num_seqs; ++s) {
+      const int q = (rng() % 3 == 0) ? 1 + rng() % 300 : rng() % 2;
+      const int k = q + rng() % 700;
+      cu[s + 1] = cu[s] + q;
+      kv[s] = k;
+      max_pages = std::max(max_pages, (k + p.page_size - 1) / p.page_size);
+    }
+    p.max_pages_per_seq = max_pages;
+    p.max_q_tokens = cu[num_seqs];
+    const int window = (rng() % 2) * (1 + rng() % 200);
+    std::string err;
+    if (rpa::validate_metadata(p, cu.data(), kv.data(), num_seqs, window, &err) != RPA_OK) {
+      std::printf("metadata rejected: %s\n", err.c_str());
+      ++bad;
+      continue;
+    }
+    rpa::Plan plan;
+    rpa::build_plan(p, cu.data(), kv.data(), num_seqs, window, &plan);
+    ++planned;
+    if (plan.prefill.empty()) {
+      bad += plan.stage_pages != 0;
+      continue;
+    }
+    bad += static_cast<int>(plan.stage.size()) != 3 * plan.stage_pages;
+    bad += plan.stage_table.size() != static_cast<size_t>(num_seqs) * max_pages;
+    for (int b = 0; b < plan.stage_pages; ++b) {
+      const int s = plan.stage[3 * b], lp = plan.stage[3 * b + 1], slot = plan.stage[3 * b + 2];
+      const bool ok = s >= 0 && s < num_seqs && lp >= 0 && lp < (kv[s] + p.page_size - 1) / p.page_size &&
+                      slot == b && plan.stage_table[static_cast<size_t>(s) * max_pages + lp] == slot;
+      bad += !ok;
+    }
+    for (const auto& it : plan.prefill) {
+      for (int lp = it.kv_begin / p.page_size; lp <= (it.kv_end - 1) / p.page_size; ++lp) {
+        const int slot = plan.stage_table[static_cast<size_t>(it.seq) * max_pages + lp];
+        const bool ok = slot >= 0 && slot < plan.stage_pages && plan.stage[3 * slot] == it.seq &&
+                        plan.stage[3 * slot + 1] == lp;
+        bad += !ok;
+      }
+    }
+  }
+  std::printf("plans %d, failed checks %d\n", planned, bad);
+  return bad == 0 ? 0 : 1;
+}

@@ -275,3 +275,23 @@ def test_plan_is_deterministic():
     a = plan_for(w)
     b = plan_for(w)
     assert a[2] == b[2] and a[3] == b[3]
+
+
+def test_fp8_staging_list_covers_every_page_prefill_items_read(tmp_path):
+    """The planner's fp8 staging list (internal, not exposed through the C
+    ABI) checked by a small C++ program on random ragged batches, built here
+    with g++ against the planner source (address and UB sanitizers on)."""
+    import os
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not found")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    csrc = os.path.join(root, "ragged_paged_attention_forward_amd", "csrc")
+    exe = str(tmp_path / "plan_stage_check")
+    subprocess.run([gxx, "-std=c++17", "-O1", "-fsanitize=address,undefined", "-I", os.path.join(root, "include"),
+                    "-I", csrc, os.path.join(root, "tests", "plan_stage_check.cpp"),
+                    os.path.join(csrc, "rpa_plan.cpp"), "-o", exe], check=True)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
