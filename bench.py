@@ -25,6 +25,13 @@ attention kernels, and the append kernel is timed beside them.
 ``--append``: ``rpa_forward_fp8_append``, which quantizes the new rows); the
 K/V bytes of the roofline are then one byte per element.
 
+By default the same run also times the other workloads of the metric (the
+8192-token window-1024 and global prefills, the tiny prefill and the two mixed
+chunked-prefill steps) and reports each under ``configs``, with its dominant
+kernel's duration and roofline fraction (``--configs ''`` skips them).
+``--stack`` adds one step of a 5 window-1024 : 1 global layer stack, timed
+eagerly and as one captured HIP graph.
+
 Prints ONE JSON line.
 
 Counter runs (HBM traffic of the dominant kernel):
@@ -146,7 +153,8 @@ def cpu_baseline(w, budget_s: float):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
-    cores = min(len(os.sched_getaffinity(0)), max(1, blas_threads))
+    host_cores = len(os.sched_getaffinity(0))
+    cores = min(host_cores, max(1, blas_threads))   # threads the oracle's BLAS products use
     inp = wl.make_inputs(w)
     cu = inp.cu_q_lens.tolist()
     t_total = cu[-1]
@@ -175,7 +183,8 @@ def cpu_baseline(w, budget_s: float):
             if time.perf_counter() - t0 > budget_s:
                 break
     el = time.perf_counter() - t0
-    return {"value": round(done_tokens / el, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(done_tokens / el, 2), "unit": "tokens/s", "cores": int(cores),
+            "host_cores": int(host_cores), "blas_threads": int(blas_threads), "kind": "oracle",
             "sample": f"{done_tokens} query tokens of a {t_total}-token step ({n_seq} sequence "
                       f"visits over {passes} pass(es), up to {rows_per_call} rows each, fp64 numpy) "
                       f"in {el:.1f} s",
@@ -300,18 +309,13 @@ def graph_layers(torch, attn, replicas, w, cu, kv, layers: int, stream):
             "replays": reps}
 
 
-def run(args):
-    import torch
+def measure(args, workload: str, torch, R, dev, graph_layers_n: int = 0):
+    """Time one workload: K wall-clock steps (``value``, ``ms_per_step``), then
+    the event-timed pass for each kernel's duration and the roofline of the
+    dominant kernel.  Returns the result dict (without the CPU baseline)."""
     import rpa_workloads as wl
-    import ragged_paged_attention_forward_amd as R
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    w = wl.by_name(args.workload)
+    w = wl.by_name(workload)
     fp8 = args.kv == "fp8"
     if fp8:
         host8 = wl.make_fp8_inputs(w)
@@ -437,7 +441,7 @@ def run(args):
     mp["frac"] = round(achieved / mp["value"], 4)
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "measured_peak": mp,
-                "traffic": load_traffic(args.workload, KERNEL_NAMES[dom], args.kv),
+                "traffic": load_traffic(workload, KERNEL_NAMES[dom], args.kv),
                 "kernel": KERNEL_NAMES[dom], "kernel_ms_mean": k_ms,
                 "algorithmic_bytes": kw["bytes"], "algorithmic_flops": kw["flops"],
                 "source_sha256_16": kernel_source_hash()}
@@ -467,7 +471,7 @@ def run(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled page tables)",
-        "config": {"workload": args.workload, "description": w.description, "seed": w.seed,
+        "config": {"workload": workload, "description": w.description, "seed": w.seed,
                    "num_seqs": w.num_seqs, "q_tokens": t_q, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "window": w.window, "replicas": reps, "append_kv": bool(args.append),
@@ -483,14 +487,99 @@ def run(args):
         "plan": info,
         "roofline": roofline,
     }
-    if args.graph_layers > 0:
-        res["graph"] = graph_layers(torch, attn, replicas, w, cu, kv, args.graph_layers, stream)
+    if graph_layers_n > 0:
+        res["graph"] = graph_layers(torch, attn, replicas, w, cu, kv, graph_layers_n, stream)
+    if args.stack:
+        res["stack"] = layer_stack(torch, attn, replicas, w, cu, kv, stream)
+    attn.close()
+    del replicas
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def config_summary(res):
+    """The fields of one workload's result that the `configs` record keeps."""
+    r = res["roofline"]
+    return {"workload": res["config"]["workload"], "description": res["config"]["description"],
+            "value": res["value"], "unit": res["unit"], "ms_per_step": res["ms_per_step"],
+            "kernels": {k: {"mean_ms": v["mean_ms"], "p50_ms": v["p50_ms"]} for k, v in res["kernels"].items()},
+            "roofline": {k: r[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel",
+                                          "kernel_ms_mean", "algorithmic_bytes", "algorithmic_flops")},
+            "measured_peak": {"value": r["measured_peak"]["value"], "unit": r["measured_peak"]["unit"],
+                              "frac": r["measured_peak"]["frac"]},
+            "step_tflops": res["step_tflops"], "step_kv_gbps": res["step_kv_gbps"],
+            "enqueue_ms_per_step": res["enqueue_ms_per_step"], "plan": res["plan"]}
+
+
+def layer_stack(torch, attn, replicas, w, cu, kv, stream, pattern=(1024, 1024, 1024, 1024, 1024, 0)):
+    """One step of a layer stack of five sliding-window layers and one global
+    layer (the pages' 5:1 pattern) on the workload's metadata: six calls, each
+    on its own input replica, two work lists (one per window).  Timed as eager
+    calls and as one captured HIP graph replayed; wall time per step."""
+    n = len(pattern)
+    outs = [torch.empty_like(replicas[i % len(replicas)][0].q) for i in range(n)]
+
+    def calls():
+        for i, win in enumerate(pattern):
+            d = replicas[i % len(replicas)][0]
+            attn.forward(d.q, d.k_pages, d.v_pages, d.page_table, cu, kv, win, w.scale, out=outs[i])
+
+    calls()                      # both work lists are on the device before the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    reps = 50
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps * 1e3
+
+    def eager():
+        with torch.cuda.stream(stream):
+            calls()
+    eager_ms = timed(eager)
+    graph_ms = timed(g.replay)
+    attn.release_captured()
+    return {"pattern": list(pattern), "eager_ms_per_step": round(eager_ms, 6),
+            "graph_ms_per_step": round(graph_ms, 6), "replays": reps,
+            "tokens_per_s_graph": round(w.total_q * n / (graph_ms * 1e-3), 1)}
+
+
+def run(args):
+    import torch
+    import ragged_paged_attention_forward_amd as R
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    res = measure(args, args.workload, torch, R, dev, args.graph_layers)
+    if args.configs:
+        # the other workloads of the metric (the prefill half: TFLOP/s of the
+        # 8192-token prefills; the mixed steps), each timed the same way
+        others = [x for x in (args.configs.split(",") if args.configs != "all" else WORKLOADS)
+                  if x != args.workload]
+        res["configs"] = {}
+        for name in others:
+            print(f"# measuring {name}", file=sys.stderr, flush=True)
+            res["configs"][name] = config_summary(measure(args, name, torch, R, dev))
     if args.copy_calibration:
         copy_calibration(torch, dev)
-    if not args.no_cpu_baseline and not fp8:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    if not args.no_cpu_baseline and args.kv != "fp8":
+        import rpa_workloads as wl
+        res["cpu_baseline"] = cpu_baseline(wl.by_name(args.workload), args.cpu_budget)
     print(json.dumps(res), flush=True)
-    attn.close()
     return 0
 
 
@@ -571,6 +660,12 @@ def main(argv=None):
                     help="K/V pool format: bf16, or OCP FP8 E4M3 with per-KV-head scales (rpa_forward_fp8)")
     ap.add_argument("--append", action="store_true",
                     help="each step also writes its new K/V rows into the pages (rpa_forward_append)")
+    ap.add_argument("--configs", default="all",
+                    help="other workloads timed in the same run and reported under `configs`: "
+                         "'all' (default), a comma-separated list, or '' for none")
+    ap.add_argument("--stack", action="store_true",
+                    help="also time one step of a 5 window-1024 : 1 global layer stack, eagerly and as "
+                         "one captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the elementwise calibration kernel (for counter runs)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),

@@ -28,7 +28,7 @@
  * Data types are fixed: bf16 tensors, int32 metadata, fp32 accumulation,
  * bf16 output rounded to nearest even.
  *
- * Threading: a context is not thread-safe; use one context per stream.
+ * Threading: a context is not thread-safe (one host thread at a time).
  * Every call that takes a stream only enqueues work on it and returns.
  */
 #ifndef RPA_H
@@ -78,7 +78,9 @@ int rpa_create(const rpa_config* cfg, rpa_ctx** out_ctx);
  *   k_pages    device, bf16 [P, page_size, Hkv, D] row-major (P pages)
  *   v_pages    device, bf16 [P, page_size, Hkv, D] row-major
  *   page_table device, int32 [num_seqs, max_pages_per_seq] row-major; entries
- *              past ceil(kv_len / page_size) are never read
+ *              past ceil(kv_len / page_size) are never read, nor (W > 0) the
+ *              entries of pages that hold only keys before the window of the
+ *              sequence's first query token (keys < kv_len - q_len - W + 1)
  *   cu_q_lens  HOST, int32 [num_seqs + 1]; cu[0] = 0, non-decreasing
  *   kv_lens    HOST, int32 [num_seqs]; q_len <= kv_len, ceil(kv_len / B) <=
  *              max_pages_per_seq; kv_len includes this step's tokens, whose K/V
@@ -92,12 +94,23 @@ int rpa_create(const rpa_config* cfg, rpa_ctx** out_ctx);
  *
  * Host arrays are read before the call returns and may be freed afterwards.
  * Device buffers are owned by the caller and must stay valid until the
- * enqueued work has completed.  Page slots past kv_len and the pool's other
- * pages may hold anything (even NaN): they never reach the result.
+ * enqueued work has completed.  Page slots past kv_len, slots of keys before
+ * the window of a sequence's first query token, and the pool's other pages
+ * may hold anything (even NaN): they are never read into the result.
  * Every argument check runs on the host before anything is enqueued: a call
  * that returns an error has enqueued nothing.  Page-table *values* are device
  * data and are not checked.  Returns RPA_OK, RPA_ERR_INVALID_ARG, RPA_ERR_OOM
  * or RPA_ERR_HIP; rpa_last_error() then holds a message.
+ *
+ * Ordering: the calls of one context run in the order they are made, also
+ * when they are made on different streams (a call on another stream than
+ * the previous call first waits, on the device, for that call to finish).
+ *
+ * Work lists: the context keeps the work list of each metadata key
+ * (cu_q_lens, kv_lens, window, bf16 or fp8 cache) it has seen recently in
+ * device buffers of its own, written once when the key is first seen and
+ * never overwritten; up to 8 keys that no capture has used are kept (least
+ * recently used first out, after its last call has finished).
  *
  * Stream capture: a call may be captured into a HIP graph (for example the
  * attention of every layer of a step, replayed as one graph) when the context
@@ -105,7 +118,13 @@ int rpa_create(const rpa_config* cfg, rpa_ctx** out_ctx);
  * its work list is on the device; the captured call enqueues only kernels
  * (and, for a mixed step, the fork and join of its second stream) and records
  * no kernel timing.  A capture that would need a new work list returns
- * RPA_ERR_INVALID_ARG.  Replays read the device buffers given at capture time.
+ * RPA_ERR_INVALID_ARG.  The work list, split workspace and fp8 staging pool
+ * that a capture used stay allocated and unchanged -- later calls with any
+ * other metadata use other buffers -- until rpa_release_captured() or
+ * rpa_destroy(), so a graph may be replayed at any time before then.  The
+ * caller orders replays against the context's eager calls (both use the
+ * same split workspace), as for any graph launch, and replays of graphs that
+ * captured the same metadata must not overlap in time.
  */
 int rpa_forward(rpa_ctx* ctx, const void* q, const void* k_pages, const void* v_pages,
                 const int32_t* page_table, const int32_t* cu_q_lens, const int32_t* kv_lens,
@@ -190,8 +209,18 @@ int rpa_forward_fp8_append(rpa_ctx* ctx, const void* q, const void* k_new, const
                            float scale, void* out, void* stream);
 
 /* rpa_destroy -- free a context (NULL-safe).  The caller must first make sure
- * no work enqueued with it is still running. */
+ * no work enqueued with it is still running, and must not replay a graph
+ * that captured one of its calls afterwards. */
 void rpa_destroy(rpa_ctx* ctx);
+
+/*
+ * rpa_release_captured -- declare that no graph holding a captured call of
+ * this context will be replayed again (and none is running).  The work
+ * lists, workspaces and staging pools that captures pinned become ordinary
+ * cache entries again (evictable; retired pools are freed).  Returns RPA_OK,
+ * RPA_ERR_INVALID_ARG for a NULL context, or RPA_ERR_HIP.
+ */
+int rpa_release_captured(rpa_ctx* ctx);
 
 /* rpa_status_string -- static text of a status code. */
 const char* rpa_status_string(int status);

@@ -88,6 +88,13 @@ class RaggedPagedAttention:
         except Exception:
             pass
 
+    def release_captured(self) -> None:
+        """``rpa_release_captured``: no graph holding a captured call of this
+        context will be replayed again; its pinned work lists become evictable."""
+        st = self._lib.rpa_release_captured(self._ctx)
+        if st != RPA_OK:
+            raise self._error(st, "rpa_release_captured")
+
     def _error(self, st: int, what: str) -> RpaError:
         msg = self._lib.rpa_last_error(self._ctx).decode(errors="replace")
         return RpaError(st, f"{what}: {self._lib.rpa_status_string(st).decode()}: {msg}")

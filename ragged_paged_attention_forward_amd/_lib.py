@@ -29,7 +29,7 @@ RPA_KERNEL_MERGE = 2
 RPA_KERNEL_APPEND = 3
 RPA_KERNEL_STAGE = 4
 
-EXPORTED = ("rpa_create", "rpa_forward", "rpa_forward_append", "rpa_forward_fp8", "rpa_forward_fp8_append", "rpa_destroy", "rpa_status_string",
+EXPORTED = ("rpa_create", "rpa_forward", "rpa_forward_append", "rpa_forward_fp8", "rpa_forward_fp8_append", "rpa_destroy", "rpa_release_captured", "rpa_status_string",
             "rpa_last_error", "rpa_set_option", "rpa_plan", "rpa_kernel_times", "rpa_probe_read", "rpa_probe_mfma",
             "rpa_probe_e4m3")
 
@@ -98,6 +98,8 @@ def load() -> ctypes.CDLL:
     lib.rpa_forward_fp8_append.restype = ctypes.c_int
     lib.rpa_destroy.argtypes = [vp]
     lib.rpa_destroy.restype = None
+    lib.rpa_release_captured.argtypes = [vp]
+    lib.rpa_release_captured.restype = ctypes.c_int
     lib.rpa_status_string.argtypes = [ctypes.c_int]
     lib.rpa_status_string.restype = ctypes.c_char_p
     lib.rpa_last_error.argtypes = [vp]

@@ -479,17 +479,22 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     const int k0 = key_of(ts);
     char* kdst = lds + buf * C::STAGE_B + wave * C::LOADS * C::BLK_K;
     char* vdst = lds + buf * C::STAGE_B + C::TILE_K + wave * C::LOADS * C::BLK_V;
+    // Only keys [lo, hi) of the item's range are read: rows of the tile below
+    // kv_begin (the first tile of a range that does not start on a tile
+    // boundary) and past kv_end read as zero, and are masked later.
+    const int lo = k0 > kv_begin ? k0 : kv_begin;
     const int hi = k0 + BN < kv_end ? k0 + BN : kv_end;
     if constexpr (UNI) {
-      // The tile lies in one page.  Rows [k0, hi) are real keys of the
-      // sequence (rows below kv_begin are masked later); rows past hi read as
-      // zero through the buffer's record count.
+      // The tile lies in one page.  The buffer starts at row lo and ends
+      // after row hi - 1: rows below lo have negative offsets, which wrap
+      // above the record count, so they read as zero like rows past hi.
       if (static_cast<unsigned>(st_pidx - pw_base) >= 64u) {   // left the window (ranges of more than 64 pages)
         load_window(st_pidx);
         wait_vmem();
       }
+      const int rel_b = (lo - k0) * row_bytes;
       const int64_t page = __builtin_amdgcn_readlane(pw_ids, st_pidx - pw_base);
-      const int64_t base_off = ((page * page_size + st_slot) * hkv + g) * D;
+      const int64_t base_off = ((page * page_size + st_slot + (lo - k0)) * hkv + g) * D;
       st_slot += BN;
       if (st_slot == page_size) {
         st_slot = 0;
@@ -500,21 +505,22 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
         st_pidx = wrap_pidx;
         st_slot = wrap_slot;
       }
-      const uint32_t nbytes = static_cast<uint32_t>((hi - k0 - 1) * row_bytes + D * 2);
+      const uint32_t nbytes = static_cast<uint32_t>((hi - lo - 1) * row_bytes + D * 2);
       const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + base_off, nbytes);
       const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + base_off, nbytes);
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
-        buffer_load_lds16(krs, kdst + i * C::BLK_K, srow[i] * row_bytes + sgk[i]);
-        buffer_load_lds16(vrs, vdst + i * C::BLK_V, srow[i] * row_bytes + sgv[i]);
+        buffer_load_lds16(krs, kdst + i * C::BLK_K, srow[i] * row_bytes + sgk[i] - rel_b);
+        buffer_load_lds16(vrs, vdst + i * C::BLK_V, srow[i] * row_bytes + sgv[i] - rel_b);
       }
     } else {
-      // Small pages: each lane looks up its row's page.  Rows past the valid
-      // range are redirected to the last valid key so every value is finite.
+      // Small pages: each lane looks up its row's page.  Rows outside [lo, hi)
+      // are redirected to the nearest key of the range, so every value read
+      // is a finite key of the range and no page before kv_begin's is looked up.
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
         int key = k0 + srow[i];
-        key = key < hi ? key : hi - 1;
+        key = key < lo ? lo : (key < hi ? key : hi - 1);
         const int pidx = key / page_size;
         const int64_t page = pt_row[pidx];
         const int64_t off = ((page * page_size + (key - pidx * page_size)) * hkv + g) * D * 2;

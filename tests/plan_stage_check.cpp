@@ -1,6 +1,8 @@
 // Invariants of the fp8 staging list built by the host planner, on random
 // ragged batches (run by tests/test_planner.py): every page that a prefill
-// item reads has a staged pool page that maps back to that (sequence, page);
+// item reads (by the kernel's key clamp, including the first tile of a range
+// that starts inside a tile) has a staged pool page that maps back to that
+// (sequence, page);
 // pool pages are numbered 0.. in list order; no staging without prefill
 // items.  Exit status 0 when every check holds.
 #include <algorithm>
@@ -59,12 +61,23 @@ int main() {
                       slot == b && plan.stage_table[static_cast<size_t>(s) * max_pages + lp] == slot;
       bad += !ok;
     }
+    // The pages the prefill kernel reads for an item: its key tiles of BN
+    // keys start at floor(kv_begin / BN) * BN, and every row of a tile reads
+    // the key clamped into [max(tile start, kv_begin), min(tile end, kv_end))
+    // -- so the first tile's rows below kv_begin read no page before
+    // kv_begin's.  Each such page must be staged and map back to itself.
     for (const auto& it : plan.prefill) {
-      for (int lp = it.kv_begin / p.page_size; lp <= (it.kv_end - 1) / p.page_size; ++lp) {
-        const int slot = plan.stage_table[static_cast<size_t>(it.seq) * max_pages + lp];
-        const bool ok = slot >= 0 && slot < plan.stage_pages && plan.stage[3 * slot] == it.seq &&
-                        plan.stage[3 * slot + 1] == lp;
-        bad += !ok;
+      const int bn = 32;   // key tile of the head size 256 kernel
+      for (int k0 = it.kv_begin / bn * bn; k0 < it.kv_end; k0 += bn) {
+        const int lo = std::max(k0, it.kv_begin), hi = std::min(k0 + bn, it.kv_end);
+        for (int r = 0; r < bn; ++r) {
+          const int key = std::min(std::max(k0 + r, lo), hi - 1);
+          const int lp = key / p.page_size;
+          const int slot = plan.stage_table[static_cast<size_t>(it.seq) * max_pages + lp];
+          const bool ok = slot >= 0 && slot < plan.stage_pages && plan.stage[3 * slot] == it.seq &&
+                          plan.stage[3 * slot + 1] == lp && lp >= it.kv_begin / p.page_size;
+          bad += !ok;
+        }
       }
     }
   }

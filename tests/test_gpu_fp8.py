@@ -215,3 +215,45 @@ def test_fp8_append_then_attend(name):
     ref = ora.forward_fp8_rows(b.q, want_k, want_v, f.k_scales, f.v_scales, b.page_table, b.cu_q_lens, b.kv_lens,
                                w.window, w.scale)
     compare(out, ref, label=name)
+
+
+def test_fp8_append_saturates_and_keeps_nan_inf_and_signed_zero():
+    """The append kernel's special branches at scales that are not powers of
+    two: new elements beyond +-448 x scale (stored as +-448), NaN (0x7f),
+    +-Inf (saturated), -0 (0x80), values near the subnormal end, and ordinary
+    values; every byte of both pools must equal the oracle's fp8 append."""
+    from append_common import new_token_slots
+    w = wl.custom([(3, 40), (1, 77), (20, 20), (0, 9), (5, 300)], 8, 2, 128, 16, 0, seed=48)
+    print("fp8 append special values", flush=True)
+    f = wl.make_fp8_inputs(w, poison=True)
+    b = f.base
+    ks = torch.tensor([0.0173, 2.71], dtype=torch.float32)
+    vs = torch.tensor([0.333, 0.00291], dtype=torch.float32)
+    rng = np.random.default_rng(49)
+    t_q, hkv, d = b.q.shape[0], w.num_kv_heads, w.head_dim
+    scale_kv = torch.stack([ks, vs])                       # [2, Hkv]
+    x = rng.standard_normal((2, t_q, hkv, d)).astype(np.float32)
+    x *= rng.choice([0.001, 1.0, 200.0, 2000.0], size=x.shape).astype(np.float32)   # subnormal .. saturating
+    new = torch.from_numpy(x) * scale_kv.view(2, 1, hkv, 1)
+    flat = new.view(-1)
+    special = torch.tensor([float("nan"), float("inf"), float("-inf"), -0.0, 0.0, 1e30, -1e30], dtype=torch.float32)
+    idx = torch.from_numpy(rng.choice(flat.numel(), size=700, replace=False))
+    flat[idx] = special[torch.arange(700) % special.numel()]
+    k_new, v_new = new[0].to(torch.bfloat16).contiguous(), new[1].to(torch.bfloat16).contiguous()
+    assert torch.isnan(k_new).any() and torch.isinf(v_new).any()
+    assert (k_new.float().abs() > 448 * ks.view(1, -1, 1)).sum() > 100
+    flat_slots = torch.from_numpy(new_token_slots(b))
+    k_stale, v_stale = f.k_pages.clone(), f.v_pages.clone()
+    k_stale.reshape(-1, hkv, d)[flat_slots] = wl.NAN_E4M3
+    v_stale.reshape(-1, hkv, d)[flat_slots] = wl.NAN_E4M3
+    want_k, want_v = ora.append_kv_fp8(k_stale, v_stale, ks, vs, b.page_table, b.cu_q_lens, b.kv_lens, k_new, v_new)
+    d_ = b.to("cuda")
+    kp, vp = k_stale.cuda(), v_stale.cuda()
+    attn = make_attn(w)
+    attn.forward_fp8_append(d_.q, k_new.cuda(), v_new.cuda(), kp, vp, ks.cuda(), vs.cuda(), d_.page_table,
+                            b.cu_q_lens, b.kv_lens, w.window, w.scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kp.cpu().numpy(), want_k)
+    np.testing.assert_array_equal(vp.cpu().numpy(), want_v)
+    got = kp.cpu().reshape(-1, hkv, d)[flat_slots]
+    assert (got == 0x7E).any() and (got == 0xFE).any() and (got == 0x7F).any() and (got == 0x80).any()

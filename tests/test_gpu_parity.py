@@ -60,6 +60,7 @@ FULL = {
 def test_parity_full_size_sampled(name):
     """Full-size workloads; the oracle computes a seeded sample of rows one by one."""
     w = FULL[name]()
+    print(f"full size {name}", flush=True)
     inp = wl.make_inputs(w, poison=True)
     attn = make_attn(w)
     got = run_gpu(attn, inp)
@@ -70,6 +71,12 @@ def test_parity_full_size_sampled(name):
         must += [cu[s], cu[s + 1] - 1, cu[s] + 127, cu[s] + 128, cu[s] + 1023, cu[s] + 1024]
     if w.num_seqs > 4:   # every decode row of the mixed step
         must += list(range(cu[4], t))
+    # the first and last token of every query tile the planner made (each
+    # token row holds every query head, so every KV head's tile is covered)
+    _, items = attn.plan(inp.cu_q_lens, inp.kv_lens, w.window)
+    for it in items:
+        if it["kind"] == 0:
+            must += [it["q_start"], it["q_start"] + it["q_count"] - 1]
     rows = wl.sample_rows(t, 40, w.seed, must)
     ref = oracle_rows(inp, rows)
     mx, mean = compare(got, ref, rows=rows, label=name)

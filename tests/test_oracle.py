@@ -702,6 +702,36 @@ def test_append_fp8_round_trip_with_power_of_two_scales():
     np.testing.assert_array_equal(v_out, f.v_pages.numpy())
 
 
+def test_append_fp8_matches_torch_division_and_cast_at_ordinary_scales():
+    """A library route for the append's arithmetic at scales that are not
+    powers of two: each new element divided by its head's scale in torch's
+    float32 (IEEE, correctly rounded) and cast by torch to E4M3 (nearest,
+    ties to even) must give the byte the oracle writes into the element's
+    slot; every other byte of both pools is left as it was.  The values are
+    kept inside +-448 x scale, where torch's cast does not saturate."""
+    w = wl.custom([(5, 40), (1, 9), (12, 12), (0, 5), (3, 3)], 6, 3, 32, 8, seed=22)
+    f = wl.make_fp8_inputs(w, poison=True)
+    b = f.base
+    ks = torch.tensor([0.0137, 0.731, 3.3], dtype=torch.float32)
+    vs = torch.tensor([0.0291, 1.37, 0.00917], dtype=torch.float32)
+    rng = np.random.default_rng(23)
+    t_q, hkv, d = b.q.shape[0], 3, 32
+    k_new = torch.from_numpy(rng.standard_normal((t_q, hkv, d)).astype(np.float32)) * ks.view(1, -1, 1) * 90
+    v_new = torch.from_numpy(rng.standard_normal((t_q, hkv, d)).astype(np.float32)) * vs.view(1, -1, 1) * 90
+    k_new = k_new.clamp(-440 * ks.view(1, -1, 1), 440 * ks.view(1, -1, 1)).to(torch.bfloat16)
+    v_new = v_new.clamp(-440 * vs.view(1, -1, 1), 440 * vs.view(1, -1, 1)).to(torch.bfloat16)
+    k_out, v_out = ora.append_kv_fp8(f.k_pages, f.v_pages, ks, vs, b.page_table, b.cu_q_lens, b.kv_lens, k_new,
+                                     v_new)
+    want_k, want_v = f.k_pages.clone(), f.v_pages.clone()
+    bsz = w.page_size
+    for t, fl in enumerate(new_token_slots(b)):
+        page, slot = int(fl) // bsz, int(fl) % bsz
+        want_k[page, slot] = (k_new[t].to(torch.float32) / ks.view(-1, 1)).to(torch.float8_e4m3fn).view(torch.uint8)
+        want_v[page, slot] = (v_new[t].to(torch.float32) / vs.view(-1, 1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    np.testing.assert_array_equal(k_out, want_k.numpy())
+    np.testing.assert_array_equal(v_out, want_v.numpy())
+
+
 def test_planted_quantize_ties_away_is_caught(monkeypatch):
     real = ora.quantize_e4m3
 
