@@ -131,6 +131,31 @@ int rpa_forward(rpa_ctx* ctx, const void* q, const void* k_pages, const void* v_
                 int32_t num_seqs, int32_t window, float scale, void* out, void* stream);
 
 /*
+ * rpa_forward_noalloc -- rpa_forward for callers that cannot allocate
+ * device memory: code in tight serving loops and harnesses that forbid
+ * hipMalloc.  It allocates nothing on the device and creates no stream or
+ * event: the call's work list and split-KV partials go into one device
+ * array that the library holds for the life of the process (per GPU, at
+ * most RPA_NOALLOC_SCRATCH_BYTES), the list is copied there from host memory
+ * on `stream` by every call, and every kernel runs on `stream` (split groups
+ * are merged by a separate merge kernel).  The result equals rpa_forward's.
+ *
+ * Arguments, checks and errors as for rpa_forward, plus RPA_ERR_INVALID_ARG
+ * when the call's work list and partials exceed the scratch size (the message
+ * gives both sizes; a larger RPA_OPT_DECODE_SPLIT_KEYS means fewer partials)
+ * and when `stream` is being captured (the per-call copy from host memory
+ * cannot be replayed; use rpa_forward under capture).  Every call on a GPU
+ * uses that GPU's one scratch array: calls that overlap in time on one GPU
+ * (from any context or thread, or on two streams) race and must be ordered
+ * by the caller; the library does not order these calls against the
+ * context's other calls either.
+ */
+#define RPA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int rpa_forward_noalloc(rpa_ctx* ctx, const void* q, const void* k_pages, const void* v_pages,
+                        const int32_t* page_table, const int32_t* cu_q_lens, const int32_t* kv_lens,
+                        int32_t num_seqs, int32_t window, float scale, void* out, void* stream);
+
+/*
  * rpa_forward_append -- write the step's new keys and values into their
  * pages, then the same attention as rpa_forward, in one call.  The pages'
  * kernel takes the step's new tokens into the paged cache within the

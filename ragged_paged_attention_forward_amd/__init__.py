@@ -207,6 +207,23 @@ class RaggedPagedAttention:
                     self._stream_ptr))
         return out
 
+    def forward_noalloc(self, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                        page_table: torch.Tensor, cu_q_lens, kv_lens, window: int = 0,
+                        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                        stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """``rpa_forward_noalloc``: the attention of ``forward`` without any device
+        allocation by the library (its work list and partials go into the
+        library's static scratch array).  ``out`` should be preallocated by
+        callers that cannot allocate."""
+        if scale is None:
+            scale = float(self.head_dim) ** -0.5
+        cu, kv, n, out = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream)
+        self._call(self._lib.rpa_forward_noalloc, "rpa_forward_noalloc", q.device,
+                   (self._ctx, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), page_table.data_ptr(),
+                    cu.ctypes.data, kv.ctypes.data, n, int(window), float(scale), out.data_ptr(),
+                    self._stream_ptr))
+        return out
+
     def forward_append(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                        k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor, cu_q_lens,
                        kv_lens, window: int = 0, scale: Optional[float] = None,

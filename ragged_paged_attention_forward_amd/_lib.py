@@ -29,7 +29,7 @@ RPA_KERNEL_MERGE = 2
 RPA_KERNEL_APPEND = 3
 RPA_KERNEL_STAGE = 4
 
-EXPORTED = ("rpa_create", "rpa_forward", "rpa_forward_append", "rpa_forward_fp8", "rpa_forward_fp8_append", "rpa_destroy", "rpa_release_captured", "rpa_status_string",
+EXPORTED = ("rpa_create", "rpa_forward", "rpa_forward_append", "rpa_forward_fp8", "rpa_forward_fp8_append", "rpa_destroy", "rpa_release_captured", "rpa_forward_noalloc", "rpa_status_string",
             "rpa_last_error", "rpa_set_option", "rpa_plan", "rpa_kernel_times", "rpa_probe_read", "rpa_probe_mfma",
             "rpa_probe_e4m3")
 
@@ -87,6 +87,9 @@ def load() -> ctypes.CDLL:
     lib.rpa_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
                                 ctypes.c_float, vp, vp]
     lib.rpa_forward.restype = ctypes.c_int
+    lib.rpa_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_float, vp, vp]
+    lib.rpa_forward_noalloc.restype = ctypes.c_int
     lib.rpa_forward_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_float, vp, vp]
     lib.rpa_forward_append.restype = ctypes.c_int

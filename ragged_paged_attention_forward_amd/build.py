@@ -27,6 +27,7 @@ KERNEL_SOURCES = {
     "rpa_kernels_d512.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "rpa_probe.hip": [],
     "rpa_e4m3.hip": [],
+    "rpa_noalloc.hip": [],
 }
 HOST_SOURCES = ["rpa_dispatch.cpp", "rpa_api.cpp", "rpa_plan.cpp"]
 ARCH = "gfx950"

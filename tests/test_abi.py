@@ -117,6 +117,36 @@ def test_forward_rejects_null_and_aliasing_pointers():
     lib.rpa_destroy(ctx)
 
 
+@pytest.mark.parametrize("case,cu,kv,n,window,scale,msg", [
+    ("q_len > kv_len", [0, 5], [4], 1, 0, 1.0, "exceeds kv_len"),
+    ("cu decreasing", [0, 5, 3], [9, 9], 2, 0, 1.0, "decreases"),
+    ("too many pages", [0, 1], [128 * 8 + 1], 1, 0, 1.0, "pages"),
+    ("negative window", [0, 1], [5], 1, -3, 1.0, "window"),
+    ("too many tokens", [0, 65], [100], 1, 0, 1.0, "max_q_tokens"),
+    ("zero scale", [0, 1], [5], 1, 0, 0.0, "scale"),
+])
+def test_forward_noalloc_rejects_invalid_arguments_before_any_device_call(case, cu, kv, n, window, scale, msg):
+    lib, st, ctx = _ctx()
+    cu_a, cu_p = i32(cu)
+    kv_a, kv_p = i32(kv)
+    st = lib.rpa_forward_noalloc(ctx, FAKE, FAKE, FAKE, FAKE, cu_p, kv_p, n, window, scale,
+                                 ctypes.c_void_p(0x9000), None)
+    assert st == _lib.RPA_ERR_INVALID_ARG, case
+    assert msg in lib.rpa_last_error(ctx).decode(), lib.rpa_last_error(ctx)
+    cu_a, cu_p = i32([0, 2])
+    kv_a, kv_p = i32([7])
+    assert lib.rpa_forward_noalloc(ctx, FAKE, None, FAKE, FAKE, cu_p, kv_p, 1, 0, 1.0, FAKE, None) == \
+        _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_forward_noalloc(ctx, FAKE, FAKE, FAKE, FAKE, cu_p, kv_p, 1, 0, 1.0, ctypes.c_void_p(0x1000 + 64),
+                                   None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_forward_noalloc(None, FAKE, FAKE, FAKE, FAKE, cu_p, kv_p, 1, 0, 1.0, FAKE, None) == \
+        _lib.RPA_ERR_INVALID_ARG
+    cu0_a, cu0_p = i32([0, 0])
+    kv0_a, kv0_p = i32([3])   # no query tokens: nothing to do, no device call
+    assert lib.rpa_forward_noalloc(ctx, None, None, None, None, cu0_p, kv0_p, 1, 0, 1.0, None, None) == _lib.RPA_OK
+    lib.rpa_destroy(ctx)
+
+
 def test_empty_call_returns_ok_without_device_work():
     lib, st, ctx = _ctx()
     cu_a, cu_p = i32([0, 0, 0])
