@@ -68,6 +68,12 @@ COPY_BYTES = 1 << 30            # calibration buffer (read once, written once)
 KERNEL_NAMES = {"prefill": "rpa_prefill_kernel", "decode": "rpa_decode_kernel", "merge": "rpa_merge_kernel",
                 "append": "rpa_append_kernel", "stage": "rpa_stage_kernel"}
 WORKLOADS = ("decode", "tiny", "swa_prefill", "global_prefill", "mixed", "mixed_swa")
+# read-probe shapes swept for the measured HBM ceiling: (workgroups, threads,
+# 16-byte loads in flight per thread), from one workgroup per compute unit
+# with deep queues to many small workgroups
+PROBE_SHAPES = [(256, 1024, 8), (256, 1024, 16), (256, 256, 32), (512, 256, 16), (512, 1024, 4),
+                (1024, 256, 8), (1024, 256, 16), (2048, 256, 4), (2048, 256, 8), (4096, 256, 4),
+                (8192, 256, 4), (1024, 1024, 4)]
 
 
 def kernel_source_hash() -> str:
@@ -248,17 +254,22 @@ def measured_peak(torch, R, dev, bound: str, nbytes: int):
         slices = max(4, int(np.ceil(4 * LLC_BYTES / nb)))   # rotate so no read finds its slice in the LLC
         pool = torch.empty(nb * slices, dtype=torch.uint8, device=dev)
         pool.fill_(1)
-        best = None
-        for wgs in (512, 1024):
-            sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
-            launch = lambda i: R.probe_read(pool[(i % slices) * nb:], nb, wgs, sink, stream)
-            time_launches(launch, 5)
-            ms = time_launches(launch, 40)
-            best = ms if best is None else min(best, ms)
+        best, best_shape, sweep = None, None, {}
+        for wgs, threads, loads in PROBE_SHAPES:
+            sink = torch.empty(wgs * threads, dtype=torch.int32, device=dev)
+            launch = lambda i: R.probe_read(pool[(i % slices) * nb:], nb, wgs, sink, stream, threads, loads)
+            time_launches(launch, 3)
+            ms = time_launches(launch, 25)
+            sweep[f"{wgs}x{threads}x{loads}"] = round(nb / (ms * 1e-3) / 1e9, 1)
+            if best is None or ms < best:
+                best, best_shape = ms, (wgs, threads, loads)
         del pool
         return {"value": round(nb / (best * 1e-3) / 1e9, 1), "unit": "GB/s",
                 "probe": f"rpa_probe_read: plain streaming read of the same {nb} bytes, cold "
-                         f"(rotated over {slices} slices), median of 40 launches, best of 512/1024 workgroups"}
+                         f"(rotated over {slices} slices), median of 25 launches per shape, best of "
+                         f"{len(PROBE_SHAPES)} shapes (workgroups x threads x 16-byte loads in flight per "
+                         f"thread): {best_shape[0]}x{best_shape[1]}x{best_shape[2]}",
+                "sweep_gbps": sweep}
     wgs, iters = 1024, 2048
     sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
     flops = R.probe_mfma(wgs, iters, sink, stream)

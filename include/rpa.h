@@ -327,10 +327,12 @@ int rpa_kernel_times(rpa_ctx* ctx, int32_t kind, float* ms, int32_t capacity, in
  *
  * rpa_probe_read -- stream `bytes` bytes of device memory at `src` (16-byte
  * aligned, bytes a positive multiple of 16) through the compute units: each
- * of `workgroups` (1 .. 65536) workgroups of 256 threads reads one contiguous
- * slice with 16-byte loads, and every thread writes one 32-bit fold of what it
- * read to `sink` (device memory of workgroups * 256 uint32, caller-owned).
- * The best case for moving that many bytes from HBM into the chip.
+ * of `workgroups` (1 .. 65536) workgroups of `threads` threads (256 or 1024)
+ * reads one contiguous slice with 16-byte loads, `loads_in_flight` of them
+ * per thread at a time (4, 8 or 16; with 256 threads also 32), and every
+ * thread writes one 32-bit fold of what it read to `sink` (device memory of
+ * workgroups * threads uint32, caller-owned).  Swept over its shapes, the
+ * best case for moving that many bytes from HBM into the chip.
  *
  * rpa_probe_mfma -- `workgroups` (1 .. 65536) workgroups of 512 threads, each
  * wave running 4 independent chains of `iterations` (>= 1)
@@ -341,7 +343,8 @@ int rpa_kernel_times(rpa_ctx* ctx, int32_t kind, float* ms, int32_t capacity, in
  * Return RPA_OK, RPA_ERR_INVALID_ARG (bad pointer or size; nothing enqueued)
  * or RPA_ERR_HIP (launch failure).
  */
-int rpa_probe_read(const void* src, int64_t bytes, int32_t workgroups, void* sink, void* stream);
+int rpa_probe_read(const void* src, int64_t bytes, int32_t workgroups, int32_t threads, int32_t loads_in_flight,
+                   void* sink, void* stream);
 int rpa_probe_mfma(int32_t workgroups, int32_t iterations, void* sink, void* stream);
 
 /*

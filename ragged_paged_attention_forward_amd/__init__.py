@@ -310,16 +310,16 @@ def rpa_forward(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, window: int
 
 
 def probe_read(src: torch.Tensor, nbytes: int, workgroups: int, sink: torch.Tensor,
-               stream: Optional[torch.cuda.Stream] = None) -> None:
+               stream: Optional[torch.cuda.Stream] = None, threads: int = 256, loads_in_flight: int = 8) -> None:
     """Enqueue the streaming-read probe over the first ``nbytes`` of ``src``
-    (``rpa_probe_read``); ``sink`` holds ``workgroups * 256`` int32."""
-    if not src.is_cuda or not sink.is_cuda or sink.numel() * sink.element_size() < workgroups * 256 * 4:
-        raise ValueError("src and sink must be CUDA tensors; sink needs workgroups * 256 words")
+    (``rpa_probe_read``); ``sink`` holds ``workgroups * threads`` int32."""
+    if not src.is_cuda or not sink.is_cuda or sink.numel() * sink.element_size() < workgroups * threads * 4:
+        raise ValueError("src and sink must be CUDA tensors; sink needs workgroups * threads words")
     if nbytes > src.numel() * src.element_size():
         raise ValueError("nbytes exceeds src")
     stream = stream or torch.cuda.current_stream(src.device)
-    st = _lib.load().rpa_probe_read(src.data_ptr(), int(nbytes), int(workgroups), sink.data_ptr(),
-                                    ctypes.c_void_p(stream.cuda_stream))
+    st = _lib.load().rpa_probe_read(src.data_ptr(), int(nbytes), int(workgroups), int(threads),
+                                    int(loads_in_flight), sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
     if st != RPA_OK:
         raise RpaError(st, "rpa_probe_read")
 

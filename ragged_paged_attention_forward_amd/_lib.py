@@ -115,7 +115,7 @@ def load() -> ctypes.CDLL:
     lib.rpa_kernel_times.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
                                      i32p]
     lib.rpa_kernel_times.restype = ctypes.c_int
-    lib.rpa_probe_read.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp]
+    lib.rpa_probe_read.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.rpa_probe_read.restype = ctypes.c_int
     lib.rpa_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.rpa_probe_e4m3.argtypes = [vp, vp, ctypes.c_int64, vp]

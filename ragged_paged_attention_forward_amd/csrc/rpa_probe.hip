@@ -4,7 +4,7 @@
 // one.
 //
 //  * rpa_probe_read -- a plain streaming read: every workgroup reads one
-//    contiguous slice with 16-byte loads, eight per thread in flight, and
+//    contiguous slice with 16-byte loads, several per thread in flight, and
 //    folds the words into one value per thread (written to `sink`, so that
 //    the loads are not removed).  Nothing of the attention method is
 //    involved; it is the best case for moving the same number of bytes from
@@ -25,27 +25,35 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kReadThreads = 256;
-constexpr int kReadUnroll = 8;
 constexpr int kMfmaThreads = 512;   // 8 waves: two per SIMD
 constexpr int kMfmaChains = 4;      // independent accumulators per wave
 
-__global__ void __launch_bounds__(kReadThreads)
+// THREADS threads per workgroup, each with UNROLL 16-byte loads in flight.
+template <int THREADS, int UNROLL>
+__global__ void __launch_bounds__(THREADS)
 probe_read_kernel(const u32x4* __restrict__ src, int64_t n16, int64_t per_wg, uint32_t* __restrict__ sink) {
   const int64_t b0 = static_cast<int64_t>(blockIdx.x) * per_wg;
   const int64_t b1 = b0 + per_wg < n16 ? b0 + per_wg : n16;
   uint32_t acc = 0;
-  for (int64_t i = b0 + threadIdx.x; i < b1; i += static_cast<int64_t>(kReadThreads) * kReadUnroll) {
-    u32x4 v[kReadUnroll];
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += static_cast<int64_t>(THREADS) * UNROLL) {
+    u32x4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) {
-      const int64_t j = i + static_cast<int64_t>(u) * kReadThreads;
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t j = i + static_cast<int64_t>(u) * THREADS;
       v[u] = j < b1 ? src[j] : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    for (int u = 0; u < UNROLL; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  sink[static_cast<int64_t>(blockIdx.x) * kReadThreads + threadIdx.x] = acc;
+  sink[static_cast<int64_t>(blockIdx.x) * THREADS + threadIdx.x] = acc;
+}
+
+template <int THREADS, int UNROLL>
+hipError_t launch_read(const void* src, int64_t n16, int32_t workgroups, void* sink, hipStream_t stream) {
+  const int64_t per_wg = (n16 + workgroups - 1) / workgroups;
+  hipLaunchKernelGGL((probe_read_kernel<THREADS, UNROLL>), dim3(workgroups), dim3(THREADS), 0, stream,
+                     static_cast<const u32x4*>(src), n16, per_wg, static_cast<uint32_t*>(sink));
+  return hipGetLastError();
 }
 
 __global__ void __launch_bounds__(kMfmaThreads)
@@ -72,15 +80,26 @@ probe_mfma_kernel(int iterations, float* __restrict__ sink) {
 
 }  // namespace
 
-extern "C" int rpa_probe_read(const void* src, int64_t bytes, int32_t workgroups, void* sink, void* stream) {
+extern "C" int rpa_probe_read(const void* src, int64_t bytes, int32_t workgroups, int32_t threads,
+                              int32_t loads_in_flight, void* sink, void* stream) {
   if (src == nullptr || sink == nullptr || bytes < 16 || bytes % 16 != 0 || workgroups < 1 ||
       workgroups > 65536)
     return RPA_ERR_INVALID_ARG;
   const int64_t n16 = bytes / 16;
-  const int64_t per_wg = (n16 + workgroups - 1) / workgroups;
-  hipLaunchKernelGGL(probe_read_kernel, dim3(workgroups), dim3(kReadThreads), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(src), n16, per_wg, static_cast<uint32_t*>(sink));
-  return hipGetLastError() == hipSuccess ? RPA_OK : RPA_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const int key = threads * 100 + loads_in_flight;
+  switch (key) {
+    case 25604: e = launch_read<256, 4>(src, n16, workgroups, sink, s); break;
+    case 25608: e = launch_read<256, 8>(src, n16, workgroups, sink, s); break;
+    case 25616: e = launch_read<256, 16>(src, n16, workgroups, sink, s); break;
+    case 25632: e = launch_read<256, 32>(src, n16, workgroups, sink, s); break;
+    case 102404: e = launch_read<1024, 4>(src, n16, workgroups, sink, s); break;
+    case 102408: e = launch_read<1024, 8>(src, n16, workgroups, sink, s); break;
+    case 102416: e = launch_read<1024, 16>(src, n16, workgroups, sink, s); break;
+    default: return RPA_ERR_INVALID_ARG;
+  }
+  return e == hipSuccess ? RPA_OK : RPA_ERR_HIP;
 }
 
 extern "C" int rpa_probe_mfma(int32_t workgroups, int32_t iterations, void* sink, void* stream) {

@@ -221,12 +221,14 @@ def test_probes_reject_bad_arguments_before_launch():
     lib = _lib.load()
     buf = ctypes.create_string_buffer(64)
     addr = ctypes.addressof(buf)
-    assert lib.rpa_probe_read(None, 64, 1, addr, None) == _lib.RPA_ERR_INVALID_ARG
-    assert lib.rpa_probe_read(addr, 64, 1, None, None) == _lib.RPA_ERR_INVALID_ARG
-    assert lib.rpa_probe_read(addr, 0, 1, addr, None) == _lib.RPA_ERR_INVALID_ARG
-    assert lib.rpa_probe_read(addr, 24, 1, addr, None) == _lib.RPA_ERR_INVALID_ARG
-    assert lib.rpa_probe_read(addr, 64, 0, addr, None) == _lib.RPA_ERR_INVALID_ARG
-    assert lib.rpa_probe_read(addr, 64, 65537, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(None, 64, 1, 256, 8, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 64, 1, 256, 8, None, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 0, 1, 256, 8, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 24, 1, 256, 8, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 64, 0, 256, 8, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 64, 65537, 256, 8, addr, None) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_probe_read(addr, 64, 1, 128, 8, addr, None) == _lib.RPA_ERR_INVALID_ARG   # no such shape
+    assert lib.rpa_probe_read(addr, 64, 1, 1024, 32, addr, None) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_probe_mfma(0, 1, addr, None) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_probe_mfma(1, 0, addr, None) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_probe_mfma(1, 1, None, None) == _lib.RPA_ERR_INVALID_ARG

@@ -18,33 +18,35 @@ if not gpu_available():
 import ragged_paged_attention_forward_amd as R  # noqa: E402
 
 
-def expected_read_fold(data: np.ndarray, workgroups: int) -> np.ndarray:
+def expected_read_fold(data: np.ndarray, workgroups: int, threads: int = 256) -> np.ndarray:
     """Thread t of workgroup b folds (XOR) the four words of every 16-byte
-    chunk b*per_wg + t + 256*i of its slice [b*per_wg, min((b+1)*per_wg, n))."""
+    chunk b*per_wg + t + threads*i of its slice [b*per_wg, min((b+1)*per_wg, n))."""
     words = data.view(np.uint32).reshape(-1, 4)
     fold = words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3]
     n = fold.shape[0]
     per_wg = -(-n // workgroups)
-    cols = -(-per_wg // 256) * 256
+    cols = -(-per_wg // threads) * threads
     grid = np.zeros((workgroups, cols), dtype=np.uint32)
     for b in range(workgroups):
         lo, hi = b * per_wg, min((b + 1) * per_wg, n)
         if hi > lo:
             grid[b, : hi - lo] = fold[lo:hi]
-    return np.bitwise_xor.reduce(grid.reshape(workgroups, cols // 256, 256), axis=1).reshape(-1)
+    return np.bitwise_xor.reduce(grid.reshape(workgroups, cols // threads, threads), axis=1).reshape(-1)
 
 
+@pytest.mark.parametrize("threads,loads", [(256, 4), (256, 8), (256, 16), (256, 32), (1024, 4), (1024, 8),
+                                           (1024, 16)])
 @pytest.mark.parametrize("nbytes,workgroups", [(16, 1), (16 * 1000, 3), (16 * 256 * 37, 37),
                                                (16 * 70001, 512)])
-def test_read_probe_reads_every_byte(nbytes, workgroups):
+def test_read_probe_reads_every_byte(nbytes, workgroups, threads, loads):
     rng = np.random.default_rng(nbytes + workgroups)
     host = rng.integers(0, 256, nbytes + 64, dtype=np.uint8)
     src = torch.from_numpy(host).cuda()
-    sink = torch.full((workgroups * 256,), -1, dtype=torch.int32, device="cuda")
-    R.probe_read(src, nbytes, workgroups, sink)
+    sink = torch.full((workgroups * threads,), -1, dtype=torch.int32, device="cuda")
+    R.probe_read(src, nbytes, workgroups, sink, threads=threads, loads_in_flight=loads)
     torch.cuda.synchronize()
     got = sink.cpu().numpy().view(np.uint32)
-    np.testing.assert_array_equal(got, expected_read_fold(host[:nbytes], workgroups))
+    np.testing.assert_array_equal(got, expected_read_fold(host[:nbytes], workgroups, threads))
 
 
 def test_mfma_probe_matches_the_closed_form():
