@@ -66,7 +66,7 @@ LLC_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "ragged_paged_attention_forward_amd", "csrc")
 COPY_BYTES = 1 << 30            # calibration buffer (read once, written once)
 KERNEL_NAMES = {"prefill": "rpa_prefill_kernel", "decode": "rpa_decode_kernel", "merge": "rpa_merge_kernel",
-                "append": "rpa_append_kernel", "stage": "rpa_stage_kernel"}
+                "append": "rpa_append_kernel", "stage": "rpa_stage_kernel", "decode2": "rpa_decode_kernel"}
 WORKLOADS = ("decode", "tiny", "swa_prefill", "global_prefill", "mixed", "mixed_swa")
 # read-probe shapes swept for the measured HBM ceiling: (workgroups, threads,
 # 16-byte loads in flight per thread), from one workgroup per compute unit
@@ -110,11 +110,11 @@ def kernel_work(w, items, merge_kernel=True, kv_elem_bytes=2):
     kind_of = {}
     split = set()
     for it in items:
-        kind_of[it["seq"]] = "decode" if it["kind"] == 1 else "prefill"
+        kind_of[it["seq"]] = {1: "decode", 2: "decode2"}.get(it["kind"], "prefill")
         if it["num_splits"] > 1:
             split.add(it["seq"])
     out = {}
-    for kind in ("prefill", "decode"):
+    for kind in ("prefill", "decode", "decode2"):
         ids = [s for s, k in kind_of.items() if k == kind]
         seqs = [w.seqs[s] for s in ids]
         q_b = metrics.qo_bytes(seqs, w.num_q_heads, w.head_dim) // 2
@@ -509,6 +509,65 @@ def measure(args, workload: str, torch, R, dev, graph_layers_n: int = 0):
     return res
 
 
+def table_sweep(args, torch, R, dev):
+    """One call per entry of the planner's (head size, group, regime, cache)
+    table: 64 sequences of q_len tokens (1: decode; 2 and 4: few-token
+    steps; 16: a short chunk) with keys U[64, 768] per entry, plus one
+    2048-token prefill per head size; each entry's kernels and their mean
+    duration over a few calls (library events).  Run under rocprofv3, the
+    kernel trace names every entry's kernel instantiation."""
+    import rpa_workloads as wl
+    rows = []
+    for d in (64, 128, 256, 512):
+        for g in (1, 2, 4, 8, 16, 32):
+            for q in (1, 2, 4, 16):
+                for kv8 in (False, True):
+                    rng = np.random.default_rng(d + g + q)
+                    w = wl.custom([(q, int(k)) for k in rng.integers(64 + q, 769, 64)], g, 1, d, 128, 0, seed=7)
+                    rows.append(_table_entry(torch, R, dev, w, kv8, f"d{d} G{g} q{q} {'fp8' if kv8 else 'bf16'}"))
+        w = wl.custom([(2048, 2048)], 8, 1, d, 128, 0, seed=8)
+        for kv8 in (False, True):
+            rows.append(_table_entry(torch, R, dev, w, kv8, f"d{d} G8 q2048 {'fp8' if kv8 else 'bf16'}"))
+    return rows
+
+
+TABLE_DECODE_ROWS = [0]   # --decode-max-rows for the table sweep (0: the library's table)
+
+
+def _table_entry(torch, R, dev, w, kv8, label):
+    import rpa_workloads as wl
+    if kv8:
+        f = wl.make_fp8_inputs(w).to(dev)
+        d, host = f.base, f.base
+    else:
+        d = host = wl.make_inputs(w).to(dev)
+    attn = R.RaggedPagedAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, w.num_seqs,
+                                  w.max_pages_per_seq, w.total_q)
+    if TABLE_DECODE_ROWS[0]:
+        attn.set_option(R.RPA_OPT_DECODE_MAX_ROWS, TABLE_DECODE_ROWS[0])
+    out = torch.empty_like(d.q)
+
+    def call():
+        if kv8:
+            attn.forward_fp8(d.q, f.k_pages, f.v_pages, f.k_scales, f.v_scales, d.page_table, host.cu_q_lens,
+                             host.kv_lens, 0, w.scale, out=out)
+        else:
+            attn.forward(d.q, d.k_pages, d.v_pages, d.page_table, host.cu_q_lens, host.kv_lens, 0, w.scale, out=out)
+    call()
+    torch.cuda.synchronize()
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 5)
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    ks = {}
+    for name, kind in R.KERNEL_KINDS.items():
+        t = attn.kernel_times(kind)
+        if len(t):
+            ks[name] = round(float(np.mean(t)) * 1e3, 2)
+    attn.close()
+    return {"entry": label, "kernels_us": ks}
+
+
 def config_summary(res):
     """The fields of one workload's result that the `configs` record keeps."""
     r = res["roofline"]
@@ -575,6 +634,11 @@ def run(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.table:
+        TABLE_DECODE_ROWS[0] = args.decode_max_rows
+        rows = table_sweep(args, torch, R, dev)
+        print(json.dumps({"table": rows}), flush=True)
+        return 0
     res = measure(args, args.workload, torch, R, dev, args.graph_layers)
     if args.configs:
         # the other workloads of the metric (the prefill half: TFLOP/s of the
@@ -611,6 +675,32 @@ def _pmc_per_dispatch(d, counter):
             vals.setdefault(name, []).append(float(v))
         con.close()
     return vals
+
+
+def trace_summary(args):
+    """Markdown kernel statistics (calls, mean / min / max duration, share)
+    from a rocprofv3 --kernel-trace database (the `kernels` view of its rocpd
+    file)."""
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(args.trace_summary, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {args.trace_summary}")
+    stats = {}
+    for db in dbs:
+        con = sqlite3.connect(db)
+        for name, dur in con.execute("select name, duration from kernels"):
+            stats.setdefault(name, []).append(dur / 1e3)
+        con.close()
+    total = sum(sum(v) for v in stats.values())
+    lines = ["| kernel | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|"]
+    for name, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        a = np.asarray(v)
+        short = name.split("(")[0] if name.startswith("void rpa::") else name
+        lines.append(f"| `{short}` | {a.size} | {a.mean():.2f} | {a.min():.2f} | {a.max():.2f} | "
+                     f"{100 * a.sum() / total:.1f} % |")
+    print("\n".join(lines))
+    return 0
 
 
 def pmc_summary(args):
@@ -677,16 +767,25 @@ def main(argv=None):
     ap.add_argument("--stack", action="store_true",
                     help="also time one step of a 5 window-1024 : 1 global layer stack, eagerly and as "
                          "one captured HIP graph")
+    ap.add_argument("--table", action="store_true",
+                    help="run one call per entry of the planner's tuning table and print its kernels' times")
+    ap.add_argument("--decode-max-rows", type=int, default=0,
+                    help="with --table: RPA_OPT_DECODE_MAX_ROWS for every call (0: the library's table), to time "
+                         "the choices the table does not make")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the elementwise calibration kernel (for counter runs)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (no GPU needed)")
     ap.add_argument("--pmc-kernel", default="rpa_decode_kernel")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="markdown kernel statistics of a rocprofv3 --kernel-trace run (no GPU needed)")
     ap.add_argument("--pmc-commands", nargs="*")
     args = ap.parse_args(argv)
 
     if args.pmc_summary:
         return pmc_summary(args)
+    if args.trace_summary:
+        return trace_summary(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(how it would shard is described in the design notes); run with --gpus 1.",

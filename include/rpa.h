@@ -269,7 +269,13 @@ enum {
                                     (longer sequences in chunks of
                                     decode-item rows; with G > 16 the
                                     prefill kernel keeps them)                  */
-  RPA_OPT_DECODE_MAX_ROWS = 4,   /* most q_len * G rows of a decode item (1..16)  */
+  RPA_OPT_DECODE_MAX_ROWS = 4,   /* most q_len * G rows of a sequence that the
+                                    decode kernels take (items of up to 16 rows
+                                    run the one-block decode kernel, of 17..32
+                                    the two-block one; head size 512: at most
+                                    16); 0 (default) = the tuning table: 16 for
+                                    a bf16 cache, 32 for an fp8 cache (its
+                                    prefill path stages pages first)           */
   RPA_OPT_DECODE_WAVES = 5,      /* waves per decode workgroup: 0 automatic
                                     (4), 4, 8 (head size 512 always runs 4)     */
   RPA_OPT_KERNEL_TIMING = 6,     /* n > 0: time up to n launches per kernel kind
@@ -315,7 +321,8 @@ int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);
  * RPA_ERR_HIP.
  */
 enum { RPA_KERNEL_PREFILL = 0, RPA_KERNEL_DECODE = 1, RPA_KERNEL_MERGE = 2, RPA_KERNEL_APPEND = 3,
-       RPA_KERNEL_STAGE = 4 /* rpa_forward_fp8: fp8 pages converted for the prefill kernel */ };
+       RPA_KERNEL_STAGE = 4 /* rpa_forward_fp8: fp8 pages converted for the prefill kernel */,
+       RPA_KERNEL_DECODE2 = 5 /* the two-block (17..32-row) decode kernel */ };
 int rpa_kernel_times(rpa_ctx* ctx, int32_t kind, float* ms, int32_t capacity, int32_t* count);
 
 /*
@@ -375,8 +382,9 @@ typedef struct rpa_work_item {
   int32_t split_index;  /* 0 .. num_splits-1 within the group                      */
   int32_t num_splits;   /* splits in the group (1 when split_group == -1)          */
   int32_t partial_base; /* first partial-result slot of the group                  */
-  int32_t kind;         /* 0: prefill kernel item, 1: decode kernel item; a split
-                           group has the kind of its splits                       */
+  int32_t kind;         /* 0: prefill kernel item, 1: decode kernel item (<= 16
+                           rows), 2: two-block decode kernel item (17..32 rows);
+                           a split group has the kind of its splits               */
 } rpa_work_item;
 
 typedef struct rpa_plan_info {

@@ -22,7 +22,7 @@ import torch
 from . import _lib
 from ._lib import (RPA_ERR_HIP, RPA_ERR_INVALID_ARG, RPA_ERR_OOM, RPA_ERR_UNSUPPORTED,
                    RPA_KERNEL_APPEND, RPA_KERNEL_DECODE, RPA_KERNEL_MERGE, RPA_KERNEL_PREFILL,
-                   RPA_KERNEL_STAGE, RPA_OK,
+                   RPA_KERNEL_STAGE, RPA_KERNEL_DECODE2, RPA_OK,
                    RPA_OPT_DECODE_MAX_ROWS, RPA_OPT_DECODE_SPLIT_KEYS, RPA_OPT_DECODE_WAVES,
                    RPA_OPT_FUSED_MERGE, RPA_OPT_KERNEL_TIMING, RPA_OPT_PATH, RPA_OPT_XCD_GROUPS,
                    RPA_OPT_PREFILL_SPLIT_KEYS, RPA_OPT_CONCURRENT,
@@ -32,11 +32,11 @@ __all__ = ["RaggedPagedAttention", "rpa_forward", "RpaError", "library_path", "R
            "RPA_ERR_INVALID_ARG", "RPA_ERR_UNSUPPORTED", "RPA_ERR_OOM", "RPA_ERR_HIP",
            "RPA_OPT_DECODE_SPLIT_KEYS", "RPA_OPT_PATH", "RPA_OPT_DECODE_MAX_ROWS",
            "RPA_OPT_DECODE_WAVES", "RPA_OPT_KERNEL_TIMING", "RPA_OPT_XCD_GROUPS", "RPA_OPT_FUSED_MERGE", "RPA_OPT_PREFILL_SPLIT_KEYS", "RPA_OPT_CONCURRENT", "RPA_KERNEL_PREFILL", "RPA_KERNEL_DECODE",
-           "RPA_KERNEL_MERGE", "RPA_KERNEL_APPEND", "RPA_KERNEL_STAGE", "KERNEL_KINDS", "probe_read", "probe_mfma",
+           "RPA_KERNEL_MERGE", "RPA_KERNEL_APPEND", "RPA_KERNEL_STAGE", "RPA_KERNEL_DECODE2", "KERNEL_KINDS", "probe_read", "probe_mfma",
            "probe_e4m3"]
 
 KERNEL_KINDS = {"prefill": RPA_KERNEL_PREFILL, "decode": RPA_KERNEL_DECODE, "merge": RPA_KERNEL_MERGE,
-                "append": RPA_KERNEL_APPEND, "stage": RPA_KERNEL_STAGE}
+                "append": RPA_KERNEL_APPEND, "stage": RPA_KERNEL_STAGE, "decode2": RPA_KERNEL_DECODE2}
 
 
 def library_path() -> str:

@@ -28,6 +28,7 @@ RPA_KERNEL_DECODE = 1
 RPA_KERNEL_MERGE = 2
 RPA_KERNEL_APPEND = 3
 RPA_KERNEL_STAGE = 4
+RPA_KERNEL_DECODE2 = 5
 
 EXPORTED = ("rpa_create", "rpa_forward", "rpa_forward_append", "rpa_forward_fp8", "rpa_forward_fp8_append", "rpa_destroy", "rpa_release_captured", "rpa_forward_noalloc", "rpa_status_string",
             "rpa_last_error", "rpa_set_option", "rpa_plan", "rpa_kernel_times", "rpa_probe_read", "rpa_probe_mfma",

@@ -941,41 +941,49 @@ RPA_DEV void merge_group(const KernelArgs& args, int q_start, int q_count, int k
 template <int D>
 __global__ void __launch_bounds__(MergeCfg<D>::THREADS) rpa_merge_kernel(KernelArgs args) {
   const rpa_work_item grp = args.groups[blockIdx.x];
+  // rows per split: a prefill tile's, 16 for a decode item, 32 for a two-block one
   merge_group<D>(args, grp.q_start, grp.q_count, grp.kv_head, grp.partial_base, grp.num_splits,
-                 grp.kind == 0 ? args.prefill_rows : 16, threadIdx.x, blockDim.x);
+                 grp.kind == 0 ? args.prefill_rows : grp.kind == 2 ? 32 : 16, threadIdx.x, blockDim.x);
 }
 
 // ---------------------------------------------------------------------------
-// Decode: rows = q_count * G <= 16; NW waves take 32-key chunks round robin.
-// Every wave issues all loads of a chunk before touching any of them; the
-// waves are combined in a fixed order through LDS (bitwise reproducible).
+// Decode: rows = q_count * G <= 16 * RB; NW waves take 32-key chunks round
+// robin.  Every wave issues all loads of a chunk before touching any of them;
+// the waves are combined in a fixed order through LDS (bitwise reproducible).
+// RB = 2 holds two blocks of 16 rows (a single token of 32 grouped heads, or
+// a few tokens of a smaller group) over the same K/V fragments: each key
+// row loaded serves twice the rows, and such items stay off the prefill
+// kernel, whose 128-256-row tiles they would leave mostly empty.
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, int RB = 1>
 struct DecodeCfg {
   static constexpr int NT = NW * 64;
+  static constexpr int ROWS = 16 * RB;                // query rows of an item
   static constexpr int NCH = D / 8;                   // 16-byte chunks per key row
   static constexpr int NU = (NCH + 15) / 16;          // V chunk rounds per lane
   static constexpr int OSTRIDE = D + 4;               // floats per LDS row (padded)
-  static constexpr int LDS_O = (NW / 2) * 16 * OSTRIDE; // tree-combine slots
-  static constexpr int LDS_BYTES = LDS_O * 4 + NW * 16 * 2 * 4 + 16;   // + merge flag
+  static constexpr int LDS_O = (NW / 2) * ROWS * OSTRIDE; // tree-combine slots
+  static constexpr int LDS_BYTES = LDS_O * 4 + NW * ROWS * 2 * 4 + 16;   // + merge flag
 };
 
 // Second launch bound: waves per SIMD to fit (two, so a compute unit holds two
-// workgroups of 4 waves; one for D = 512 whose fragments need the full file).
+// workgroups of 4 waves; one for D = 512 whose fragments need the full file,
+// and for two row blocks at D = 256).
 // KV8: the pools hold OCP FP8 E4M3 bytes with one K and one V scale per KV
 // head; each lane loads 8 bytes where the bf16 form loads 16 and converts
 // them to the same bf16 operand layout.  The K scale joins the score scale
 // and the V scale the output weight (both are per KV head, so they factor
 // out of the dot products).
-template <int D, int NW, bool UNI, bool KV8>
-__global__ void __launch_bounds__(NW * 64, D >= 512 ? 1 : 2)
+template <int D, int NW, bool UNI, bool KV8, int RB = 1>
+__global__ void __launch_bounds__(NW * 64, (D >= 512 || (RB == 2 && D >= 256)) ? 1 : 2)
 rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
-  using C = DecodeCfg<D, NW>;
+  using C = DecodeCfg<D, NW, RB>;
+  constexpr int ROWS = C::ROWS;
   extern __shared__ __attribute__((aligned(16))) float dsm[];
-  float* lds_o = dsm;                     // [NW/2][16][OSTRIDE]
-  float* lds_m = dsm + C::LDS_O;          // [NW][16]
-  float* lds_l = lds_m + NW * 16;         // [NW][16]
-  int* lds_flag = reinterpret_cast<int*>(lds_l + NW * 16);
+  float* lds_o = dsm;                     // [NW/2][ROWS][OSTRIDE]
+  float* lds_m = dsm + C::LDS_O;          // [NW][ROWS]
+  float* lds_l = lds_m + NW * ROWS;       // [NW][ROWS]
+  int* lds_flag = reinterpret_cast<int*>(lds_l + NW * ROWS);
 
   const rpa_work_item it = items[blockIdx.x];
   // the work item's load goes out before the argument block's: nothing is
@@ -1008,24 +1016,36 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     vscale = uniform_load(args.v_scales, g);
   }
 
-  // query row n = ln: token ln / G, head ln % G
-  const int tk = ln / G;
-  const int hh = ln - tk * G;
-  const bool row_ok = ln < rows;
-  const int pos = it.q_pos0 + tk;
-  const int64_t q_off = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
+  // query row n = rb*16 + ln: token n / G, head n % G
+  int pos[RB];
+  bool row_ok[RB];
+  u32x4 qf[RB][D / 32];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = rb * 16 + ln;
+    const int tk = r / G;
+    const int hh = r - tk * G;
+    row_ok[rb] = r < rows;
+    pos[rb] = it.q_pos0 + tk;
+    const int64_t q_off = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      qf[rb][kk] = row_ok[rb] ? load16(q + q_off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
+  }
 
-  u32x4 qf[D / 32];
+  f32x4 o[RB][C::NU][8];
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    qf[kk] = row_ok ? load16(q + q_off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
-
-  f32x4 o[C::NU][8];
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-  for (int u = 0; u < C::NU; ++u)
+    for (int u = 0; u < C::NU; ++u)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[u][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
+      for (int e = 0; e < 8; ++e) o[rb][u][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = kNegInf;
+    l_run[rb] = 0.f;
+  }
 
   // 32-key chunks aligned to 32 keys; with UNI a chunk never crosses a page.
   const int chunk0 = (kv_begin / 32) * 32;
@@ -1125,104 +1145,126 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
         for (int j = 0; j < 8; ++j) vf[u][j] = e4m3x8_to_bf16x8(vr[u][j]);
     }
 
-    f32x4 s[2];
+    u32x4 pf[RB];
+    float alpha[RB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x4 s[2];
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) s[kb] = mfma16(kf[kb][kk], qf[kk], s[kb]);
-    }
-
-    float mx = kNegInf;
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+        for (int kk = 0; kk < D / 32; ++kk) s[kb] = mfma16(kf[kb][kk], qf[rb][kk], s[kb]);
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = k0 + kb * 16 + lq * 4 + j;
+          float x = s[kb][j] * sl2;
+          if (!key_visible(key, pos[rb], kv_begin, kv_end, window)) x = kNegInf;
+          s[kb][j] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = xor_max(mx);
+      const float m_new = fmaxf(m_run[rb], mx);
+      const float base = (m_new == kNegInf) ? 0.f : m_new;
+      alpha[rb] = fast_exp2(m_run[rb] - base);
+      m_run[rb] = m_new;
+      float p[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int key = k0 + kb * 16 + lq * 4 + j;
-        float x = s[kb][j] * sl2;
-        if (!key_visible(key, pos, kv_begin, kv_end, window)) x = kNegInf;
-        s[kb][j] = x;
-        mx = fmaxf(mx, x);
+        p[j] = fast_exp2(s[0][j] - base);
+        p[4 + j] = fast_exp2(s[1][j] - base);
       }
-    }
-    mx = xor_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float base = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - base);
-    m_run = m_new;
-    float p[8];
+      float lsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = fast_exp2(s[0][j] - base);
-      p[4 + j] = fast_exp2(s[1][j] - base);
+      for (int j = 0; j < 8; ++j) lsum += p[j];
+      l_run[rb] = l_run[rb] * alpha[rb] + lsum;
+      pf[rb] = u32x4{pack_bf16x2_split(p[0], p[1]), pack_bf16x2_split(p[2], p[3]),
+                     pack_bf16x2_split(p[4], p[5]), pack_bf16x2_split(p[6], p[7])};
     }
-    float lsum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lsum += p[j];
-    l_run = l_run * alpha + lsum;
-    const u32x4 pf = {pack_bf16x2_split(p[0], p[1]), pack_bf16x2_split(p[2], p[3]),
-                      pack_bf16x2_split(p[4], p[5]), pack_bf16x2_split(p[6], p[7])};
 #pragma unroll
     for (int u = 0; u < C::NU; ++u) {
       u32x4 vt[8];
       transpose8x8(vf[u], vt);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[u][e] = mfma16(vt[e], pf, o[u][e] * alpha);
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[rb][u][e] = mfma16(vt[e], pf[rb], o[rb][u][e] * alpha[rb]);
     }
   }
 
   // ---- combine the waves: common max, per-wave weight, fixed-order tree ----
-  const float l_wave = xor_sum(l_run);
-  if (lq == 0) {
-    lds_m[wave * 16 + ln] = m_run;
-    lds_l[wave * 16 + ln] = l_wave;
+  float lsum[RB], base[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_wave = xor_sum(l_run[rb]);
+    if (lq == 0) {
+      lds_m[wave * ROWS + rb * 16 + ln] = m_run[rb];
+      lds_l[wave * ROWS + rb * 16 + ln] = l_wave;
+    }
   }
   __syncthreads();
-  float mx = kNegInf;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_m[w * 16 + ln]);
-  const float base = (mx == kNegInf) ? 0.f : mx;
-  float lsum = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = rb * 16 + ln;
+    float mx = kNegInf;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) lsum += fast_exp2(lds_m[w * 16 + ln] - base) * lds_l[w * 16 + ln];
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  const float wscale = fast_exp2(m_run - base) * inv * vscale;   // this wave's share, normalised
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, lds_m[w * ROWS + r]);
+    base[rb] = (mx == kNegInf) ? 0.f : mx;
+    lsum[rb] = 0.f;
 #pragma unroll
-  for (int u = 0; u < C::NU; ++u)
+    for (int w = 0; w < NW; ++w) lsum[rb] += fast_exp2(lds_m[w * ROWS + r] - base[rb]) * lds_l[w * ROWS + r];
+    const float inv = lsum[rb] > 0.f ? 1.f / lsum[rb] : 0.f;
+    const float wscale = fast_exp2(m_run[rb] - base[rb]) * inv * vscale;   // this wave's share, normalised
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[u][e] *= wscale;
-  // lane (lq, ln) holds O[row ln][d = 8*(16u + 4lq + j) + e]; slot rows are padded by 4 floats
-  auto slot_ptr = [&](int slot, int u, int j) {
-    return reinterpret_cast<f32x4*>(lds_o + (slot * 16 + ln) * C::OSTRIDE + (u * 16 + lq * 4 + j) * 8);
+    for (int u = 0; u < C::NU; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[rb][u][e] *= wscale;
+  }
+  // lane (lq, ln) holds O[row rb*16 + ln][d = 8*(16u + 4lq + j) + e]; slot rows are padded by 4 floats
+  auto slot_ptr = [&](int slot, int rb, int u, int j) {
+    return reinterpret_cast<f32x4*>(lds_o + (slot * ROWS + rb * 16 + ln) * C::OSTRIDE + (u * 16 + lq * 4 + j) * 8);
   };
 #pragma unroll
   for (int half = NW / 2; half >= 1; half /= 2) {
-    if (wave >= half && wave < 2 * half && row_ok) {
+    if (wave >= half && wave < 2 * half) {
 #pragma unroll
-      for (int u = 0; u < C::NU; ++u)
+      for (int rb = 0; rb < RB; ++rb) {
+        if (!row_ok[rb]) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (u * 16 + lq * 4 + j < C::NCH) {
-            f32x4* dst = slot_ptr(wave - half, u, j);
-            dst[0] = f32x4{o[u][0][j], o[u][1][j], o[u][2][j], o[u][3][j]};
-            dst[1] = f32x4{o[u][4][j], o[u][5][j], o[u][6][j], o[u][7][j]};
-          }
+        for (int u = 0; u < C::NU; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (u * 16 + lq * 4 + j < C::NCH) {
+              f32x4* dst = slot_ptr(wave - half, rb, u, j);
+              dst[0] = f32x4{o[rb][u][0][j], o[rb][u][1][j], o[rb][u][2][j], o[rb][u][3][j]};
+              dst[1] = f32x4{o[rb][u][4][j], o[rb][u][5][j], o[rb][u][6][j], o[rb][u][7][j]};
+            }
+      }
     }
     __syncthreads();
-    if (wave < half && row_ok) {
+    if (wave < half) {
 #pragma unroll
-      for (int u = 0; u < C::NU; ++u)
+      for (int rb = 0; rb < RB; ++rb) {
+        if (!row_ok[rb]) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (u * 16 + lq * 4 + j < C::NCH) {
-            const f32x4* src = slot_ptr(wave, u, j);
-            const f32x4 lo = src[0], hi = src[1];
+        for (int u = 0; u < C::NU; ++u)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              o[u][e][j] += lo[e];
-              o[u][4 + e][j] += hi[e];
+          for (int j = 0; j < 4; ++j)
+            if (u * 16 + lq * 4 + j < C::NCH) {
+              const f32x4* src = slot_ptr(wave, rb, u, j);
+              const f32x4 lo = src[0], hi = src[1];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                o[rb][u][e][j] += lo[e];
+                o[rb][u][4 + e][j] += hi[e];
+              }
             }
-          }
+      }
     }
     if (half > 1) __syncthreads();
   }
@@ -1231,16 +1273,20 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   // (row-major, rows padded to OSTRIDE floats) and every thread then stores
   // 16 contiguous bytes of a row, consecutive threads along the row, instead
   // of wave 0 storing 16-byte pieces strewn over 16 rows.
-  if (wave == 0 && row_ok) {
+  if (wave == 0) {
 #pragma unroll
-    for (int u = 0; u < C::NU; ++u)
+    for (int rb = 0; rb < RB; ++rb) {
+      if (!row_ok[rb]) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (u * 16 + lq * 4 + j < C::NCH) {
-          f32x4* dst = slot_ptr(0, u, j);
-          dst[0] = f32x4{o[u][0][j], o[u][1][j], o[u][2][j], o[u][3][j]};
-          dst[1] = f32x4{o[u][4][j], o[u][5][j], o[u][6][j], o[u][7][j]};
-        }
+      for (int u = 0; u < C::NU; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (u * 16 + lq * 4 + j < C::NCH) {
+            f32x4* dst = slot_ptr(0, rb, u, j);
+            dst[0] = f32x4{o[rb][u][0][j], o[rb][u][1][j], o[rb][u][2][j], o[rb][u][3][j]};
+            dst[1] = f32x4{o[rb][u][4][j], o[rb][u][5][j], o[rb][u][6][j], o[rb][u][7][j]};
+          }
+    }
   }
   __syncthreads();
   const bool split = it.split_group >= 0;
@@ -1257,15 +1303,20 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     }
     return;
   }
-  const int64_t slot = static_cast<int64_t>(it.partial_base) + it.split_index;
+  // a split's rows take RB consecutive 16-row partial slots
+  const int64_t slot = static_cast<int64_t>(it.partial_base) + static_cast<int64_t>(it.split_index) * RB;
   for (int idx = tid; idx < rows * C4; idx += C::NT) {
     const int r = idx / C4;
     const int c = idx - r * C4;
     *reinterpret_cast<f32x4*>(args.partial_o + (slot * 16 + r) * D + c * 4) =
         *reinterpret_cast<const f32x4*>(lds_o + r * C::OSTRIDE + c * 4);
   }
-  if (wave == 0 && row_ok && lq == 0)
-    args.partial_lse[slot * 16 + ln] = (lsum > 0.f) ? base + __builtin_log2f(lsum) : kNegInf;
+  if (wave == 0 && lq == 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      if (row_ok[rb])
+        args.partial_lse[slot * 16 + rb * 16 + ln] = (lsum[rb] > 0.f) ? base[rb] + __builtin_log2f(lsum[rb]) : kNegInf;
+  }
   if (!args.fused_merge) return;
 
   // ---- last split of the group merges it (the group's ticket counts arrivals) ----
@@ -1283,7 +1334,7 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   __syncthreads();
   if (*lds_flag == 0) return;
   asm volatile("" ::: "memory");
-  merge_group<D>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, 16, tid, C::NT);
+  merge_group<D>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, ROWS, tid, C::NT);
   if (tid == 0) __hip_atomic_store(args.merge_tickets + it.split_group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1415,19 +1466,41 @@ static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, hipStream_t
   return launch_prefill_u<D, BN, NW, NB, NS, DS, false>(a, n_items, stream);
 }
 
-template <int D, int NW, bool UNI, bool KV8 = false>
+template <int D, int NW, bool UNI, bool KV8 = false, int RB = 1>
 static hipError_t launch_decode_u(const KernelArgs& a, int n_items, hipStream_t stream) {
-  using C = DecodeCfg<D, NW>;
-  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, UNI, KV8>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream,
+  using C = DecodeCfg<D, NW, RB>;
+  if constexpr (C::LDS_BYTES > 64 * 1024) {   // beyond the default dynamic LDS limit
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_decode_kernel<D, NW, UNI, KV8, RB>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+  }
+  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, UNI, KV8, RB>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream,
                      a.items, a.page_table, a.q, a.k, a.v, a);
   return hipGetLastError();
 }
 
 // Eight-wave workgroups are not used for D = 512: two waves per SIMD cannot
-// hold its fragments.  The fp8 form is built with four waves only.
+// hold its fragments.  The fp8 form and the two-block (32-row) form are built
+// with four waves only; there is no two-block form for D = 512.
 template <int D>
-static hipError_t launch_decode_t(const KernelArgs& a, int n_items, int waves, bool kv8, hipStream_t stream) {
+static hipError_t launch_decode_t(const KernelArgs& a, int n_items, int waves, bool kv8, int rows,
+                                  hipStream_t stream) {
   const bool uni = a.page_size % 32 == 0;
+  if constexpr (D < 512) {
+    if (rows > 16) {
+      if (kv8)
+        return uni ? launch_decode_u<D, 4, true, true, 2>(a, n_items, stream)
+                   : launch_decode_u<D, 4, false, true, 2>(a, n_items, stream);
+      return uni ? launch_decode_u<D, 4, true, false, 2>(a, n_items, stream)
+                 : launch_decode_u<D, 4, false, false, 2>(a, n_items, stream);
+    }
+  } else {
+    if (rows > 16) return hipErrorInvalidValue;
+  }
   if (kv8)
     return uni ? launch_decode_u<D, 4, true, true>(a, n_items, stream)
                : launch_decode_u<D, 4, false, true>(a, n_items, stream);
@@ -1493,8 +1566,9 @@ constexpr int prefill_wgs_per_cu() {
   hipError_t launch_prefill_d##D(const KernelArgs& a, int n, hipStream_t s) {               \
     return launch_prefill_t<RPA_PREFILL_SHAPE_##D>(a, n, s);                               \
   }                                                                                         \
-  hipError_t launch_decode_d##D(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s) { \
-    return launch_decode_t<D>(a, n, waves, kv8, s);                                         \
+  hipError_t launch_decode_d##D(const KernelArgs& a, int n, int waves, bool kv8, int rows,    \
+                                hipStream_t s) {                                            \
+    return launch_decode_t<D>(a, n, waves, kv8, rows, s);                                   \
   }                                                                                         \
   hipError_t launch_merge_d##D(const KernelArgs& a, int n, hipStream_t s) {                 \
     return launch_merge_t<D>(a, n, s);                                                      \

@@ -10,7 +10,7 @@
 namespace rpa {
 
 hipError_t launch_prefill_d64(const KernelArgs& a, int n, hipStream_t s);
-hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
+hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d64(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               bool kv8, hipStream_t s);
@@ -18,7 +18,7 @@ hipError_t launch_stage_d64(const KernelArgs& a, const int32_t* st, int n, void*
 int prefill_rows_d64();
 int prefill_wgs_per_cu_d64();
 hipError_t launch_prefill_d128(const KernelArgs& a, int n, hipStream_t s);
-hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
+hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               bool kv8, hipStream_t s);
@@ -26,7 +26,7 @@ hipError_t launch_stage_d128(const KernelArgs& a, const int32_t* st, int n, void
 int prefill_rows_d128();
 int prefill_wgs_per_cu_d128();
 hipError_t launch_prefill_d256(const KernelArgs& a, int n, hipStream_t s);
-hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
+hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               bool kv8, hipStream_t s);
@@ -34,7 +34,7 @@ hipError_t launch_stage_d256(const KernelArgs& a, const int32_t* st, int n, void
 int prefill_rows_d256();
 int prefill_wgs_per_cu_d256();
 hipError_t launch_prefill_d512(const KernelArgs& a, int n, hipStream_t s);
-hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, bool kv8, hipStream_t s);
+hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d512(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               bool kv8, hipStream_t s);
@@ -103,17 +103,17 @@ hipError_t launch_prefill(const LaunchArgs& l, const rpa_work_item* items, int n
   }
 }
 
-hipError_t launch_decode(const LaunchArgs& l, const rpa_work_item* items, int n_items) {
+hipError_t launch_decode(const LaunchArgs& l, const rpa_work_item* items, int n_items, int rows) {
   if (n_items <= 0) return hipSuccess;
   const KernelArgs a = make_args(l, items);
   hipStream_t s = static_cast<hipStream_t>(l.stream);
   const int w = l.decode_waves;
   const bool kv8 = l.kv_fp8 != 0;
   switch (l.head_dim) {
-    case 64: return launch_decode_d64(a, n_items, w, kv8, s);
-    case 128: return launch_decode_d128(a, n_items, w, kv8, s);
-    case 256: return launch_decode_d256(a, n_items, w, kv8, s);
-    case 512: return launch_decode_d512(a, n_items, w, kv8, s);
+    case 64: return launch_decode_d64(a, n_items, w, kv8, rows, s);
+    case 128: return launch_decode_d128(a, n_items, w, kv8, rows, s);
+    case 256: return launch_decode_d256(a, n_items, w, kv8, rows, s);
+    case 512: return launch_decode_d512(a, n_items, w, kv8, rows, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -41,7 +41,8 @@ int prefill_wgs_per_cu_for(int head_dim);
 bool head_dim_supported(int head_dim);
 
 hipError_t launch_prefill(const LaunchArgs& a, const rpa_work_item* items, int n_items);
-hipError_t launch_decode(const LaunchArgs& a, const rpa_work_item* items, int n_items);
+// rows: 16 for the one-block decode kernel, 32 for the two-block one.
+hipError_t launch_decode(const LaunchArgs& a, const rpa_work_item* items, int n_items, int rows);
 hipError_t launch_merge(const LaunchArgs& a, int n_groups);
 // Copies the step's new K/V rows (k_new / v_new, [T, Hkv, D]) into their page
 // slots of k_dst / v_dst, one workgroup per work item.

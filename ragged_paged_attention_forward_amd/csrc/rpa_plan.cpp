@@ -196,6 +196,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
                 int32_t window, Plan* out) {
   out->prefill.clear();
   out->decode.clear();
+  out->decode2.clear();
   out->groups.clear();
   out->num_partials = 0;
   out->stage.clear();
@@ -206,7 +207,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
 
   const int group = p.num_q_heads / p.num_kv_heads;
   const int tile_tokens = std::max(1, p.prefill_rows / group);
-  const int dec_tokens = p.decode_max_rows / group;  // 0 when G exceeds a decode item
+  const int dec_tokens = decode_rows_limit(p) / group;  // 0 when G exceeds a decode item
 
   struct DecodeSeq {
     int32_t seq, q_start, q_count, pos0, kv_begin, kv_end;
@@ -334,6 +335,10 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
   for (const auto& d : dec) {
     const int64_t keys = d.kv_end - d.kv_begin;
     const int32_t n = static_cast<int32_t>(std::max<int64_t>(1, (keys + split - 1) / split));
+    // items of more than 16 rows go to the two-block decode kernel (kind 2),
+    // whose splits take two 16-row partial slots each
+    const bool two = d.q_count * group > 16;
+    std::vector<rpa_work_item>& dst = two ? out->decode2 : out->decode;
     for (int32_t g = 0; g < p.num_kv_heads; ++g) {
       rpa_work_item base{};
       base.seq = d.seq;
@@ -341,7 +346,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
       base.q_start = d.q_start;
       base.q_count = d.q_count;
       base.q_pos0 = d.pos0;
-      base.kind = 1;
+      base.kind = two ? 2 : 1;
       base.num_splits = n;
       if (n == 1) {
         base.kv_begin = d.kv_begin;
@@ -349,12 +354,12 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
         base.split_group = -1;
         base.split_index = 0;
         base.partial_base = 0;
-        out->decode.push_back(base);
+        dst.push_back(base);
         continue;
       }
       base.split_group = static_cast<int32_t>(out->groups.size());
       base.partial_base = out->num_partials;
-      out->num_partials += n;
+      out->num_partials += n * (two ? 2 : 1);
       split_bounds(d.kv_begin, d.kv_end, n);
       for (int32_t i = 0; i < n; ++i) {
         rpa_work_item it = base;
@@ -367,14 +372,15 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
           grp.kv_end = d.kv_end;
           out->groups.push_back(grp);
         }
-        out->decode.push_back(it);
+        dst.push_back(it);
       }
     }
   }
-  std::stable_sort(out->decode.begin(), out->decode.end(),
-                   [](const rpa_work_item& a, const rpa_work_item& b) {
-                     return (a.kv_end - a.kv_begin) > (b.kv_end - b.kv_begin);
-                   });
+  auto longest_first = [](const rpa_work_item& a, const rpa_work_item& b) {
+    return (a.kv_end - a.kv_begin) > (b.kv_end - b.kv_begin);
+  };
+  std::stable_sort(out->decode.begin(), out->decode.end(), longest_first);
+  std::stable_sort(out->decode2.begin(), out->decode2.end(), longest_first);
 }
 
 }  // namespace rpa

@@ -21,7 +21,10 @@ struct PlanParams {
   int64_t max_q_tokens = 0;
   int prefill_rows = 128;      // query rows (tokens x grouped heads) per prefill tile
   int prefill_wgs_per_cu = 1;  // prefill workgroups one compute unit holds at once
-  int decode_max_rows = 16;    // most rows of one decode item
+  int decode_max_rows = 0;     // most rows of one decode item, 0 = the tuning table
+                               // (decode_rows_limit); items of up to 16 rows run the one-block
+                               // decode kernel, of 17..32 rows the two-block one (head sizes
+                               // up to 256; 512 stops at 16)
   int decode_wave_keys = 32;   // keys one decode wave takes per step
   int decode_waves = 4;        // waves of one decode workgroup
   int64_t decode_split_keys = 0;  // 0: automatic
@@ -38,9 +41,11 @@ struct PlanParams {
 
 struct Plan {
   std::vector<rpa_work_item> prefill;  // launch order
-  std::vector<rpa_work_item> decode;   // launch order
+  std::vector<rpa_work_item> decode;   // launch order, items of up to 16 rows (kind 1)
+  std::vector<rpa_work_item> decode2;  // launch order, items of 17..32 rows (kind 2)
   std::vector<rpa_work_item> groups;   // one entry per split group (its split 0)
-  int num_partials = 0;                // 16-row partial-result slots (a prefill split takes rows/16)
+  int num_partials = 0;                // 16-row partial-result slots (a prefill split takes rows/16,
+                                       // a two-block decode split 2)
   int prefill_split_keys = 0;          // keys per prefill split chosen (0: none split)
   int decode_split_keys = 0;
   int64_t visible_pairs = 0;
@@ -60,6 +65,26 @@ int validate_metadata(const PlanParams& p, const int32_t* cu_q_lens, const int32
 // Builds the work lists (metadata must have passed validate_metadata).
 void build_plan(const PlanParams& p, const int32_t* cu_q_lens, const int32_t* kv_lens,
                 int32_t num_seqs, int32_t window, Plan* out);
+
+// The tuning table's decode regime: the most rows (query tokens x grouped
+// heads) of a sequence that the decode kernels take; sequences with more
+// rows go to the prefill kernel.  Measured on MI355X (128 sequences, keys
+// U[64, 1024], 32-row steps: G = 32 x 1 token, G = 8 x 4 tokens):
+//   bf16 cache: the prefill kernel (its few-row items cut into short key
+//     pieces) is as fast as the two-block decode kernel at head sizes 64
+//     and 128 and 22 % faster at 256 (where the two-block kernel holds one
+//     wave per SIMD) -> 16 rows;
+//   fp8 cache: the prefill kernel first stages the sequences' pages to bf16,
+//     so the two-block decode kernel, which converts in registers, is 1.5-2x
+//     faster (d 64: 14.3 against 24.6 us; d 128: 17.6 against 33.9; d 256:
+//     38.8 against 56.5) -> 32 rows for head sizes up to 256.
+// Head size 512 has no two-block kernel: 16 rows.  A non-zero
+// RPA_OPT_DECODE_MAX_ROWS replaces the table's value (within that cap).
+inline int decode_rows_limit(const PlanParams& p) {
+  const int cap = p.head_dim <= 256 ? 32 : 16;
+  const int want = p.decode_max_rows > 0 ? p.decode_max_rows : (p.stage_prefill ? 32 : 16);
+  return want < cap ? want : cap;
+}
 
 // Number of visible keys of query position `pos` (keys 0..pos, clipped by the window).
 inline int64_t visible_keys(int64_t pos, int32_t window) {

@@ -164,7 +164,10 @@ def test_set_option_validation():
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_PATH, 3) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_WAVES, 6) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_WAVES, 8) == _lib.RPA_OK
-    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_MAX_ROWS, 17) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_MAX_ROWS, 33) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_MAX_ROWS, -1) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_MAX_ROWS, 0) == _lib.RPA_OK
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_MAX_ROWS, 17) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_DECODE_SPLIT_KEYS, -5) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, 999, 0) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_PATH, 1) == _lib.RPA_OK
@@ -195,7 +198,7 @@ def test_kernel_times_validation_and_empty_read():
     count = ctypes.c_int32(-7)
     buf = (ctypes.c_float * 4)()
     assert lib.rpa_kernel_times(None, 0, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
-    assert lib.rpa_kernel_times(ctx, 5, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_kernel_times(ctx, 6, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_kernel_times(ctx, -1, buf, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_kernel_times(ctx, 0, buf, -1, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_kernel_times(ctx, 0, None, 4, ctypes.byref(count)) == _lib.RPA_ERR_INVALID_ARG

@@ -41,7 +41,10 @@ def check_plan(w, cu, kv, info, items):
         assert it["q_pos0"] == kv[s] - (cu[s + 1] - cu[s]) + (it["q_start"] - cu[s])
         if it["kind"] == 1:
             assert it["q_count"] * g_ratio <= 16
+        elif it["kind"] == 2:
+            assert 16 < it["q_count"] * g_ratio <= 32 and w.head_dim <= 256
         else:
+            assert it["kind"] == 0
             assert it["q_count"] * g_ratio <= info["prefill_rows"]
         for t in range(it["q_start"], it["q_start"] + it["q_count"]):
             cover.setdefault((t, g), []).append(it)
@@ -83,7 +86,7 @@ def check_plan(w, cu, kv, info, items):
     used = []
     for grp in {(it["split_group"], it["partial_base"], it["num_splits"], it["kind"])
                 for it in items if it["split_group"] >= 0}:
-        per = 1 if grp[3] == 1 else info["prefill_rows"] // 16
+        per = {1: 1, 2: 2}.get(grp[3], info["prefill_rows"] // 16)
         used.extend(range(grp[1], grp[1] + grp[2] * per))
     assert len(used) == len(set(used))
     assert all(0 <= u < info["num_partials"] for u in used)
@@ -127,19 +130,20 @@ def test_plan_options_keep_coverage(options):
 
 @pytest.mark.parametrize("w", WORKLOADS, ids=lambda w: w.name + f"_w{w.window}_g{w.num_q_heads // w.num_kv_heads}")
 def test_all_decode_path_chunks_every_sequence(w):
-    """Path 3 (the path of fp8 calls): every token in decode items of at most
-    16 rows, long sequences in consecutive chunks; with G > 16 no decode item
-    fits and the prefill kernel keeps the sequences."""
+    """Path 3: every token in decode items of at most 16 rows (the bf16
+    table), long sequences in consecutive chunks; with G above that no decode
+    item fits and the prefill kernel keeps the sequences."""
     cu, kv, info, items = plan_for(w, [(RPA_OPT_PATH, 3)])
     check_plan(w, cu, kv, info, items)
     g_ratio = w.num_q_heads // w.num_kv_heads
-    if g_ratio <= 16:
+    limit = 16
+    if g_ratio <= limit:
         assert info["num_prefill_items"] == 0
-        per = 16 // g_ratio
+        per = limit // g_ratio
         for it in items:
             if it["split_index"] == 0:
                 s = it["seq"]
-                # chunks start at multiples of 16 / G tokens of their sequence
+                # chunks start at multiples of limit / G tokens of their sequence
                 assert (it["q_start"] - cu[s]) % per == 0
                 assert it["q_count"] == min(per, cu[s + 1] - it["q_start"])
     else:
@@ -172,13 +176,18 @@ def test_long_prefill_items_are_split_when_they_would_dominate():
 
 
 def test_few_row_prefill_items_split_finer():
-    """Single tokens of 32 grouped heads (too many rows for a decode item) go to
-    the prefill kernel with a quarter of its tile's rows.  Their key ranges are
-    cut into pieces of the average per workgroup slot (two d = 128 prefill
-    workgroups per compute unit), rounded up to 128 keys, at least 128; items
-    with full tiles keep the 512-key floor (the mixed step above)."""
+    """Single tokens of 32 grouped heads (too many rows for a decode item of
+    the bf16 table) go to the prefill kernel with a quarter of its tile's
+    rows.  Their key ranges are cut into pieces of the average per
+    workgroup slot (two d = 128 prefill workgroups per compute unit), rounded
+    up to 128 keys, at least 128; items with full tiles keep the 512-key floor
+    (the mixed step above).  With decode items of up to 32 rows the same
+    step runs two-block decode items."""
     rng = np.random.default_rng(7)
     w = wl.custom([(1, int(k)) for k in rng.integers(64, 2049, 128)], 32, 1, 128, 128, 0, seed=312)
+    cu, kv, info, items = plan_for(w, [(RPA_OPT_DECODE_MAX_ROWS, 32)])
+    check_plan(w, cu, kv, info, items)
+    assert info["num_prefill_items"] == 0 and all(it["kind"] == 2 for it in items)
     cu, kv, info, items = plan_for(w)
     check_plan(w, cu, kv, info, items)
     assert info["num_decode_items"] == 0
@@ -201,11 +210,54 @@ def test_fixed_prefill_split_keeps_coverage(piece):
 
 
 def test_decode_selection_rule():
-    # q_len * G <= 16 -> decode kernel
-    w = wl.custom([(1, 50), (2, 50), (3, 50)], 8, 1, 256, 128, 0, 9)
+    # bf16 table: q_len * G <= 16 -> decode kernel, more -> prefill
+    w = wl.custom([(1, 50), (2, 50), (3, 50), (4, 50), (5, 50)], 8, 1, 256, 128, 0, 9)
     cu, kv, info, items = plan_for(w)
     kinds = {it["seq"]: it["kind"] for it in items}
+    assert kinds == {0: 1, 1: 1, 2: 0, 3: 0, 4: 0}
+    # the option raises the rows of a decode item: 17..32 -> two-block decode kernel
+    kinds = {it["seq"]: it["kind"] for it in plan_for(w, [(RPA_OPT_DECODE_MAX_ROWS, 32)])[3]}
+    assert kinds == {0: 1, 1: 1, 2: 2, 3: 2, 4: 0}
+    # head size 512 has no two-block decode kernel
+    w = wl.custom([(1, 50), (2, 50), (3, 50)], 8, 1, 512, 128, 0, 9)
+    kinds = {it["seq"]: it["kind"] for it in plan_for(w, [(RPA_OPT_DECODE_MAX_ROWS, 32)])[3]}
     assert kinds == {0: 1, 1: 1, 2: 0}
+    # and a lower cap keeps more sequences on the prefill kernel
+    w = wl.custom([(1, 50), (2, 50), (3, 50)], 8, 1, 256, 128, 0, 9)
+    kinds = {it["seq"]: it["kind"] for it in plan_for(w, [(RPA_OPT_DECODE_MAX_ROWS, 8)])[3]}
+    assert kinds == {0: 1, 1: 0, 2: 0}
+
+
+# The (head size, group, regime) table the planner follows for a bf16
+# cache: for each head size d and group G, a sequence of q_len tokens has
+# q_len * G rows; up to 16 rows run the decode kernel (kind 1), more rows the
+# prefill kernel (kind 0) with its tile of prefill_rows rows.  (An fp8 cache
+# sends 17..32 rows to the two-block decode kernel at d <= 256; the GPU tests
+# check that half of the table, whose plans rpa_plan does not expose.)
+TABLE_ROWS = {64: 256, 128: 128, 256: 256, 512: 128}
+
+
+def table_kind(d, rows, fp8=False):
+    if rows <= 16:
+        return 1
+    if fp8 and rows <= 32 and d <= 256:
+        return 2
+    return 0
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("g", [1, 2, 4, 8, 16, 32])
+def test_tuning_table(d, g):
+    """Every (head size, group) pair in each regime: single-token decode,
+    few-token steps (2 and 4 tokens), a short chunk and a long prefill."""
+    q_lens = [1, 2, 4, 9, 300]
+    w = wl.custom([(q, q + 200) for q in q_lens], g, 1, d, 64, 0, 11)
+    cu, kv, info, items = plan_for(w)
+    check_plan(w, cu, kv, info, items)
+    assert info["prefill_rows"] == TABLE_ROWS[d]
+    for s, q in enumerate(q_lens):
+        kinds = {it["kind"] for it in items if it["seq"] == s}
+        assert kinds == {table_kind(d, q * g)}, (d, g, q, kinds)
 
 
 def test_prefill_tile_rows_and_longest_first():
