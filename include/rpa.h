@@ -172,8 +172,13 @@ int rpa_forward_noalloc(rpa_ctx* ctx, const void* q, const void* k_pages, const 
  *                 k_new / v_new must not overlap them
  *   all other arguments as for rpa_forward (kv_len counts the new tokens)
  *
- * The copy runs on `stream` before the attention kernels (which then see the
- * new rows); page slots of different tokens must be distinct (a page table
+ * The rows are written on `stream` within the call, and every product of
+ * the call sees them.  A sequence whose new tokens all sit in one decode
+ * item (rpa_work_item.self_append) has them written by the decode kernel
+ * itself: the wave that reads the 32-key chunk holding a new key writes that
+ * key's rows just before it reads the chunk.  The rows of every other
+ * sequence are written by a copy kernel that runs before the attention
+ * kernels.  Page slots of different tokens must be distinct (a page table
  * that maps two positions to one slot leaves either row there).  Errors as
  * for rpa_forward, plus RPA_ERR_INVALID_ARG for a NULL k_new / v_new or
  * k_pages == v_pages.
@@ -385,6 +390,9 @@ typedef struct rpa_work_item {
   int32_t kind;         /* 0: prefill kernel item, 1: decode kernel item (<= 16
                            rows), 2: two-block decode kernel item (17..32 rows);
                            a split group has the kind of its splits               */
+  int32_t self_append;  /* 1: a decode item holding every new token of its
+                           sequence; in an appending call it writes their K/V
+                           rows itself (the split whose key range holds them) */
 } rpa_work_item;
 
 typedef struct rpa_plan_info {

@@ -974,7 +974,10 @@ struct DecodeCfg {
 // them to the same bf16 operand layout.  The K scale joins the score scale
 // and the V scale the output weight (both are per KV head, so they factor
 // out of the dot products).
-template <int D, int NW, bool UNI, bool KV8, int RB = 1>
+// AP: an appending call (the fused KV write of the items holding all of
+// their sequence's new tokens); a separate instantiation, so that plain calls
+// carry none of its code.
+template <int D, int NW, bool UNI, bool KV8, int RB = 1, bool AP = false>
 __global__ void __launch_bounds__(NW * 64, (D >= 512 || (RB == 2 && D >= 256)) ? 1 : 2)
 rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   using C = DecodeCfg<D, NW, RB>;
@@ -1052,9 +1055,89 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   const int n_chunks = (kv_end - chunk0 + 31) / 32;
   const int row_bytes = static_cast<int>(row_stride) * ESZ;   // bytes between key rows of a page
   int next_page = 0;
-  if constexpr (UNI) {
-    if (wave < n_chunks) next_page = uniform_load(pt_row, (chunk0 + wave * 32) / page_size);
+  auto first_page = [&]() {
+    if constexpr (UNI) {
+      if (wave < n_chunks) next_page = uniform_load(pt_row, (chunk0 + wave * 32) / page_size);
+    }
+  };
+
+  // ---- fused KV write (appending calls, AP) ----
+  // An item that holds every new token of its sequence writes the new K/V
+  // rows whose keys lie in its key range into their page slots itself (the
+  // new tokens are the last keys of the sequence, so one split of a group
+  // holds each): the rows go through HBM once and no other launch is needed.
+  // Each new key's rows are written by the wave that takes the key's chunk,
+  // before that wave loads the chunk, so the wave reads them back from the
+  // pages in its own program order (a wave-scope release and acquire, no
+  // barrier): the loop below is the same as for a call without new rows,
+  // and the other waves start their loads without waiting.  With an fp8
+  // cache the rows are quantized on the way, and the chunk load converts the
+  // stored bytes as it does every other key's.  A lane's first row piece is
+  // requested before the first chunk's page id, so that the two wait on one
+  // memory round trip rather than two.
+  if constexpr (AP) {
+    int new_lo = 0, n_new = 0;
+    if (it.self_append != 0) {
+      new_lo = it.q_pos0 > kv_begin ? it.q_pos0 : kv_begin;
+      const int new_hi = it.q_pos0 + it.q_count < kv_end ? it.q_pos0 + it.q_count : kv_end;
+      n_new = new_hi > new_lo ? new_hi - new_lo : 0;
+    }
+    constexpr int CH = D / 8;   // 16-byte pieces of a bf16 row
+    const int pieces = 2 * n_new * CH;
+    // piece i: the K (i < n_new*CH) or V row of key new_lo + r, piece c
+    auto piece = [&](int i, int& which, int& key, int& c) {
+      which = i >= n_new * CH;
+      const int rem = i - which * n_new * CH;
+      const int r = rem / CH;
+      c = rem - r * CH;
+      key = new_lo + r;
+    };
+    auto mine = [&](int key) { return ((key - chunk0) / 32) % NW == wave; };
+    auto src_of = [&](int key, int c) {
+      return (static_cast<int64_t>(it.q_start + (key - it.q_pos0)) * hkv + g) * D + c * 8;
+    };
+    u32x4 x0 = u32x4{0, 0, 0, 0};
+    int page0 = 0;
+    bool first = false;
+    if (lane < pieces) {
+      int which, key, c;
+      piece(lane, which, key, c);
+      first = mine(key);
+      if (first) {
+        x0 = load16((which ? args.v_new : args.k_new) + src_of(key, c));
+        page0 = pt_row[key / page_size];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    first_page();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = lane; i < pieces; i += 64) {
+      int which, key, c;
+      piece(i, which, key, c);
+      if (!mine(key)) continue;
+      u32x4 x = x0;
+      int page = page0;
+      if (i != lane || !first) {
+        x = load16((which ? args.v_new : args.k_new) + src_of(key, c));
+        page = pt_row[key / page_size];
+      }
+      const int64_t slot =
+          ((static_cast<int64_t>(page) * page_size + (key - (key / page_size) * page_size)) * hkv + g) * D + c * 8;
+      if constexpr (KV8) {
+        uint8_t* pool = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(which ? v_pages : k_pages));
+        *reinterpret_cast<u32x2*>(pool + slot) = bf16x8_to_e4m3x8(x, which ? args.v_scales[g] : args.k_scales[g]);
+      } else {
+        uint16_t* pool = const_cast<uint16_t*>(which ? v_pages : k_pages);
+        *reinterpret_cast<u32x4*>(pool + slot) = x;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    first_page();
   }
+
   for (int ch = wave; ch < n_chunks; ch += NW) {
     const int k0 = chunk0 + ch * 32;
     // keys of this lane: K rows k0 + 16*kb + ln; V rows k0 + 4*lq + j and k0 + 16 + 4*lq + j
@@ -1144,7 +1227,6 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) vf[u][j] = e4m3x8_to_bf16x8(vr[u][j]);
     }
-
     u32x4 pf[RB];
     float alpha[RB];
 #pragma unroll
@@ -1359,7 +1441,9 @@ rpa_append_kernel(const rpa_work_item* __restrict__ items, const int32_t* __rest
                   const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
                   uint16_t* __restrict__ k_dst, uint16_t* __restrict__ v_dst, KernelArgs args) {
   const rpa_work_item it = items[blockIdx.x];
-  if (it.split_index != 0) return;
+  // decode items that hold all of their sequence's new tokens write them
+  // themselves (the decode kernel's fused write)
+  if (it.split_index != 0 || it.self_append != 0) return;
   constexpr int CH = D / 8;   // 16-byte chunks per row
   const int hkv = args.num_kv_heads;
   const int ps = args.page_size;
@@ -1466,21 +1550,28 @@ static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, hipStream_t
   return launch_prefill_u<D, BN, NW, NB, NS, DS, false>(a, n_items, stream);
 }
 
-template <int D, int NW, bool UNI, bool KV8 = false, int RB = 1>
-static hipError_t launch_decode_u(const KernelArgs& a, int n_items, hipStream_t stream) {
+template <int D, int NW, bool UNI, bool KV8, int RB, bool AP>
+static hipError_t launch_decode_v(const KernelArgs& a, int n_items, hipStream_t stream) {
   using C = DecodeCfg<D, NW, RB>;
   if constexpr (C::LDS_BYTES > 64 * 1024) {   // beyond the default dynamic LDS limit
     static bool attr_set = false;
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_decode_kernel<D, NW, UNI, KV8, RB>),
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_decode_kernel<D, NW, UNI, KV8, RB, AP>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
   }
-  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, UNI, KV8, RB>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream,
+  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, UNI, KV8, RB, AP>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream,
                      a.items, a.page_table, a.q, a.k, a.v, a);
   return hipGetLastError();
+}
+
+// Appending calls (new rows given) run the AP form, with four waves.
+template <int D, int NW, bool UNI, bool KV8 = false, int RB = 1>
+static hipError_t launch_decode_u(const KernelArgs& a, int n_items, hipStream_t stream) {
+  if (a.k_new != nullptr) return launch_decode_v<D, 4, UNI, KV8, RB, true>(a, n_items, stream);
+  return launch_decode_v<D, NW, UNI, KV8, RB, false>(a, n_items, stream);
 }
 
 // Eight-wave workgroups are not used for D = 512: two waves per SIMD cannot

@@ -87,6 +87,8 @@ static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
   a.prefill_rows = prefill_rows_for(l.head_dim);
   a.k_scales = l.k_scales;
   a.v_scales = l.v_scales;
+  a.k_new = static_cast<const uint16_t*>(l.k_new);
+  a.v_new = static_cast<const uint16_t*>(l.v_new);
   return a;
 }
 

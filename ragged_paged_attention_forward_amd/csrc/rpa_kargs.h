@@ -29,6 +29,8 @@ struct KernelArgs {
   int32_t prefill_rows;  // rows of a prefill tile (rows of a prefill split's partial block)
   const float* k_scales; // fp8 pools: K scale per KV head (else unused)
   const float* v_scales; // fp8 pools: V scale per KV head (else unused)
+  const uint16_t* k_new; // appending calls: the step's new K rows [T, Hkv, D] bf16 (else null)
+  const uint16_t* v_new; // appending calls: the step's new V rows (else null)
 };
 
 }  // namespace rpa

@@ -31,6 +31,8 @@ struct LaunchArgs {
   int32_t kv_fp8;        // 1: k / v hold OCP FP8 E4M3 bytes with per-KV-head scales
   const float* k_scales; // device [Hkv] (fp8 only)
   const float* v_scales; // device [Hkv] (fp8 only)
+  const void* k_new;     // appending calls: new K rows [T, Hkv, D] bf16 (else null)
+  const void* v_new;     // appending calls: new V rows (else null)
   void* stream;
 };
 

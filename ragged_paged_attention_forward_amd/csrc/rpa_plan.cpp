@@ -211,6 +211,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
 
   struct DecodeSeq {
     int32_t seq, q_start, q_count, pos0, kv_begin, kv_end;
+    bool whole;   // the item holds every token of its sequence
   };
   std::vector<DecodeSeq> dec;
 
@@ -224,7 +225,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
     const bool fits_decode = dec_tokens > 0 && q_len <= dec_tokens;
     const bool use_decode = p.path_mode != 1 && fits_decode;
     if (use_decode) {
-      dec.push_back({s, cu[s], q_len, pos_first, range_begin(pos_first, window), kv_len});
+      dec.push_back({s, cu[s], q_len, pos_first, range_begin(pos_first, window), kv_len, true});
       continue;
     }
     if (p.path_mode == 3 && dec_tokens > 0) {
@@ -233,7 +234,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
       for (int32_t t = 0; t < q_len; t += dec_tokens) {
         const int32_t count = std::min(dec_tokens, q_len - t);
         const int32_t pos0 = pos_first + t;
-        dec.push_back({s, cu[s] + t, count, pos0, range_begin(pos0, window), pos0 + count});
+        dec.push_back({s, cu[s] + t, count, pos0, range_begin(pos0, window), pos0 + count, count == q_len});
       }
       continue;
     }
@@ -347,6 +348,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
       base.q_count = d.q_count;
       base.q_pos0 = d.pos0;
       base.kind = two ? 2 : 1;
+      base.self_append = d.whole ? 1 : 0;
       base.num_splits = n;
       if (n == 1) {
         base.kv_begin = d.kv_begin;
@@ -381,6 +383,9 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
   };
   std::stable_sort(out->decode.begin(), out->decode.end(), longest_first);
   std::stable_sort(out->decode2.begin(), out->decode2.end(), longest_first);
+  out->append_items = 0;
+  for (const auto* list : {&out->prefill, &out->decode, &out->decode2})
+    for (const auto& it : *list) out->append_items += (it.split_index == 0 && it.self_append == 0) ? 1 : 0;
 }
 
 }  // namespace rpa

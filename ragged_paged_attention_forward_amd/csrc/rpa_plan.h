@@ -50,6 +50,8 @@ struct Plan {
   int decode_split_keys = 0;
   int64_t visible_pairs = 0;
   int64_t total_q = 0;
+  int32_t append_items = 0;            // items whose new rows the append kernel writes (the others
+                                       // write their own in the decode kernel)
   // Staging (stage_prefill): three ints per staged page (sequence, page of
   // the sequence, page of the bf16 pool), and the bf16 pool's page table
   // [num_seqs * max_pages_per_seq] (rows of staged sequences; 0 elsewhere).

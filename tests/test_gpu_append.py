@@ -85,13 +85,26 @@ def test_append_matches_forward_on_filled_pages_bitwise():
 
 
 def test_append_kernel_is_timed():
-    w = wl.decode()
+    """A mixed step runs the append kernel for its prefill chunks (timed as its
+    own kind); a step of decodes only writes every new row in the decode
+    kernel (the fused write) and launches no append kernel."""
+    w = mixed_small(0)
     attn = make_attn(w)
     attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
     run_append(w, attn)
     t = attn.kernel_times(R.RPA_KERNEL_APPEND)
     assert len(t) == 1 and t[0] > 0
     assert len(attn.kernel_times(R.RPA_KERNEL_DECODE)) == 1
+    w = wl.decode()
+    attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
+    inp, (k_new, k_stale, v_new, v_stale), kp, vp, out = run_append(w, attn)
+    assert len(attn.kernel_times(R.RPA_KERNEL_APPEND)) == 0
+    assert len(attn.kernel_times(R.RPA_KERNEL_DECODE)) == 1
+    want_k, want_v = ora.append_kv(k_stale, v_stale, inp.page_table, inp.cu_q_lens, inp.kv_lens, k_new, v_new)
+    assert torch.equal(kp.cpu().view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(vp.cpu().view(torch.int16), want_v.view(torch.int16))
+    compare(out, oracle_rows(inp), label="decode, fused write")
 
 
 @pytest.mark.parametrize("path", [1, 2])
