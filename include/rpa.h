@@ -279,8 +279,7 @@ enum {
                                     run the one-block decode kernel, of 17..32
                                     the two-block one; head size 512: at most
                                     16); 0 (default) = the tuning table: 16 for
-                                    a bf16 cache, 32 for an fp8 cache (its
-                                    prefill path stages pages first)           */
+                                    a bf16 cache, 32 for an fp8 cache          */
   RPA_OPT_DECODE_WAVES = 5,      /* waves per decode workgroup: 0 automatic
                                     (4), 4, 8 (head size 512 always runs 4)     */
   RPA_OPT_KERNEL_TIMING = 6,     /* n > 0: time up to n launches per kernel kind
@@ -301,12 +300,21 @@ enum {
                                     by half), -1 = never split, > 0 = split every
                                     item longer than 1.5x this many keys (rounded
                                     up to 256); <= 2^30                         */
-  RPA_OPT_CONCURRENT = 10        /* 1 (default): when a step has both decode
+  RPA_OPT_CONCURRENT = 10,       /* 1 (default): when a step has both decode
                                     and prefill items, the decode kernel runs
                                     on a second stream of
                                     the context, forked from and joined back
                                     into the caller's stream; 0: both kernels
                                     on the caller's stream                      */
+  RPA_OPT_FP8_STAGE = 11         /* fp8 calls with prefill items: 1 (default)
+                                    a staging kernel first converts the pages
+                                    those items read into a bf16 pool (value
+                                    times scale, rounded to bf16) that the
+                                    bf16 prefill kernel reads; 0 the prefill
+                                    kernel loads the E4M3 tiles and converts
+                                    them to bf16 in LDS itself (no staging
+                                    pass, half the tile bytes; slower on
+                                    MI355X at every head size measured)         */
 };
 /* Returns RPA_OK or RPA_ERR_INVALID_ARG (unknown option or bad value). */
 int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);

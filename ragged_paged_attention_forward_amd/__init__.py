@@ -25,13 +25,13 @@ from ._lib import (RPA_ERR_HIP, RPA_ERR_INVALID_ARG, RPA_ERR_OOM, RPA_ERR_UNSUPP
                    RPA_KERNEL_STAGE, RPA_KERNEL_DECODE2, RPA_OK,
                    RPA_OPT_DECODE_MAX_ROWS, RPA_OPT_DECODE_SPLIT_KEYS, RPA_OPT_DECODE_WAVES,
                    RPA_OPT_FUSED_MERGE, RPA_OPT_KERNEL_TIMING, RPA_OPT_PATH, RPA_OPT_XCD_GROUPS,
-                   RPA_OPT_PREFILL_SPLIT_KEYS, RPA_OPT_CONCURRENT,
+                   RPA_OPT_PREFILL_SPLIT_KEYS, RPA_OPT_CONCURRENT, RPA_OPT_FP8_STAGE,
                    PlanInfo, RpaError, WorkItem)
 
 __all__ = ["RaggedPagedAttention", "rpa_forward", "RpaError", "library_path", "RPA_OK",
            "RPA_ERR_INVALID_ARG", "RPA_ERR_UNSUPPORTED", "RPA_ERR_OOM", "RPA_ERR_HIP",
            "RPA_OPT_DECODE_SPLIT_KEYS", "RPA_OPT_PATH", "RPA_OPT_DECODE_MAX_ROWS",
-           "RPA_OPT_DECODE_WAVES", "RPA_OPT_KERNEL_TIMING", "RPA_OPT_XCD_GROUPS", "RPA_OPT_FUSED_MERGE", "RPA_OPT_PREFILL_SPLIT_KEYS", "RPA_OPT_CONCURRENT", "RPA_KERNEL_PREFILL", "RPA_KERNEL_DECODE",
+           "RPA_OPT_DECODE_WAVES", "RPA_OPT_KERNEL_TIMING", "RPA_OPT_XCD_GROUPS", "RPA_OPT_FUSED_MERGE", "RPA_OPT_PREFILL_SPLIT_KEYS", "RPA_OPT_CONCURRENT", "RPA_OPT_FP8_STAGE", "RPA_KERNEL_PREFILL", "RPA_KERNEL_DECODE",
            "RPA_KERNEL_MERGE", "RPA_KERNEL_APPEND", "RPA_KERNEL_STAGE", "RPA_KERNEL_DECODE2", "KERNEL_KINDS", "probe_read", "probe_mfma",
            "probe_e4m3"]
 

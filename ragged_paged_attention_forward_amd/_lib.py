@@ -22,6 +22,7 @@ RPA_OPT_XCD_GROUPS = 7
 RPA_OPT_FUSED_MERGE = 8
 RPA_OPT_PREFILL_SPLIT_KEYS = 9
 RPA_OPT_CONCURRENT = 10
+RPA_OPT_FP8_STAGE = 11
 
 RPA_KERNEL_PREFILL = 0
 RPA_KERNEL_DECODE = 1

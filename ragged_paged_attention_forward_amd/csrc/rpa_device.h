@@ -274,6 +274,9 @@ RPA_DEV void wait_vmem() { wait_vmem_le<0>(); }
 // `later` tiles of `LPT` loads each were staged after it.
 template <int LPT, int MAXLATER>
 RPA_DEV void wait_tile_loads(int later) {
+  if constexpr (MAXLATER >= 3) {
+    if (later >= 3) { wait_vmem_le<3 * LPT>(); return; }
+  }
   if constexpr (MAXLATER >= 2) {
     if (later >= 2) { wait_vmem_le<2 * LPT>(); return; }
   }
@@ -301,7 +304,7 @@ RPA_DEV void sched_reads_ahead() {
   }
 }
 
-template <int D, int BN, int NW, int NB, int NS, int DS = 1>
+template <int D, int BN, int NW, int NB, int NS, int DS = 1, bool KV8 = false>
 struct PrefillCfg {
   static constexpr int NT = NW * 64;
   static constexpr int DH = D / DS;                  // head columns per wave
@@ -327,10 +330,23 @@ struct PrefillCfg {
   static constexpr int TILE_K = BLOCKS * BLK_K;
   static constexpr int TILE_V = BLOCKS * BLK_V;
   static constexpr int STAGE_B = TILE_K + TILE_V;
-  static constexpr int LDS_BYTES = NS * STAGE_B;     // NS tiles in flight
   static constexpr int LOADS = BLOCKS / NW;          // 1 KB direct loads per wave per tensor
-  static constexpr int LPT = 2 * LOADS;              // load instructions per wave per tile
+  // KV8 (an E4M3 cache): the NS stages in flight hold the tiles' bytes as
+  // loaded (BN rows of D bytes, K then V), and CB tiles in the bf16 layout
+  // above are converted from them inside the kernel: two when that still
+  // lets a compute unit hold as many workgroups as the bf16 form (the next
+  // tile is converted while the current one is used), else one (converted
+  // after the current one's products).
+  static constexpr int STAGE8 = 2 * BN * D;
+  static constexpr int LOADS8 = BN * D / 1024 / NW;  // 1 KB direct loads per wave per tensor
+  static constexpr int WGS = (160 * 1024) / (NS * STAGE_B) < 8 * 64 / NT ? (160 * 1024) / (NS * STAGE_B)
+                                                                           : 8 * 64 / NT;   // bf16 form, per CU
+  static constexpr int CB = 2 * STAGE_B + NS * STAGE8 <= (160 * 1024) / (WGS > 0 ? WGS : 1) ? 2 : 1;
+  static constexpr int LDS_BYTES = KV8 ? CB * STAGE_B + NS * STAGE8 : NS * STAGE_B;
+  static constexpr int LPT = 2 * (KV8 ? LOADS8 : LOADS);   // load instructions per wave per tile
   static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  static_assert(!KV8 || (LOADS8 >= 1 && (BN * D) % (1024 * NW) == 0), "fp8 tile must split into 1 KB loads per wave");
+  static_assert(!KV8 || (BN * D / 16) % NT == 0, "fp8 tile conversion: whole 16-byte pieces per thread");
   static_assert((NS - 2) * LPT < 64, "vmcnt field");
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert(BLOCKS % NW == 0, "tile must split into 1 KB loads per wave");
@@ -342,10 +358,10 @@ struct PrefillCfg {
 
 RPA_DEV int xor_k(int s) { return s & 1; }
 
-template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI>
+template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI, bool KV8 = false>
 __global__ void __launch_bounds__(NW * 64, 1)
 rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
-  using C = PrefillCfg<D, BN, NW, NB, NS, DS>;
+  using C = PrefillCfg<D, BN, NW, NB, NS, DS, KV8>;
   constexpr int DH = C::DH;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   char* lds = reinterpret_cast<char*>(smem);
@@ -373,6 +389,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   const uint16_t* __restrict__ vbase = v_pages;
   const int page_size = args.page_size;
   const int row_bytes = hkv * D * 2;   // bytes between consecutive key rows of a page
+  const int row_bytes8 = hkv * D;      // the same for an E4M3 cache
 
   // Page ids of the key range, one per lane, 64 at a time (pw_ids holds pages
   // pw_base ..), loaded ahead of Q so that the first tile's staging does not
@@ -443,7 +460,14 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     return tile0 + u * BN;
   };
   const int window = args.window;
-  const float sl2 = args.scale_log2;
+  // An E4M3 cache: the K scale joins the score scale and the V scale the
+  // output weight (both are per KV head, so they factor out of the products).
+  float sl2 = args.scale_log2;
+  float vsc = 1.f;
+  if constexpr (KV8) {
+    sl2 *= uniform_load(args.k_scales, g);
+    vsc = uniform_load(args.v_scales, g);
+  }
 
   // ---- direct HBM -> LDS staging of one K/V tile ----
   // Load i of this wave fills block wave*LOADS + i of the K and V tiles; lane
@@ -475,6 +499,27 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     st_slot = kr - st_pidx * page_size;
   }
 
+  // page slot row (page * page_size + slot) of the next tile's first key; advances
+  auto next_tile_row = [&]() -> int64_t {
+    if (static_cast<unsigned>(st_pidx - pw_base) >= 64u) {   // left the window (ranges of more than 64 pages)
+      load_window(st_pidx);
+      wait_vmem();
+    }
+    const int64_t page = __builtin_amdgcn_readlane(pw_ids, st_pidx - pw_base);
+    const int64_t row = page * page_size + st_slot;
+    st_slot += BN;
+    if (st_slot == page_size) {
+      st_slot = 0;
+      ++st_pidx;
+    }
+    if (++st_u == n_tiles) {
+      st_u = 0;
+      st_pidx = wrap_pidx;
+      st_slot = wrap_slot;
+    }
+    return row;
+  };
+
   auto stage = [&](int ts, int buf) {
     const int k0 = key_of(ts);
     char* kdst = lds + buf * C::STAGE_B + wave * C::LOADS * C::BLK_K;
@@ -488,23 +533,8 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       // The tile lies in one page.  The buffer starts at row lo and ends
       // after row hi - 1: rows below lo have negative offsets, which wrap
       // above the record count, so they read as zero like rows past hi.
-      if (static_cast<unsigned>(st_pidx - pw_base) >= 64u) {   // left the window (ranges of more than 64 pages)
-        load_window(st_pidx);
-        wait_vmem();
-      }
       const int rel_b = (lo - k0) * row_bytes;
-      const int64_t page = __builtin_amdgcn_readlane(pw_ids, st_pidx - pw_base);
-      const int64_t base_off = ((page * page_size + st_slot + (lo - k0)) * hkv + g) * D;
-      st_slot += BN;
-      if (st_slot == page_size) {
-        st_slot = 0;
-        ++st_pidx;
-      }
-      if (++st_u == n_tiles) {
-        st_u = 0;
-        st_pidx = wrap_pidx;
-        st_slot = wrap_slot;
-      }
+      const int64_t base_off = ((next_tile_row() + (lo - k0)) * hkv + g) * D;
       const uint32_t nbytes = static_cast<uint32_t>((hi - lo - 1) * row_bytes + D * 2);
       const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + base_off, nbytes);
       const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + base_off, nbytes);
@@ -526,6 +556,77 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
         const int64_t off = ((page * page_size + (key - pidx * page_size)) * hkv + g) * D * 2;
         global_load_lds16(reinterpret_cast<const char*>(kbase) + off + sgk[i], kdst + i * C::BLK_K);
         global_load_lds16(reinterpret_cast<const char*>(vbase) + off + sgv[i], vdst + i * C::BLK_V);
+      }
+    }
+  };
+
+  // ---- an E4M3 cache: direct HBM -> LDS loads of the tile's bytes ----
+  // Load i of this wave fills 1 KB block wave*LOADS8 + i of the K and V bytes
+  // (rows of D bytes, no XOR), with the same range rules as stage().
+  auto stage8 = [&](int ts, int slot) {
+    const int k0 = key_of(ts);
+    char* kdst = lds + C::CB * C::STAGE_B + slot * C::STAGE8 + wave * C::LOADS8 * 1024;
+    char* vdst = kdst + BN * D;
+    const int lo = k0 > kv_begin ? k0 : kv_begin;
+    const int hi = k0 + BN < kv_end ? k0 + BN : kv_end;
+    const char* k8 = reinterpret_cast<const char*>(kbase);
+    const char* v8 = reinterpret_cast<const char*>(vbase);
+    if constexpr (UNI) {
+      const int rel_b = (lo - k0) * row_bytes8;
+      const int64_t base_off = ((next_tile_row() + (lo - k0)) * hkv + g) * D;
+      const uint32_t nbytes = static_cast<uint32_t>((hi - lo - 1) * row_bytes8 + D);
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(k8 + base_off, nbytes);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v8 + base_off, nbytes);
+#pragma unroll
+      for (int i = 0; i < C::LOADS8; ++i) {
+        const int at = (wave * C::LOADS8 + i) * 1024 + lane * 16;   // byte of the tile
+        const int off = (at / D) * row_bytes8 + at % D - rel_b;
+        buffer_load_lds16(krs, kdst + i * 1024, off);
+        buffer_load_lds16(vrs, vdst + i * 1024, off);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::LOADS8; ++i) {
+        const int at = (wave * C::LOADS8 + i) * 1024 + lane * 16;
+        int key = k0 + at / D;
+        key = key < lo ? lo : (key < hi ? key : hi - 1);
+        const int pidx = key / page_size;
+        const int64_t page = pt_row[pidx];
+        const int64_t off = ((page * page_size + (key - pidx * page_size)) * hkv + g) * D + at % D;
+        global_load_lds16(k8 + off, kdst + i * 1024);
+        global_load_lds16(v8 + off, vdst + i * 1024);
+      }
+    }
+  };
+  // E4M3 bytes of stage `slot` -> bf16 tile `cb` in the layout the products
+  // read (every E4M3 value is exact in bf16).  Thread t takes 16-byte pieces
+  // t, t + NT, ...: 16 elements of one key row, i.e. two of its 16-byte bf16
+  // chunks, each stored at its XOR position.
+  auto convert = [&](int slot, int cb) {
+    const char* src = lds + C::CB * C::STAGE_B + slot * C::STAGE8;
+    char* dst = lds + cb * C::STAGE_B;
+    // The piece offsets are recomputed at every call (a few VALU operations)
+    // rather than kept in registers across the loop: held there, they leave
+    // too few registers for the products' operand reads to run ahead.
+    int me = tid;
+    asm volatile("" : "+v"(me));
+    // unrolled where the conversion runs before the products (few registers
+    // live); rolled behind them, where unrolling spills (d = 512)
+    constexpr int UNR = C::CB == 2 ? 8 : 1;
+#pragma unroll UNR
+    for (int tv = 0; tv < 2; ++tv) {   // K, then V
+#pragma unroll UNR
+      for (int j0 = 0; j0 < BN * D / 16; j0 += C::NT) {
+        const int j = j0 + me;
+        const int sr8 = (j * 16) / D;          // key row of the tile
+        const int c = ((j * 16) % D) / 8;      // first bf16 chunk of the piece (even)
+        const int sr = sr8 % C::RPI;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src + tv * BN * D + j * 16);
+        char* d = tv == 0 ? dst + (sr8 / C::RPI) * C::BLK_K + sr * C::ROW_B
+                          : dst + C::TILE_K + (sr8 / C::RPI) * C::BLK_V + sr * C::ROW_B;
+        const int xr = tv == 0 ? xor_k(sr) : (sr & 1) * C::XV;
+        *reinterpret_cast<u32x4*>(d + (c ^ xr) * 16) = e4m3x8_to_bf16x8(u32x2{x[0], x[1]});
+        *reinterpret_cast<u32x4*>(d + ((c + 1) ^ xr) * 16) = e4m3x8_to_bf16x8(u32x2{x[2], x[3]});
       }
     }
   };
@@ -678,39 +779,19 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // NS-stage pipeline: while tile t is used, the loads of tiles t+1 ..
-  // t+NS-1 are in flight; one barrier per tile guards the reuse of a buffer.
-  // (Measured: two tiles per barrier step, or running half of the waves one
-  // phase behind the other half, are both slower on this kernel.)
-#pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
-    if (t < n_tiles) stage(t, t);
-  if constexpr (UNI) {
-    // Q and the first tiles: every load of the prologue is complete before the loop
-    wait_vmem();
-  } else {
-    // the first tile must have landed
-    const int later = (n_tiles < NS - 1 ? n_tiles : NS - 1) - 1;
-    wait_tile_loads<C::LPT, NS - 2>(later < 0 ? 0 : later);
-  }
-  __syncthreads();
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int ts = tile + NS - 1;   // into the buffer of tile - 1, released by the last barrier
-    if (ts < n_tiles) stage(ts, ts % NS);
+  // ---- the products of tile `tile`, whose K/V tile is at ks ----
+  auto products = [&](int tile, char* ks) __attribute__((always_inline)) {
     const int k0 = key_of(tile);
-    const int cur = tile % NS;
     const bool skip = tile_skipped(k0);
-    const char* ks = lds + cur * C::STAGE_B;
     f32x16 sc[BN / 32][NB];
     if (!skip) scores(ks, sc);
     if constexpr (DS == 2) {
       // ---- d split: add the partner wave's partial scores ----
-      // Every wave has finished its reads of this stage's K tile, whose space
-      // then carries the exchange (16 B per lane and store, lanes contiguous).
+      // Every wave has finished its reads of this K tile, whose space then
+      // carries the exchange (16 B per lane and store, lanes contiguous).
       // Float addition commutes, so both waves of a pair hold identical sums.
       __syncthreads();
-      f32x4* xb = reinterpret_cast<f32x4*>(lds + cur * C::STAGE_B);
+      f32x4* xb = reinterpret_cast<f32x4*>(ks);
       if (!skip) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -731,13 +812,80 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       softmax(sc, k0, pf);
       pv(pf, ks);
     }
-    // the next tile must have landed; later ones may still be in flight
-    {
-      const int staged_last = (tile + NS - 1 < n_tiles ? tile + NS - 1 : n_tiles - 1);
-      const int later = staged_last - (tile + 1);
+  };
+
+  if constexpr (!KV8) {
+    // NS-stage pipeline: while tile t is used, the loads of tiles t+1 ..
+    // t+NS-1 are in flight; one barrier per tile guards the reuse of a buffer.
+    // (Measured: two tiles per barrier step, or running half of the waves one
+    // phase behind the other half, are both slower on this kernel.)
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < n_tiles) stage(t, t);
+    if constexpr (UNI) {
+      // Q and the first tiles: every load of the prologue is complete before the loop
+      wait_vmem();
+    } else {
+      // the first tile must have landed
+      const int later = (n_tiles < NS - 1 ? n_tiles : NS - 1) - 1;
       wait_tile_loads<C::LPT, NS - 2>(later < 0 ? 0 : later);
     }
     __syncthreads();
+
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      const int ts = tile + NS - 1;   // into the buffer of tile - 1, released by the last barrier
+      if (ts < n_tiles) stage(ts, ts % NS);
+      products(tile, lds + (tile % NS) * C::STAGE_B);
+      // the next tile must have landed; later ones may still be in flight
+      {
+        const int staged_last = (tile + NS - 1 < n_tiles ? tile + NS - 1 : n_tiles - 1);
+        const int later = staged_last - (tile + 1);
+        wait_tile_loads<C::LPT, NS - 2>(later < 0 ? 0 : later);
+      }
+      __syncthreads();
+    }
+  } else {
+    // An E4M3 cache: NS stages of loaded bytes and CB converted bf16 tiles.
+    // At the barrier that opens step t, bf16 tile t is complete and stage t
+    // has been converted, so step t loads tile t+NS into it.  With two bf16
+    // tiles, step t converts tile t+1 (landed before that barrier) into the
+    // tile that t-1 used, before the products of tile t; with one, it
+    // converts tile t+1 after them, behind a second barrier.
+    for (int t = 0; t < NS; ++t)
+      if (t < n_tiles) stage8(t, t);
+    if constexpr (UNI) {
+      // Q and the first tiles: every load of the prologue is complete before the loop
+      wait_vmem();
+    } else {
+      const int later = (n_tiles < NS ? n_tiles : NS) - 1;   // tiles staged after tile 0
+      wait_tile_loads<C::LPT, NS - 1>(later < 0 ? 0 : later);
+    }
+    __syncthreads();
+    if (n_tiles > 0) convert(0, 0);
+    if constexpr (C::CB == 2) {
+      const int later = (n_tiles < NS ? n_tiles : NS) - 2;   // tiles staged after tile 1
+      wait_tile_loads<C::LPT, NS - 1>(later < 0 ? 0 : later);
+    }
+    __syncthreads();
+
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      if (tile + NS < n_tiles) stage8(tile + NS, tile % NS);
+      const int staged_last = tile + NS < n_tiles ? tile + NS : n_tiles - 1;
+      if constexpr (C::CB == 2) {
+        if (tile + 1 < n_tiles) convert((tile + 1) % NS, (tile + 1) & 1);
+        products(tile, lds + (tile & 1) * C::STAGE_B);
+        // the bytes of tile + 2 must have landed; later ones may be in flight
+        const int later = staged_last - (tile + 2);
+        wait_tile_loads<C::LPT, NS - 1>(later < 0 ? 0 : later);
+      } else {
+        products(tile, lds);
+        const int later = staged_last - (tile + 1);   // tile + 1 must have landed
+        wait_tile_loads<C::LPT, NS - 1>(later < 0 ? 0 : later);
+        __syncthreads();   // every wave is done with the bf16 tile
+        if (tile + 1 < n_tiles) convert((tile + 1) % NS, 0);
+      }
+      __syncthreads();
+    }
   }
 
   constexpr int OROWS = NB * 32;   // rows per wave
@@ -751,7 +899,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float l = l_run[nb] + __shfl_xor(l_run[nb], 32);
-      inv[nb] = l > 0.f ? 1.f / l : 0.f;
+      inv[nb] = l > 0.f ? vsc / l : 0.f;
       const float base = (m_run[nb] == kNegInf) ? 0.f : m_run[nb];
       const int r = (rw * NB + nb) * 32 + n32;
       if (lq2 == 0 && dh == 0 && r / G < it.q_count)
@@ -849,7 +997,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float l = l_run[nb] + __shfl_xor(l_run[nb], 32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l > 0.f ? vsc / l : 0.f;
     char* srow = ost + (nb * 32 + n32) * OP + lq2 * 8;
 #pragma unroll
     for (int db = 0; db < DH / 32; ++db) {
@@ -1527,27 +1675,33 @@ rpa_stage_kernel(const int32_t* __restrict__ stage, const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI>
+template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI, bool KV8>
 static hipError_t launch_prefill_u(const KernelArgs& a, int n_items, hipStream_t stream) {
-  using C = PrefillCfg<D, BN, NW, NB, NS, DS>;
+  using C = PrefillCfg<D, BN, NW, NB, NS, DS, KV8>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, NS, DS, UNI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, NS, DS, UNI, KV8>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, NS, DS, UNI>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
+  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, NS, DS, UNI, KV8>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
                      stream, a.items, a.page_table, a.q, a.k, a.v, a);
   return hipGetLastError();
 }
 
 template <int D, int BN, int NW, int NB, int NS, int DS>
-static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, hipStream_t stream) {
+static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, bool kv8, hipStream_t stream) {
   // one buffer descriptor per tile needs the tile inside one page and 32-bit offsets
-  const bool uni = a.page_size % BN == 0 && int64_t(a.page_size) * a.num_kv_heads * D * 2 < (int64_t(1) << 31);
-  if (uni) return launch_prefill_u<D, BN, NW, NB, NS, DS, true>(a, n_items, stream);
-  return launch_prefill_u<D, BN, NW, NB, NS, DS, false>(a, n_items, stream);
+  const int esz = kv8 ? 1 : 2;
+  const bool uni = a.page_size % BN == 0 && int64_t(a.page_size) * a.num_kv_heads * D * esz < (int64_t(1) << 31);
+  if (kv8) {
+    if (uni) return launch_prefill_u<D, BN, NW, NB, NS, DS, true, true>(a, n_items, stream);
+    return launch_prefill_u<D, BN, NW, NB, NS, DS, false, true>(a, n_items, stream);
+  }
+  if (uni) return launch_prefill_u<D, BN, NW, NB, NS, DS, true, false>(a, n_items, stream);
+  return launch_prefill_u<D, BN, NW, NB, NS, DS, false, false>(a, n_items, stream);
 }
 
 template <int D, int NW, bool UNI, bool KV8, int RB, bool AP>
@@ -1654,8 +1808,8 @@ constexpr int prefill_wgs_per_cu() {
 
 // Defines the per-head-size entry points called by rpa_dispatch.cpp.
 #define RPA_DEFINE_HEAD_DIM(D)                                                              \
-  hipError_t launch_prefill_d##D(const KernelArgs& a, int n, hipStream_t s) {               \
-    return launch_prefill_t<RPA_PREFILL_SHAPE_##D>(a, n, s);                               \
+  hipError_t launch_prefill_d##D(const KernelArgs& a, int n, bool kv8, hipStream_t s) {     \
+    return launch_prefill_t<RPA_PREFILL_SHAPE_##D>(a, n, kv8, s);                          \
   }                                                                                         \
   hipError_t launch_decode_d##D(const KernelArgs& a, int n, int waves, bool kv8, int rows,    \
                                 hipStream_t s) {                                            \

@@ -9,7 +9,7 @@
 
 namespace rpa {
 
-hipError_t launch_prefill_d64(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_prefill_d64(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d64(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
@@ -17,7 +17,7 @@ hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const v
 hipError_t launch_stage_d64(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d64();
 int prefill_wgs_per_cu_d64();
-hipError_t launch_prefill_d128(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_prefill_d128(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
@@ -25,7 +25,7 @@ hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const 
 hipError_t launch_stage_d128(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d128();
 int prefill_wgs_per_cu_d128();
-hipError_t launch_prefill_d256(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_prefill_d256(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
@@ -33,7 +33,7 @@ hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const 
 hipError_t launch_stage_d256(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d256();
 int prefill_wgs_per_cu_d256();
-hipError_t launch_prefill_d512(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_prefill_d512(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_append_d512(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
@@ -96,11 +96,12 @@ hipError_t launch_prefill(const LaunchArgs& l, const rpa_work_item* items, int n
   if (n_items <= 0) return hipSuccess;
   const KernelArgs a = make_args(l, items);
   hipStream_t s = static_cast<hipStream_t>(l.stream);
+  const bool kv8 = l.kv_fp8 != 0;
   switch (l.head_dim) {
-    case 64: return launch_prefill_d64(a, n_items, s);
-    case 128: return launch_prefill_d128(a, n_items, s);
-    case 256: return launch_prefill_d256(a, n_items, s);
-    case 512: return launch_prefill_d512(a, n_items, s);
+    case 64: return launch_prefill_d64(a, n_items, kv8, s);
+    case 128: return launch_prefill_d128(a, n_items, kv8, s);
+    case 256: return launch_prefill_d256(a, n_items, kv8, s);
+    case 512: return launch_prefill_d512(a, n_items, kv8, s);
     default: return hipErrorInvalidValue;
   }
 }

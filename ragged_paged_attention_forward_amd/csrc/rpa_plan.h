@@ -35,8 +35,10 @@ struct PlanParams {
   int xcd_groups = 8;          // prefill order: workgroups b, b+X, b+2X, ... share a
                                // chiplet (and its L2); <= 1 keeps the plain order
   int xcd_run = 4;             // consecutive items dealt to one chiplet at a time
-  bool stage_prefill = false;  // fp8 calls: the pages of sequences with prefill items are
-                               // staged into a bf16 pool that the prefill kernel reads
+  bool kv8 = false;            // an fp8 (E4M3) cache
+  bool stage_prefill = false;  // fp8 calls (RPA_OPT_FP8_STAGE): the pages of sequences with
+                               // prefill items are staged into a bf16 pool that the prefill
+                               // kernel reads
 };
 
 struct Plan {
@@ -84,7 +86,7 @@ void build_plan(const PlanParams& p, const int32_t* cu_q_lens, const int32_t* kv
 // RPA_OPT_DECODE_MAX_ROWS replaces the table's value (within that cap).
 inline int decode_rows_limit(const PlanParams& p) {
   const int cap = p.head_dim <= 256 ? 32 : 16;
-  const int want = p.decode_max_rows > 0 ? p.decode_max_rows : (p.stage_prefill ? 32 : 16);
+  const int want = p.decode_max_rows > 0 ? p.decode_max_rows : (p.kv8 ? 32 : 16);
   return want < cap ? want : cap;
 }
 

@@ -179,6 +179,10 @@ def test_set_option_validation():
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_CONCURRENT, 2) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_CONCURRENT, 0) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_CONCURRENT, 1) == _lib.RPA_OK
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FP8_STAGE, 2) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FP8_STAGE, -1) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FP8_STAGE, 1) == _lib.RPA_OK
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FP8_STAGE, 0) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_PREFILL_SPLIT_KEYS, -2) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_PREFILL_SPLIT_KEYS, (1 << 30) + 1) == _lib.RPA_ERR_INVALID_ARG
     for v in (-1, 0, 512, 1 << 30):

@@ -80,14 +80,18 @@ def test_keys_before_the_window_are_never_read(name):
         compare(out, ref, label=f"{name} path {path}")
 
 
-@pytest.mark.parametrize("name", ["d256_b16_first_tile_spans_pages", "d256_b128_prefill_and_decode", "d512_b16"])
-def test_fp8_keys_before_the_window_are_never_read(name):
-    """The fp8 path stages only pages from the first key its prefill items
-    read: a first tile that starts below that key must not look up an
-    unstaged page (the staged pool's table holds 0 there)."""
+@pytest.mark.parametrize("stage", [0, 1])
+@pytest.mark.parametrize("name", ["d256_b16_first_tile_spans_pages", "d256_b128_prefill_and_decode", "d512_b16",
+                                  "d128_b32_g16", "d64_b16"])
+def test_fp8_keys_before_the_window_are_never_read(name, stage):
+    """Both fp8 prefill routes: the prefill kernel's E4M3 tile loads clamp to
+    the item's key range like the bf16 ones, and the staging route stages
+    only pages from the first key its prefill items read (a first tile that
+    starts below that key must not look up an unstaged page: the staged
+    pool's table holds 0 there)."""
     seqs, hq, hkv, d, b, window = BEFORE_WINDOW[name]
     w = wl.custom(seqs, hq, hkv, d, b, window, seed=62)
-    print(f"fp8 before-window poison {name}", flush=True)
+    print(f"fp8 before-window poison {name} stage {stage}", flush=True)
     f = wl.make_fp8_inputs(w, poison=True)
     base = f.base
     ref = ora.forward_fp8_rows(base.q, f.k_pages, f.v_pages, f.k_scales, f.v_scales, base.page_table,
@@ -95,6 +99,7 @@ def test_fp8_keys_before_the_window_are_never_read(name):
     k, v, pt = poison_before_window(f.k_pages, f.v_pages, base.page_table, base.cu_q_lens, base.kv_lens, window,
                                     b, base.trap_page, wl.NAN_E4M3)
     attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_FP8_STAGE, stage)
     out = attn.forward_fp8(base.q.cuda(), k.cuda(), v.cuda(), f.k_scales.cuda(), f.v_scales.cuda(), pt.cuda(),
                            base.cu_q_lens, base.kv_lens, window, base.scale)
     torch.cuda.synchronize()

@@ -45,12 +45,13 @@ CASES = {
 }
 
 
-def run_fp8(f: wl.Fp8Inputs, attn=None, path=0):
+def run_fp8(f: wl.Fp8Inputs, attn=None, path=0, stage=1):
     d = f.to("cuda")
     b = f.base
     if attn is None:
         attn = make_attn(b.workload)
         attn.set_option(R.RPA_OPT_PATH, path)
+        attn.set_option(R.RPA_OPT_FP8_STAGE, stage)
     out = attn.forward_fp8(d.base.q, d.k_pages, d.v_pages, d.k_scales, d.v_scales, d.base.page_table,
                            b.cu_q_lens, b.kv_lens, b.window, b.scale)
     torch.cuda.synchronize()
@@ -76,51 +77,82 @@ def test_e4m3_conversion_matches_torch_for_every_byte():
     assert torch.equal(g[~nan], w[~nan])
 
 
-@pytest.mark.parametrize("path", [0, 3], ids=["staged_prefill", "all_decode"])
+ROUTES = {"prefill_converts": (0, 0), "staged_prefill": (0, 1), "all_decode": (3, 1)}
+
+
+@pytest.mark.parametrize("route", list(ROUTES))
 @pytest.mark.parametrize("name", list(CASES))
-def test_fp8_parity(name, path):
-    """Path 0: prefill sequences through the staged bf16 pool and the prefill
-    kernel, the rest through the decode kernel; path 3: every token through
+def test_fp8_parity(name, route):
+    """prefill_converts: prefill sequences through the prefill kernel, which
+    loads the E4M3 tiles and converts them in LDS, the rest through the
+    decode kernel; staged_prefill: the same after a staging kernel has
+    converted their pages into a bf16 pool; all_decode: every token through
     the decode kernel (G <= 16)."""
+    path, stage = ROUTES[route]
     w = CASES[name]()
-    print(f"fp8 parity {name} path {path}: seqs={w.num_seqs} T={w.total_q} d={w.head_dim} B={w.page_size} "
+    print(f"fp8 parity {name} {route}: seqs={w.num_seqs} T={w.total_q} d={w.head_dim} B={w.page_size} "
           f"W={w.window}", flush=True)
     f = wl.make_fp8_inputs(w, poison=True)
-    out = run_fp8(f, path=path)
+    out = run_fp8(f, path=path, stage=stage)
     compare(out, oracle_fp8(f), label=name)
 
 
+def tile_edge_rows(attn, f):
+    """First and last token row of every prefill query tile of the call's plan."""
+    b = f.base
+    _, items = attn.plan(b.cu_q_lens, b.kv_lens, b.window)
+    rows = []
+    for it in items:
+        if it["kind"] == 0:
+            rows += [it["q_start"], it["q_start"] + it["q_count"] - 1]
+    return rows
+
+
+@pytest.mark.parametrize("stage", [0, 1])
 @pytest.mark.parametrize("window", [0, 1024])
-def test_fp8_mixed_full_size_sampled(window):
+def test_fp8_mixed_full_size_sampled(window, stage):
     w = wl.mixed(window=window)
-    print(f"fp8 mixed full size W={window}: T={w.total_q}", flush=True)
+    print(f"fp8 mixed full size W={window} stage={stage}: T={w.total_q}", flush=True)
     f = wl.make_fp8_inputs(w, poison=True)
-    out = run_fp8(f)
+    attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_FP8_STAGE, stage)
+    out = run_fp8(f, attn)
     t_q = w.total_q
     rows = wl.sample_rows(t_q, 48, seed=window + 3, must=[0, 4095, 4096, t_q - 513, t_q - 1])
     compare(out, oracle_fp8(f, rows), rows=rows, label=f"mixed_w{window}")
 
 
+@pytest.mark.parametrize("stage", [0, 1])
 @pytest.mark.parametrize("name", ["swa_prefill", "global_prefill"])
-def test_fp8_prefill_full_size_sampled(name):
+def test_fp8_prefill_full_size_sampled(name, stage):
+    """Full-size fp8 prefills, both prefill routes: a seeded sample plus the
+    first and last row of every query tile."""
     w = wl.by_name(name)
-    print(f"fp8 {name} full size: T={w.total_q} d={w.head_dim}", flush=True)
+    print(f"fp8 {name} full size stage={stage}: T={w.total_q} d={w.head_dim}", flush=True)
     f = wl.make_fp8_inputs(w, poison=True)
-    out = run_fp8(f)
+    attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_FP8_STAGE, stage)
+    out = run_fp8(f, attn)
     t_q = w.total_q
-    rows = wl.sample_rows(t_q, 24, seed=11, must=[0, 127, 128, 1023, 1024, t_q - 1])
+    rows = wl.sample_rows(t_q, 24, seed=11, must=[0, 127, 128, 1023, 1024, t_q - 1] + tile_edge_rows(attn, f))
     compare(out, oracle_fp8(f, rows), rows=rows, label=name)
 
 
-def test_fp8_staging_kernel_is_timed():
+@pytest.mark.parametrize("stage", [0, 1])
+def test_fp8_staging_kernel_runs_only_when_asked(stage):
+    """The staging kernel (timed as its own kind) runs with RPA_OPT_FP8_STAGE
+    = 1 (the default) and not with 0, where the prefill kernel reads the
+    E4M3 pages itself; both routes match the oracle."""
     w = CASES["mixed_small_w0"]()
     f = wl.make_fp8_inputs(w, poison=True)
     attn = make_attn(w)
     attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
-    run_fp8(f, attn)
-    assert len(attn.kernel_times(R.RPA_KERNEL_STAGE)) == 1
+    attn.set_option(R.RPA_OPT_FP8_STAGE, stage)
+    out = run_fp8(f, attn)
+    assert len(attn.kernel_times(R.RPA_KERNEL_STAGE)) == stage
     assert len(attn.kernel_times(R.RPA_KERNEL_PREFILL)) == 1
     assert len(attn.kernel_times(R.RPA_KERNEL_DECODE)) == 1
+    compare(out, oracle_fp8(f), label=f"stage {stage}")
 
 
 def test_fp8_is_bitwise_reproducible():
