@@ -320,6 +320,15 @@ def graph_layers(torch, attn, replicas, w, cu, kv, layers: int, stream):
             "replays": reps}
 
 
+def library_options(args):
+    """(name, value) pairs of --set NAME=VALUE (RPA_OPT_<NAME> of the library)."""
+    out = []
+    for item in args.set or []:
+        name, _, value = item.partition("=")
+        out.append((name.strip().upper(), int(value)))
+    return out
+
+
 def measure(args, workload: str, torch, R, dev, graph_layers_n: int = 0):
     """Time one workload: K wall-clock steps (``value``, ``ms_per_step``), then
     the event-timed pass for each kernel's duration and the roofline of the
@@ -351,6 +360,8 @@ def measure(args, workload: str, torch, R, dev, graph_layers_n: int = 0):
 
     attn = R.RaggedPagedAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
                                   w.num_seqs, w.max_pages_per_seq, t_q)
+    for name, value in library_options(args):
+        attn.set_option(getattr(R, "RPA_OPT_" + name), value)
     info, items = attn.plan(cu, kv, w.window)
     # host metadata builder: one rpa_plan call (work list built, not copied out), best of 20
     plan_s = []
@@ -487,6 +498,7 @@ def measure(args, workload: str, torch, R, dev, graph_layers_n: int = 0):
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "page_size": w.page_size, "window": w.window, "replicas": reps, "append_kv": bool(args.append),
                    "kv_dtype": "fp8_e4m3" if fp8 else "bf16",
+                   "options": {n: v for n, v in library_options(args)},
                    "parallelism": "single GPU"},
         "step_tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -772,6 +784,9 @@ def main(argv=None):
     ap.add_argument("--decode-max-rows", type=int, default=0,
                     help="with --table: RPA_OPT_DECODE_MAX_ROWS for every call (0: the library's table), to time "
                          "the choices the table does not make")
+    ap.add_argument("--set", action="append", metavar="NAME=VALUE",
+                    help="library option RPA_OPT_<NAME> for every call of the run (repeatable), "
+                         "e.g. --set CONCURRENT=0 or --set FP8_STAGE=0")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run the elementwise calibration kernel (for counter runs)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),

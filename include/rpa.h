@@ -208,11 +208,14 @@ int rpa_forward_append(rpa_ctx* ctx, const void* q, const void* k_new, const voi
  *
  * The work is planned as for rpa_forward.  The split-KV decode kernel reads
  * the bytes itself and converts them to bf16 exactly in registers (the K
- * scale joins the score scale, the V scale the output weight).  For the
- * sequences the prefill kernel serves, a staging kernel first converts
+ * scale joins the score scale, the V scale the output weight).  The
+ * sequences the prefill kernel serves take one of two routes
+ * (RPA_OPT_FP8_STAGE; by default chosen by head size): the prefill kernel
+ * loads each E4M3 tile into LDS and converts it there exactly (the scales
+ * applied as in the decode kernel), or a staging kernel first converts
  * their pages to bf16 (value times scale, rounded to nearest even) in a
  * pool the context owns (grown on demand, like the split workspace), which
- * the prefill kernel then reads through the pool's own page table; both run
+ * the prefill kernel then reads through the pool's own page table; all run
  * on `stream`.  With RPA_OPT_PATH = 3 every token goes through the decode
  * kernel instead (no staging).  Errors as for rpa_forward, plus
  * RPA_ERR_INVALID_ARG for a NULL scale array.
@@ -306,15 +309,17 @@ enum {
                                     the context, forked from and joined back
                                     into the caller's stream; 0: both kernels
                                     on the caller's stream                      */
-  RPA_OPT_FP8_STAGE = 11         /* fp8 calls with prefill items: 1 (default)
-                                    a staging kernel first converts the pages
-                                    those items read into a bf16 pool (value
-                                    times scale, rounded to bf16) that the
-                                    bf16 prefill kernel reads; 0 the prefill
-                                    kernel loads the E4M3 tiles and converts
-                                    them to bf16 in LDS itself (no staging
-                                    pass, half the tile bytes; slower on
-                                    MI355X at every head size measured)         */
+  RPA_OPT_FP8_STAGE = 11         /* fp8 calls with prefill items: 1 a staging
+                                    kernel first converts the pages those
+                                    items read into a bf16 pool (value times
+                                    scale, rounded to bf16) that the bf16
+                                    prefill kernel reads; 0 the prefill kernel
+                                    loads the E4M3 tiles (half the bytes) and
+                                    converts them to bf16 in LDS itself; 2
+                                    (default) by head size: 0 for 64 and 256,
+                                    whose tiles leave room to convert the next
+                                    tile while the current one is used, 1 for
+                                    128 and 512                                  */
 };
 /* Returns RPA_OK or RPA_ERR_INVALID_ARG (unknown option or bad value). */
 int rpa_set_option(rpa_ctx* ctx, int32_t option, int64_t value);

@@ -1827,6 +1827,7 @@ constexpr int prefill_wgs_per_cu() {
     return launch_stage_t<D>(a, st, n, kd, vd, s);                                          \
   }                                                                                         \
   int prefill_rows_d##D() { return PrefillCfg<RPA_PREFILL_SHAPE_##D>::ROWS; }              \
-  int prefill_wgs_per_cu_d##D() { return prefill_wgs_per_cu<PrefillCfg<RPA_PREFILL_SHAPE_##D>>(); }
+  int prefill_wgs_per_cu_d##D() { return prefill_wgs_per_cu<PrefillCfg<RPA_PREFILL_SHAPE_##D>>(); } \
+  int prefill_fp8_tiles_d##D() { return PrefillCfg<RPA_PREFILL_SHAPE_##D, true>::CB; }
 
 }  // namespace rpa

@@ -17,6 +17,7 @@ hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const v
 hipError_t launch_stage_d64(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d64();
 int prefill_wgs_per_cu_d64();
+int prefill_fp8_tiles_d64();
 hipError_t launch_prefill_d128(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d128(const KernelArgs& a, int n, hipStream_t s);
@@ -25,6 +26,7 @@ hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const 
 hipError_t launch_stage_d128(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d128();
 int prefill_wgs_per_cu_d128();
+int prefill_fp8_tiles_d128();
 hipError_t launch_prefill_d256(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d256(const KernelArgs& a, int n, hipStream_t s);
@@ -33,6 +35,7 @@ hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const 
 hipError_t launch_stage_d256(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d256();
 int prefill_wgs_per_cu_d256();
+int prefill_fp8_tiles_d256();
 hipError_t launch_prefill_d512(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d512(const KernelArgs& a, int n, hipStream_t s);
@@ -41,6 +44,7 @@ hipError_t launch_append_d512(const KernelArgs& a, int n, const void* kn, const 
 hipError_t launch_stage_d512(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
 int prefill_rows_d512();
 int prefill_wgs_per_cu_d512();
+int prefill_fp8_tiles_d512();
 
 int prefill_rows_for(int head_dim) {
   switch (head_dim) {
@@ -53,6 +57,16 @@ int prefill_rows_for(int head_dim) {
 }
 
 bool head_dim_supported(int head_dim) { return prefill_rows_for(head_dim) > 0; }
+
+int prefill_fp8_tiles_for(int head_dim) {
+  switch (head_dim) {
+    case 64: return prefill_fp8_tiles_d64();
+    case 128: return prefill_fp8_tiles_d128();
+    case 256: return prefill_fp8_tiles_d256();
+    case 512: return prefill_fp8_tiles_d512();
+    default: return 1;
+  }
+}
 
 int prefill_wgs_per_cu_for(int head_dim) {
   switch (head_dim) {

@@ -40,6 +40,10 @@ struct LaunchArgs {
 int prefill_rows_for(int head_dim);
 // Prefill workgroups one compute unit holds at once for a head size.
 int prefill_wgs_per_cu_for(int head_dim);
+// bf16 tiles the prefill kernel's E4M3 form converts into per workgroup: 2
+// (the next tile is converted while the current one is used) or 1 (after
+// its products, behind a second barrier).
+int prefill_fp8_tiles_for(int head_dim);
 bool head_dim_supported(int head_dim);
 
 hipError_t launch_prefill(const LaunchArgs& a, const rpa_work_item* items, int n_items);

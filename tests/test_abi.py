@@ -179,7 +179,8 @@ def test_set_option_validation():
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_CONCURRENT, 2) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_CONCURRENT, 0) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_CONCURRENT, 1) == _lib.RPA_OK
-    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FP8_STAGE, 2) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FP8_STAGE, 3) == _lib.RPA_ERR_INVALID_ARG
+    assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FP8_STAGE, 2) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FP8_STAGE, -1) == _lib.RPA_ERR_INVALID_ARG
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FP8_STAGE, 1) == _lib.RPA_OK
     assert lib.rpa_set_option(ctx, _lib.RPA_OPT_FP8_STAGE, 0) == _lib.RPA_OK

@@ -45,7 +45,7 @@ CASES = {
 }
 
 
-def run_fp8(f: wl.Fp8Inputs, attn=None, path=0, stage=1):
+def run_fp8(f: wl.Fp8Inputs, attn=None, path=0, stage=2):
     d = f.to("cuda")
     b = f.base
     if attn is None:
@@ -77,7 +77,7 @@ def test_e4m3_conversion_matches_torch_for_every_byte():
     assert torch.equal(g[~nan], w[~nan])
 
 
-ROUTES = {"prefill_converts": (0, 0), "staged_prefill": (0, 1), "all_decode": (3, 1)}
+ROUTES = {"prefill_converts": (0, 0), "staged_prefill": (0, 1), "all_decode": (3, 2)}
 
 
 @pytest.mark.parametrize("route", list(ROUTES))
@@ -138,18 +138,19 @@ def test_fp8_prefill_full_size_sampled(name, stage):
     compare(out, oracle_fp8(f, rows), rows=rows, label=name)
 
 
-@pytest.mark.parametrize("stage", [0, 1])
+@pytest.mark.parametrize("stage", [0, 1, 2])
 def test_fp8_staging_kernel_runs_only_when_asked(stage):
     """The staging kernel (timed as its own kind) runs with RPA_OPT_FP8_STAGE
-    = 1 (the default) and not with 0, where the prefill kernel reads the
-    E4M3 pages itself; both routes match the oracle."""
+    = 1 and not with 0, where the prefill kernel reads the E4M3 pages itself;
+    with 2 (the default) the head size decides (d = 64, 256: no staging); every
+    route matches the oracle."""
     w = CASES["mixed_small_w0"]()
     f = wl.make_fp8_inputs(w, poison=True)
     attn = make_attn(w)
     attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
     attn.set_option(R.RPA_OPT_FP8_STAGE, stage)
     out = run_fp8(f, attn)
-    assert len(attn.kernel_times(R.RPA_KERNEL_STAGE)) == stage
+    assert len(attn.kernel_times(R.RPA_KERNEL_STAGE)) == (1 if stage == 1 else 0)   # d = 256
     assert len(attn.kernel_times(R.RPA_KERNEL_PREFILL)) == 1
     assert len(attn.kernel_times(R.RPA_KERNEL_DECODE)) == 1
     compare(out, oracle_fp8(f), label=f"stage {stage}")

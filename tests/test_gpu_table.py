@@ -4,7 +4,7 @@ cache type) table: for each head size d in {64, 128, 256, 512} and group G in
 steps, a short chunk and a long prefill, so every regime the table assigns
 for that (d, G) runs -- with a bf16 cache the decode kernel (<= 16 rows) and
 the prefill kernel; with an fp8 cache also the two-block decode kernel (17..32
-rows, d <= 256) and the staged prefill -- and is compared element by element
+rows, d <= 256) and the fp8 prefill route of the head size -- and is compared element by element
 with the oracle (page tails and the trap page hold NaN).  The two-block kernel
 is also checked on bf16 caches (selected by RPA_OPT_DECODE_MAX_ROWS) with key
 splits (fused and separate merge), windows and small pages."""
@@ -76,7 +76,10 @@ def test_table_entry_parity_fp8(d, g):
     kinds = {table_kind(d, q * g, fp8=True) for q in Q_LENS}
     for k, kind in KIND_TIMING.items():
         assert (len(attn.kernel_times(kind)) > 0) == (k in kinds), (d, g, k)
-    assert len(attn.kernel_times(R.RPA_KERNEL_STAGE)) == 1   # the long prefill is always there
+    # the long prefill is always there: staged pages, except at d = 64 and 256,
+    # whose E4M3 tiles the prefill kernel converts itself (RPA_OPT_FP8_STAGE's
+    # default: two bf16 tiles fit there)
+    assert len(attn.kernel_times(R.RPA_KERNEL_STAGE)) == (0 if d in (64, 256) else 1)
 
 
 TWO_BLOCK = {
