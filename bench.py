@@ -426,14 +426,19 @@ def measure(args, workload: str, torch, R, dev, graph_layers_n: int = 0):
 
     # Kernel durations: up to --timing-steps of the same steps again with the library's HIP events
     # around every kernel.  A sleep kernel queued first lets the host run
-    # ahead, so that no kernel waits for its own launch inside its brackets.
+    # ahead, so that no kernel waits for its own launch inside its brackets;
+    # untimed steps between the sleep and the timed ones bring the device
+    # back to the clock it holds under the steady load of the timed region.
     timed = min(args.steps, args.timing_steps)
-    head_ms = 1.5 * enqueue_ms * timed + 1.0
-    attn.set_option(R.RPA_OPT_KERNEL_TIMING, timed)
+    settle = max(4, int(np.ceil(2.0 / max(wall * 1e3 / args.steps, 1e-3))))   # about 2 ms of steps
+    head_ms = 1.5 * enqueue_ms * (timed + settle) + 1.0
     torch.cuda.synchronize()
     torch.cuda._sleep(int(head_ms * sleep_cycles_per_ms(torch)))
-    for i in range(timed):
+    for i in range(settle):
         step(1 + args.warmup + args.steps + i)
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, timed)
+    for i in range(timed):
+        step(1 + args.warmup + args.steps + settle + i)
     torch.cuda.synchronize()
     kernels = {}
     for name, kind in R.KERNEL_KINDS.items():
