@@ -107,6 +107,29 @@ def test_append_kernel_is_timed():
     compare(out, oracle_rows(inp), label="decode, fused write")
 
 
+@pytest.mark.parametrize("name, seqs, hq, hkv, d, b, window", [
+    ("g8_d256_four_tokens", [(4, 200 + 131 * i) for i in range(24)], 8, 1, 256, 128, 700),
+    ("g32_d128_pages16", [(1, 64 + 97 * i) for i in range(30)], 32, 1, 128, 16, 0),
+    ("g16_d64_two_tokens", [(2, 50 + 61 * i) for i in range(30)], 16, 1, 64, 32, 0),
+])
+def test_append_in_two_block_decode_items(name, seqs, hq, hkv, d, b, window):
+    """The two-block decode kernel (17..32 rows, selected by
+    RPA_OPT_DECODE_MAX_ROWS) writes its items' new rows itself as well:
+    byte-exact pools, no append kernel, attention within the bar."""
+    w = wl.custom(seqs, hq, hkv, d, b, window, seed=81)
+    print(f"two-block append {name}", flush=True)
+    attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_DECODE_MAX_ROWS, 32)
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
+    inp, (k_new, k_stale, v_new, v_stale), kp, vp, out = run_append(w, attn)
+    assert len(attn.kernel_times(R.RPA_KERNEL_DECODE2)) == 1
+    assert len(attn.kernel_times(R.RPA_KERNEL_APPEND)) == 0
+    want_k, want_v = ora.append_kv(k_stale, v_stale, inp.page_table, inp.cu_q_lens, inp.kv_lens, k_new, v_new)
+    assert torch.equal(kp.cpu().view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(vp.cpu().view(torch.int16), want_v.view(torch.int16))
+    compare(out, oracle_rows(inp), label=name)
+
+
 @pytest.mark.parametrize("path", [1, 2])
 def test_append_through_one_kernel_kind(path):
     """Every sequence through the prefill kernel (path 1: the append kernel
