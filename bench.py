@@ -67,7 +67,8 @@ CSRC = os.path.join(ROOT, "ragged_paged_attention_forward_amd", "csrc")
 COPY_BYTES = 1 << 30            # calibration buffer (read once, written once)
 KERNEL_NAMES = {"prefill": "rpa_prefill_kernel", "decode": "rpa_decode_kernel", "merge": "rpa_merge_kernel",
                 "append": "rpa_append_kernel", "stage": "rpa_stage_kernel", "decode2": "rpa_decode_kernel"}
-WORKLOADS = ("decode", "tiny", "swa_prefill", "global_prefill", "mixed", "mixed_swa")
+WORKLOADS = ("decode", "tiny", "swa_prefill", "global_prefill", "mixed", "mixed_swa", "swa_prefill_share8",
+             "global_prefill_share2")
 # read-probe shapes swept for the measured HBM ceiling: (workgroups, threads,
 # 16-byte loads in flight per thread), from one workgroup per compute unit
 # with deep queues to many small workgroups

@@ -293,10 +293,12 @@ enum {
                                     (workgroup b runs on chiplet b mod X; MI355X
                                     has 8, the default); 0 or 1 = plain
                                     longest-first order; <= 64                  */
-  RPA_OPT_FUSED_MERGE = 8,       /* 1 (default): the split (decode or prefill)
-                                    that finishes last merges its group's
+  RPA_OPT_FUSED_MERGE = 8,       /* 1 (default): the decode split that
+                                    finishes last merges its group's
                                     partials; 0: a separate merge kernel does
-                                    (same result)                               */
+                                    (same result).  Prefill splits are always
+                                    merged by the merge kernel (a tile's rows
+                                    spread over several workgroups)             */
   RPA_OPT_PREFILL_SPLIT_KEYS = 9, /* keys per split of a long prefill item: 0 =
                                     automatic (split only when the longest item
                                     exceeds the average work of a compute unit

@@ -892,8 +892,8 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   if (it.split_group >= 0) {
     // ---- a split of a long item: normalised fp32 O and base-2 LSE per row ----
     // Row r of split i sits at row i * ROWS of the group's partial block; the
-    // split that draws the group's last ticket merges the block (the same
-    // arithmetic and the same uncached workspace as the decode splits).
+    // merge kernel that follows the launch merges the block (the same
+    // arithmetic as the decode splits' merge).
     const int64_t prow = static_cast<int64_t>(it.partial_base) * 16 + static_cast<int64_t>(it.split_index) * C::ROWS;
     float inv[NB];
 #pragma unroll
@@ -962,19 +962,6 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
         }
       }
     }
-    if (!args.fused_merge) return;   // the merge kernel follows
-    // every wave's stores are complete in memory before the group's ticket is drawn
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    int* flag = reinterpret_cast<int*>(lds);   // the tile buffers are free after the loop
-    if (tid == 0)
-      *flag = __hip_atomic_fetch_add(args.merge_tickets + it.split_group, 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT) == it.num_splits - 1;
-    __syncthreads();
-    if (*flag == 0) return;
-    asm volatile("" ::: "memory");
-    merge_group<D>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, C::ROWS, tid, C::NT);
-    if (tid == 0) __hip_atomic_store(args.merge_tickets + it.split_group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
 
@@ -1086,12 +1073,16 @@ RPA_DEV void merge_group(const KernelArgs& args, int q_start, int q_count, int k
   }
 }
 
+// Workgroup (x, y) merges column slots y * THREADS .. of group x: a prefill
+// group's 128-256 rows are spread over several workgroups (one round of
+// loads each) instead of being walked by one.
 template <int D>
 __global__ void __launch_bounds__(MergeCfg<D>::THREADS) rpa_merge_kernel(KernelArgs args) {
   const rpa_work_item grp = args.groups[blockIdx.x];
   // rows per split: a prefill tile's, 16 for a decode item, 32 for a two-block one
   merge_group<D>(args, grp.q_start, grp.q_count, grp.kv_head, grp.partial_base, grp.num_splits,
-                 grp.kind == 0 ? args.prefill_rows : grp.kind == 2 ? 32 : 16, threadIdx.x, blockDim.x);
+                 grp.kind == 0 ? args.prefill_rows : grp.kind == 2 ? 32 : 16, blockIdx.y * blockDim.x + threadIdx.x,
+                 blockDim.x * gridDim.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -1782,8 +1773,10 @@ static hipError_t launch_stage_t(const KernelArgs& a, const int32_t* stage, int 
 }
 
 template <int D>
-static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, hipStream_t stream) {
-  hipLaunchKernelGGL((rpa_merge_kernel<D>), dim3(n_groups), dim3(MergeCfg<D>::THREADS), 0, stream, a);
+static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, int max_rows, hipStream_t stream) {
+  const int chunks = (max_rows * (D / 4) + MergeCfg<D>::THREADS - 1) / MergeCfg<D>::THREADS;
+  hipLaunchKernelGGL((rpa_merge_kernel<D>), dim3(n_groups, chunks > 0 ? chunks : 1), dim3(MergeCfg<D>::THREADS), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -1815,8 +1808,8 @@ constexpr int prefill_wgs_per_cu() {
                                 hipStream_t s) {                                            \
     return launch_decode_t<D>(a, n, waves, kv8, rows, s);                                   \
   }                                                                                         \
-  hipError_t launch_merge_d##D(const KernelArgs& a, int n, hipStream_t s) {                 \
-    return launch_merge_t<D>(a, n, s);                                                      \
+  hipError_t launch_merge_d##D(const KernelArgs& a, int n, int rows, hipStream_t s) {       \
+    return launch_merge_t<D>(a, n, rows, s);                                                \
   }                                                                                         \
   hipError_t launch_append_d##D(const KernelArgs& a, int n, const void* kn, const void* vn, \
                                 void* kd, void* vd, bool kv8, hipStream_t s) {              \

@@ -11,7 +11,7 @@ namespace rpa {
 
 hipError_t launch_prefill_d64(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
-hipError_t launch_merge_d64(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_merge_d64(const KernelArgs& a, int n, int rows, hipStream_t s);
 hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               bool kv8, hipStream_t s);
 hipError_t launch_stage_d64(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
@@ -20,7 +20,7 @@ int prefill_wgs_per_cu_d64();
 int prefill_fp8_tiles_d64();
 hipError_t launch_prefill_d128(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
-hipError_t launch_merge_d128(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_merge_d128(const KernelArgs& a, int n, int rows, hipStream_t s);
 hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               bool kv8, hipStream_t s);
 hipError_t launch_stage_d128(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
@@ -29,7 +29,7 @@ int prefill_wgs_per_cu_d128();
 int prefill_fp8_tiles_d128();
 hipError_t launch_prefill_d256(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
-hipError_t launch_merge_d256(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_merge_d256(const KernelArgs& a, int n, int rows, hipStream_t s);
 hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               bool kv8, hipStream_t s);
 hipError_t launch_stage_d256(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
@@ -38,7 +38,7 @@ int prefill_wgs_per_cu_d256();
 int prefill_fp8_tiles_d256();
 hipError_t launch_prefill_d512(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
-hipError_t launch_merge_d512(const KernelArgs& a, int n, hipStream_t s);
+hipError_t launch_merge_d512(const KernelArgs& a, int n, int rows, hipStream_t s);
 hipError_t launch_append_d512(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
                               bool kv8, hipStream_t s);
 hipError_t launch_stage_d512(const KernelArgs& a, const int32_t* st, int n, void* kd, void* vd, hipStream_t s);
@@ -162,15 +162,15 @@ hipError_t launch_stage(const LaunchArgs& l, const int32_t* stage, int n_pages, 
   }
 }
 
-hipError_t launch_merge(const LaunchArgs& l, int n_groups) {
+hipError_t launch_merge(const LaunchArgs& l, int n_groups, int max_rows) {
   if (n_groups <= 0) return hipSuccess;
   const KernelArgs a = make_args(l, nullptr);
   hipStream_t s = static_cast<hipStream_t>(l.stream);
   switch (l.head_dim) {
-    case 64: return launch_merge_d64(a, n_groups, s);
-    case 128: return launch_merge_d128(a, n_groups, s);
-    case 256: return launch_merge_d256(a, n_groups, s);
-    case 512: return launch_merge_d512(a, n_groups, s);
+    case 64: return launch_merge_d64(a, n_groups, max_rows, s);
+    case 128: return launch_merge_d128(a, n_groups, max_rows, s);
+    case 256: return launch_merge_d256(a, n_groups, max_rows, s);
+    case 512: return launch_merge_d512(a, n_groups, max_rows, s);
     default: return hipErrorInvalidValue;
   }
 }

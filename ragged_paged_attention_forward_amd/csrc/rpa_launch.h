@@ -49,7 +49,9 @@ bool head_dim_supported(int head_dim);
 hipError_t launch_prefill(const LaunchArgs& a, const rpa_work_item* items, int n_items);
 // rows: 16 for the one-block decode kernel, 32 for the two-block one.
 hipError_t launch_decode(const LaunchArgs& a, const rpa_work_item* items, int n_items, int rows);
-hipError_t launch_merge(const LaunchArgs& a, int n_groups);
+// Merges split groups a.groups[0 .. n_groups) (max_rows: the most rows of a
+// split among them), several workgroups per group.
+hipError_t launch_merge(const LaunchArgs& a, int n_groups, int max_rows);
 // Copies the step's new K/V rows (k_new / v_new, [T, Hkv, D]) into their page
 // slots of k_dst / v_dst, one workgroup per work item.
 hipError_t launch_append(const LaunchArgs& a, const rpa_work_item* items, int n_items, const void* k_new,

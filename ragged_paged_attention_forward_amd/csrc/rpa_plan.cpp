@@ -283,6 +283,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
   }
 
   split_long_prefill_items(p, out);
+  out->prefill_groups = static_cast<int32_t>(out->groups.size());
 
   // Longest first: the most expensive tiles start first so the tail is short.
   std::stable_sort(out->prefill.begin(), out->prefill.end(),

@@ -45,7 +45,8 @@ struct Plan {
   std::vector<rpa_work_item> prefill;  // launch order
   std::vector<rpa_work_item> decode;   // launch order, items of up to 16 rows (kind 1)
   std::vector<rpa_work_item> decode2;  // launch order, items of 17..32 rows (kind 2)
-  std::vector<rpa_work_item> groups;   // one entry per split group (its split 0)
+  std::vector<rpa_work_item> groups;   // one entry per split group (its split 0): prefill groups first
+  int32_t prefill_groups = 0;          // groups[0 .. prefill_groups) are prefill split groups
   int num_partials = 0;                // 16-row partial-result slots (a prefill split takes rows/16,
                                        // a two-block decode split 2)
   int prefill_split_keys = 0;          // keys per prefill split chosen (0: none split)

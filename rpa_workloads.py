@@ -132,10 +132,27 @@ def mixed(seed: int = SEEDS["mixed"], window: int = 0, num_decodes: int = 512) -
                     length_draw=(64, 1025, num_decodes))
 
 
+def swa_prefill_share8(seed: int = SEEDS["swa_prefill"]) -> Workload:
+    """One GPU's share of swa_prefill split by KV head over 8 GPUs: 2 q / 1 KV head."""
+    w = swa_prefill(seed, num_q_heads=2, num_kv_heads=1)
+    w.name = "swa_prefill_share8"
+    w.description += " (one GPU's share of 8)"
+    return w
+
+
+def global_prefill_share2(seed: int = SEEDS["global_prefill"]) -> Workload:
+    """One GPU's share of global_prefill split by KV head over 2 GPUs: 8 q / 1 KV head."""
+    w = global_prefill(seed, num_q_heads=8, num_kv_heads=1)
+    w.name = "global_prefill_share2"
+    w.description += " (one GPU's share of 2)"
+    return w
+
+
 def by_name(name: str) -> Workload:
     table = {"tiny": tiny, "decode": decode, "swa_prefill": swa_prefill,
              "global_prefill": global_prefill, "mixed": lambda: mixed(window=0),
-             "mixed_swa": lambda: mixed(window=1024)}
+             "mixed_swa": lambda: mixed(window=1024), "swa_prefill_share8": swa_prefill_share8,
+             "global_prefill_share2": global_prefill_share2}
     return table[name]()
 
 

@@ -53,6 +53,9 @@ FULL = {
     "global_prefill": wl.global_prefill,
     "mixed": lambda: wl.mixed(window=0),
     "mixed_swa": lambda: wl.mixed(window=1024),
+    # one GPU's share of the prefills split by KV head (8 and 2 GPUs)
+    "swa_prefill_share8": wl.swa_prefill_share8,
+    "global_prefill_share2": wl.global_prefill_share2,
 }
 
 
@@ -227,10 +230,12 @@ def test_kernel_timing_leaves_results_unchanged():
     for _ in range(3):   # the third call is past the cap and is not recorded
         timed = run_gpu(attn, inp)
         assert torch.equal(base, timed)
-    info, _ = attn.plan(inp.cu_q_lens, inp.kv_lens, w.window)
+    info, items = attn.plan(inp.cu_q_lens, inp.kv_lens, w.window)
+    prefill_splits = any(it["kind"] == 0 and it["split_group"] >= 0 for it in items)
     for kind, present in ((R.RPA_KERNEL_PREFILL, info["num_prefill_items"] > 0),
                           (R.RPA_KERNEL_DECODE, info["num_decode_items"] > 0),
-                          (R.RPA_KERNEL_MERGE, False)):   # merged inside the decode kernel
+                          # decode splits merge inside the decode kernel, prefill splits in the merge kernel
+                          (R.RPA_KERNEL_MERGE, prefill_splits)):
         t = attn.kernel_times(kind)
         assert len(t) == (2 if present else 0)
         assert np.all(t > 0) and np.all(t < 1000)
@@ -276,10 +281,11 @@ def test_fused_merge_matches_merge_kernel_bitwise(window):
     (4, 1, 64, 16, [(500, 1500), (7, 7)], 0),
 ])
 def test_prefill_splits(hq, hkv, d, b, seqs, window):
-    """Long prefill items cut along their key range: the partial results merged
-    by the last split (fused) match the oracle, give the same bits as the
-    separate merge kernel and as a repeated call (the tickets return to zero),
-    and agree with the unsplit kernel."""
+    """Long prefill items cut along their key range: the partial results,
+    merged by the merge kernel (several workgroups per group), match the
+    oracle, give the same bits whether the decode splits merge in the decode
+    kernel or in the merge kernel, and on a repeated call, and agree with the
+    unsplit kernel."""
     w = wl.custom(seqs, hq, hkv, d, b, window, seed=d + window)
     inp = wl.make_inputs(w, poison=True)
     ref = oracle_rows(inp)
@@ -289,7 +295,7 @@ def test_prefill_splits(hq, hkv, d, b, seqs, window):
     assert info["prefill_split_keys"] == 512
     assert sum(1 for it in items if it["kind"] == 0 and it["split_group"] >= 0) >= 4
     got = run_gpu(fused, inp).clone()
-    compare(got, ref, label="prefill splits, fused merge")
+    compare(got, ref, label="prefill splits")
     for _ in range(2):
         assert torch.equal(run_gpu(fused, inp), got)
     sep = make_attn(w)
