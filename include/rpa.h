@@ -304,7 +304,8 @@ enum {
                                     exceeds the average work of a compute unit
                                     by half), -1 = never split, > 0 = split every
                                     item longer than 1.5x this many keys (rounded
-                                    up to 256); <= 2^30                         */
+                                    up to 256, at least 512 for items of full
+                                    tiles); <= 2^30                              */
   RPA_OPT_CONCURRENT = 10,       /* 1 (default): when a step has both decode
                                     and prefill items, the decode kernel runs
                                     on a second stream of

@@ -23,7 +23,8 @@
 //    workgroup each stream a different 32-key chunk straight from HBM into
 //    v_mfma_f32_16x16x32_bf16 operand registers; the waves are combined
 //    through LDS, and the splits of a long sequence are merged by log-sum-exp
-//    by the split that finishes last (or by rpa_merge_kernel).
+//    by the split that finishes last (or by rpa_merge_kernel, which always
+//    merges the splits of long prefill items).
 //
 // Both compute scores transposed (S^T = K Q^T), so a query row is an MFMA
 // column and the probabilities feed the P V product from the same lanes.

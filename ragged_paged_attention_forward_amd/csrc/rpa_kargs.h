@@ -18,7 +18,7 @@ struct KernelArgs {
   float* partial_o;      // [slot][16 rows][D]; a prefill split uses prefill_rows / 16 slots
   float* partial_lse;    // [slot][16 rows], base-2 log-sum-exp
   int32_t* merge_tickets;  // [group] splits finished so far (0 between calls)
-  int32_t fused_merge;   // 1: the last split of a group merges it (no merge kernel)
+  int32_t fused_merge;   // decode kernel: 1 the last split of a group merges it (no merge kernel)
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;         // G = Hq / Hkv

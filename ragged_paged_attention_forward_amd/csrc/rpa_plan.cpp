@@ -121,8 +121,8 @@ int validate_metadata(const PlanParams& p, const int32_t* cu, const int32_t* kv,
 // Long prefill items (the last query tiles of a long chunk) can outlast the
 // rest of the launch by far, with most compute units idle.  Such an item is
 // cut along its key range into splits that each write a partial result
-// (normalised O and log-sum-exp per row); the split that finishes last merges
-// them, as for decode.  Automatic mode splits only when the longest item
+// (normalised O and log-sum-exp per row); the merge kernel that follows the
+// prefill launch combines them (several workgroups per group).  Automatic mode splits only when the longest item
 // exceeds 1.5x the average work of a compute unit, into pieces of about that
 // average, at least 512 keys on multiples of 256 for items with full tiles
 // (smaller pieces measured slower: every split writes and re-reads its rows'
