@@ -138,6 +138,27 @@ def test_fp8_prefill_full_size_sampled(name, stage):
     compare(out, oracle_fp8(f, rows), rows=rows, label=name)
 
 
+@pytest.mark.parametrize("stage", [0, 1])
+@pytest.mark.parametrize("window", [0, 1024])
+def test_fp8_long_contexts_sampled(window, stage):
+    """Decodes over 40K-key contexts and a 2048-token chunk on a 30K prefix
+    (a prefill key range of 235 pages: the prefill kernel's page-id window
+    of 64 pages is reloaded as its tiles move on), both prefill routes;
+    sampled rows, every row of the chunk's first and last tile included."""
+    seqs = [(1, 40_000), (2048, 30_000), (1, 129), (3, 17_001)]
+    w = wl.custom(seqs, 8, 1, 256, 128, window, seed=73 + window)
+    print(f"fp8 long contexts W={window} stage={stage}", flush=True)
+    f = wl.make_fp8_inputs(w, poison=True)
+    attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_FP8_STAGE, stage)
+    out = run_fp8(f, attn)
+    t = w.total_q
+    cu = f.base.cu_q_lens.tolist()
+    must = [0, cu[1], cu[1] + 1, cu[2] - 1, cu[2], t - 1, t - 2, t - 3] + tile_edge_rows(attn, f)
+    rows = wl.sample_rows(t, 24, w.seed, must)
+    compare(out, oracle_fp8(f, rows), rows=rows, label=f"fp8 long w{window} stage {stage}")
+
+
 @pytest.mark.parametrize("stage", [0, 1, 2])
 def test_fp8_staging_kernel_runs_only_when_asked(stage):
     """The staging kernel (timed as its own kind) runs with RPA_OPT_FP8_STAGE
