@@ -329,6 +329,27 @@ def test_concurrent_decode_stream(n_prefill):
         assert torch.equal(run_gpu(two, inp), base)
 
 
+def test_many_sequences_sampled():
+    """A step of 3000 sequences (about 12000 decode items and 400 prefill
+    tiles in one call): 2990 decodes of 1-4 tokens over 1-700 keys and ten
+    prefill chunks, d 128, G 4, 64-token pages; sampled rows, and a repeated
+    call gives the same bits."""
+    rng = np.random.default_rng(75)
+    seqs = [(int(q), int(q + k)) for q, k in zip(rng.integers(1, 5, 2990), rng.integers(0, 700, 2990))]
+    seqs += [(int(q), int(q + k)) for q, k in zip(rng.integers(100, 600, 10), rng.integers(0, 2000, 10))]
+    w = wl.custom(seqs, 16, 4, 128, 64, 0, seed=75)
+    print(f"many sequences: S={w.num_seqs} T={w.total_q}", flush=True)
+    inp = wl.make_inputs(w, poison=True)
+    attn = make_attn(w)
+    info, _ = attn.plan(inp.cu_q_lens, inp.kv_lens, 0)
+    assert info["num_decode_items"] > 2990
+    got = run_gpu(attn, inp)
+    t = w.total_q
+    rows = wl.sample_rows(t, 200, w.seed, [0, 1, t - 1])
+    compare(got, oracle_rows(inp, rows), rows=rows, label="many sequences")
+    assert torch.equal(run_gpu(attn, inp), got)
+
+
 def test_long_contexts_sampled():
     """Decodes over 40K-key contexts (many splits per group) and a 2048-token
     chunk on a 30K prefix, with and without a window; sampled rows."""
