@@ -359,10 +359,16 @@ struct PrefillCfg {
 
 RPA_DEV int xor_k(int s) { return s & 1; }
 
-template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI, bool KV8 = false>
+template <int D, int BN, int NW, int NB, int NS, int DS, int SEG, bool KV8 = false>
 __global__ void __launch_bounds__(NW * 64, 1)
 rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   using C = PrefillCfg<D, BN, NW, NB, NS, DS, KV8>;
+  // SEG: keys of an aligned run that lies in one page.  BN: a whole tile
+  // (pages of a multiple of BN keys); BN / NW: the rows that one wave stages
+  // of a tile; 0: a page id per lane.
+  static_assert(SEG == 0 || SEG == BN || SEG * NW == BN, "page runs: a tile, a wave's rows of a tile, or none");
+  constexpr bool UNI = SEG == BN;
+  constexpr bool BUF = SEG > 0;   // buffer loads (no per-lane page lookups)
   constexpr int DH = C::DH;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   char* lds = reinterpret_cast<char*>(smem);
@@ -470,6 +476,43 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     vsc = uniform_load(args.v_scales, g);
   }
 
+  // ---- the page of this wave's run of a tile (SEG = BN / NW) ----
+  // Tiles are staged in order 0, 1, ..; each stage reads the page id the
+  // previous one requested (a scalar load, one stage ahead).  The id is the
+  // page of the run's first key inside the range, clipped to its last key,
+  // so that only entries of the range are read.
+  [[maybe_unused]] int run_page = 0, run_pidx = 0;
+  auto fetch_run_page = [&](int ts) {
+    int key = key_of(ts) + wave * SEG;
+    key = key > kv_begin ? key : kv_begin;
+    key = key < kv_end ? key : kv_end - 1;
+    run_pidx = (key > 0 ? key : 0) / page_size;
+    run_page = uniform_load(pt_row, run_pidx);
+  };
+  if constexpr (BUF && !UNI) {
+    if (n_tiles > 0) fetch_run_page(0);
+  }
+  // The rows [lo, hi) of this wave's run of tile ts (k0 its first key): the
+  // byte offset of the first in the pool, their byte count (0 for none) and
+  // the bytes from the tile's first row to it.
+  auto run_rows = [&](int ts, int k0, int lo, int hi, int rbytes, int esz, int64_t& base_off, uint32_t& nbytes,
+                      int& rel_b) {
+    const int64_t page = run_page;
+    const int pidx = run_pidx;
+    if (ts + 1 < n_tiles) fetch_run_page(ts + 1);
+    const int s0 = k0 + wave * SEG;
+    const int slo = s0 > lo ? s0 : lo;
+    const int shi = s0 + SEG < hi ? s0 + SEG : hi;
+    rel_b = (slo - k0) * rbytes;
+    const int64_t off = ((page * page_size + (slo - pidx * page_size)) * hkv + g) * D * esz;
+    const uint32_t n = shi > slo ? static_cast<uint32_t>((shi - slo - 1) * rbytes + D * esz) : 0u;
+    // wave-uniform values: kept in scalar registers for the descriptors
+    base_off = static_cast<int64_t>(
+        (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(off >> 32)))) << 32) |
+        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(off))));
+    nbytes = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(n)));
+  };
+
   // ---- direct HBM -> LDS staging of one K/V tile ----
   // Load i of this wave fills block wave*LOADS + i of the K and V tiles; lane
   // l writes 16 bytes at +16*l of the block: key row s = 16*l / ROW_B of the
@@ -544,10 +587,25 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
         buffer_load_lds16(krs, kdst + i * C::BLK_K, srow[i] * row_bytes + sgk[i] - rel_b);
         buffer_load_lds16(vrs, vdst + i * C::BLK_V, srow[i] * row_bytes + sgv[i] - rel_b);
       }
+    } else if constexpr (BUF) {
+      // This wave's rows lie in one page: the same loads against a buffer
+      // over the run's rows inside [lo, hi).
+      int64_t base_off;
+      uint32_t nbytes;
+      int rel_b;
+      run_rows(ts, k0, lo, hi, row_bytes, 2, base_off, nbytes, rel_b);
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const char*>(kbase) + base_off, nbytes);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const char*>(vbase) + base_off, nbytes);
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        buffer_load_lds16(krs, kdst + i * C::BLK_K, srow[i] * row_bytes + sgk[i] - rel_b);
+        buffer_load_lds16(vrs, vdst + i * C::BLK_V, srow[i] * row_bytes + sgv[i] - rel_b);
+      }
     } else {
-      // Small pages: each lane looks up its row's page.  Rows outside [lo, hi)
-      // are redirected to the nearest key of the range, so every value read
-      // is a finite key of the range and no page before kv_begin's is looked up.
+      // A wave's rows span pages: each lane looks up its row's page.  Rows
+      // outside [lo, hi) are redirected to the nearest key of the range, so
+      // every value read is a finite key of the range and no page before
+      // kv_begin's is looked up.
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
         int key = k0 + srow[i];
@@ -576,6 +634,20 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       const int rel_b = (lo - k0) * row_bytes8;
       const int64_t base_off = ((next_tile_row() + (lo - k0)) * hkv + g) * D;
       const uint32_t nbytes = static_cast<uint32_t>((hi - lo - 1) * row_bytes8 + D);
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(k8 + base_off, nbytes);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v8 + base_off, nbytes);
+#pragma unroll
+      for (int i = 0; i < C::LOADS8; ++i) {
+        const int at = (wave * C::LOADS8 + i) * 1024 + lane * 16;   // byte of the tile
+        const int off = (at / D) * row_bytes8 + at % D - rel_b;
+        buffer_load_lds16(krs, kdst + i * 1024, off);
+        buffer_load_lds16(vrs, vdst + i * 1024, off);
+      }
+    } else if constexpr (BUF) {
+      int64_t base_off;
+      uint32_t nbytes;
+      int rel_b;
+      run_rows(ts, k0, lo, hi, row_bytes8, 1, base_off, nbytes, rel_b);
       const __amdgpu_buffer_rsrc_t krs = make_rsrc(k8 + base_off, nbytes);
       const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v8 + base_off, nbytes);
 #pragma unroll
@@ -823,7 +895,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t)
       if (t < n_tiles) stage(t, t);
-    if constexpr (UNI) {
+    if constexpr (BUF) {
       // Q and the first tiles: every load of the prologue is complete before the loop
       wait_vmem();
     } else {
@@ -854,7 +926,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     // converts tile t+1 after them, behind a second barrier.
     for (int t = 0; t < NS; ++t)
       if (t < n_tiles) stage8(t, t);
-    if constexpr (UNI) {
+    if constexpr (BUF) {
       // Q and the first tiles: every load of the prologue is complete before the loop
       wait_vmem();
     } else {
@@ -1117,7 +1189,7 @@ struct DecodeCfg {
 // AP: an appending call (the fused KV write of the items holding all of
 // their sequence's new tokens); a separate instantiation, so that plain calls
 // carry none of its code.
-template <int D, int NW, bool UNI, bool KV8, int RB = 1, bool AP = false>
+template <int D, int NW, int SEG, bool KV8, int RB = 1, bool AP = false>
 __global__ void __launch_bounds__(NW * 64, (D >= 512 || (RB == 2 && D >= 256)) ? 1 : 2)
 rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   using C = DecodeCfg<D, NW, RB>;
@@ -1190,14 +1262,28 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     l_run[rb] = 0.f;
   }
 
-  // 32-key chunks aligned to 32 keys; with UNI a chunk never crosses a page.
+  // 32-key chunks aligned to 32 keys.  SEG > 0: each aligned run of SEG keys
+  // of a chunk (the whole chunk, or each 16-key half) lies in one page, whose
+  // id the wave reads one chunk ahead (the page of the run's first key inside
+  // the item's range, clipped to its last key, so that only entries of the
+  // range are read).  SEG = 0 (page sizes that are not a multiple of 16
+  // keys): a page id per lane.
+  constexpr int NSEG = SEG > 0 ? 32 / SEG : 1;
   const int chunk0 = (kv_begin / 32) * 32;
   const int n_chunks = (kv_end - chunk0 + 31) / 32;
   const int row_bytes = static_cast<int>(row_stride) * ESZ;   // bytes between key rows of a page
-  int next_page = 0;
+  int next_page[NSEG];
+  auto fetch_pages = [&](int k0) {
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg) {
+      int key = k0 + sg * SEG > kv_begin ? k0 + sg * SEG : kv_begin;
+      key = key < kv_end ? key : kv_end - 1;
+      next_page[sg] = uniform_load(pt_row, (key > 0 ? key : 0) / page_size);
+    }
+  };
   auto first_page = [&]() {
-    if constexpr (UNI) {
-      if (wave < n_chunks) next_page = uniform_load(pt_row, (chunk0 + wave * 32) / page_size);
+    if constexpr (SEG > 0) {
+      if (wave < n_chunks) fetch_pages(chunk0 + wave * 32);
     }
   };
 
@@ -1285,36 +1371,47 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     u32x4 vf[C::NU][8];
     [[maybe_unused]] u32x2 kr[2][D / 32];   // KV8: the raw bytes of kf / vf
     [[maybe_unused]] u32x2 vr[C::NU][8];
-    if constexpr (UNI) {
-      // One page holds the whole chunk: buffer loads against the chunk's valid
-      // key rows [lo, hi); rows outside read as zero (negative offsets wrap
-      // above the record count), so there are no branches and no NaN reads.
-      const int page = next_page;
-      if (ch + NW < n_chunks) next_page = uniform_load(pt_row, (k0 + NW * 32) / page_size);
-      const int lo = k0 > kv_begin ? k0 : kv_begin;
-      const int hi = k0 + 32 < kv_end ? k0 + 32 : kv_end;
-      const int64_t lo_off = ((static_cast<int64_t>(page) * page_size + (lo - (lo / page_size) * page_size)) * hkv + g) * D;
-      const uint32_t nbytes = static_cast<uint32_t>((hi - lo - 1) * row_bytes + D * ESZ);
-      const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + lo_off, nbytes);
-      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + lo_off, nbytes);
-      const int rel = k0 - lo;   // <= 0
+    if constexpr (SEG > 0) {
+      // Buffer loads against each run's valid key rows [lo, hi); rows outside
+      // read as zero (negative offsets wrap above the record count, an empty
+      // run has no records), so there are no branches and no NaN reads.
+      int page[NSEG];
+#pragma unroll
+      for (int sg = 0; sg < NSEG; ++sg) page[sg] = next_page[sg];
+      if (ch + NW < n_chunks) fetch_pages(k0 + NW * 32);
+      __amdgpu_buffer_rsrc_t krs[NSEG], vrs[NSEG];
+      int rel[NSEG];   // run start - lo (<= 0)
+#pragma unroll
+      for (int sg = 0; sg < NSEG; ++sg) {
+        const int s0 = k0 + sg * SEG;
+        const int lo = s0 > kv_begin ? s0 : kv_begin;
+        const int hi = s0 + SEG < kv_end ? s0 + SEG : kv_end;
+        const int64_t lo_off =
+            ((static_cast<int64_t>(page[sg]) * page_size + (lo - (lo / page_size) * page_size)) * hkv + g) * D;
+        const uint32_t nbytes = hi > lo ? static_cast<uint32_t>((hi - lo - 1) * row_bytes + D * ESZ) : 0u;
+        krs[sg] = make_rsrc(kbase + lo_off, nbytes);
+        vrs[sg] = make_rsrc(vbase + lo_off, nbytes);
+        rel[sg] = s0 - lo;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int off = (rel + kb * 16 + ln) * row_bytes + lq * 8 * ESZ;
+        const int sg = (kb * 16) / (SEG > 0 ? SEG : 32);
+        const int off = (rel[sg] + kb * 16 - sg * SEG + ln) * row_bytes + lq * 8 * ESZ;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-          if constexpr (KV8) kr[kb][kk] = buffer_load8(krs, off + kk * 32);
-          else kf[kb][kk] = buffer_load16(krs, off + kk * 64);
+          if constexpr (KV8) kr[kb][kk] = buffer_load8(krs[sg], off + kk * 32);
+          else kf[kb][kk] = buffer_load16(krs[sg], off + kk * 64);
         }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int key_rel = rel + ((j < 4) ? (lq * 4 + j) : (16 + lq * 4 + j - 4));
+        const int sg = (j < 4 ? 0 : 16) / (SEG > 0 ? SEG : 32);
+        const int key_rel = rel[sg] - sg * SEG + ((j < 4) ? (lq * 4 + j) : (16 + lq * 4 + j - 4));
 #pragma unroll
         for (int u = 0; u < C::NU; ++u) {
           const int c = u * 16 + ln;
-          if constexpr (KV8) vr[u][j] = c < C::NCH ? buffer_load8(vrs, key_rel * row_bytes + c * 8) : u32x2{0, 0};
-          else vf[u][j] = c < C::NCH ? buffer_load16(vrs, key_rel * row_bytes + c * 16) : u32x4{0, 0, 0, 0};
+          if constexpr (KV8) vr[u][j] = c < C::NCH ? buffer_load8(vrs[sg], key_rel * row_bytes + c * 8) : u32x2{0, 0};
+          else vf[u][j] = c < C::NCH ? buffer_load16(vrs[sg], key_rel * row_bytes + c * 16) : u32x4{0, 0, 0, 0};
         }
       }
     } else {
@@ -1667,57 +1764,70 @@ rpa_stage_kernel(const int32_t* __restrict__ stage, const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int D, int BN, int NW, int NB, int NS, int DS, bool UNI, bool KV8>
+template <int D, int BN, int NW, int NB, int NS, int DS, int SEG, bool KV8>
 static hipError_t launch_prefill_u(const KernelArgs& a, int n_items, hipStream_t stream) {
   using C = PrefillCfg<D, BN, NW, NB, NS, DS, KV8>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, NS, DS, UNI, KV8>),
+        reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, NS, DS, SEG, KV8>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, NS, DS, UNI, KV8>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
+  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, NS, DS, SEG, KV8>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
                      stream, a.items, a.page_table, a.q, a.k, a.v, a);
   return hipGetLastError();
 }
 
 template <int D, int BN, int NW, int NB, int NS, int DS>
 static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, bool kv8, hipStream_t stream) {
-  // one buffer descriptor per tile needs the tile inside one page and 32-bit offsets
+  // Buffer descriptors need a run of keys inside one page (the tile, else each
+  // wave's rows of it) and 32-bit offsets; otherwise each lane looks up its
+  // row's page.
+  constexpr int WR = BN / NW;
   const int esz = kv8 ? 1 : 2;
-  const bool uni = a.page_size % BN == 0 && int64_t(a.page_size) * a.num_kv_heads * D * esz < (int64_t(1) << 31);
+  const bool fits = int64_t(a.page_size) * a.num_kv_heads * D * esz < (int64_t(1) << 31);
+  const int seg = !fits ? 0 : a.page_size % BN == 0 ? BN : a.page_size % WR == 0 ? WR : 0;
   if (kv8) {
-    if (uni) return launch_prefill_u<D, BN, NW, NB, NS, DS, true, true>(a, n_items, stream);
-    return launch_prefill_u<D, BN, NW, NB, NS, DS, false, true>(a, n_items, stream);
+    if (seg == BN) return launch_prefill_u<D, BN, NW, NB, NS, DS, BN, true>(a, n_items, stream);
+    if (seg == WR) return launch_prefill_u<D, BN, NW, NB, NS, DS, WR, true>(a, n_items, stream);
+    return launch_prefill_u<D, BN, NW, NB, NS, DS, 0, true>(a, n_items, stream);
   }
-  if (uni) return launch_prefill_u<D, BN, NW, NB, NS, DS, true, false>(a, n_items, stream);
-  return launch_prefill_u<D, BN, NW, NB, NS, DS, false, false>(a, n_items, stream);
+  if (seg == BN) return launch_prefill_u<D, BN, NW, NB, NS, DS, BN, false>(a, n_items, stream);
+  if (seg == WR) return launch_prefill_u<D, BN, NW, NB, NS, DS, WR, false>(a, n_items, stream);
+  return launch_prefill_u<D, BN, NW, NB, NS, DS, 0, false>(a, n_items, stream);
 }
 
-template <int D, int NW, bool UNI, bool KV8, int RB, bool AP>
+template <int D, int NW, int SEG, bool KV8, int RB, bool AP>
 static hipError_t launch_decode_v(const KernelArgs& a, int n_items, hipStream_t stream) {
   using C = DecodeCfg<D, NW, RB>;
   if constexpr (C::LDS_BYTES > 64 * 1024) {   // beyond the default dynamic LDS limit
     static bool attr_set = false;
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_decode_kernel<D, NW, UNI, KV8, RB, AP>),
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rpa_decode_kernel<D, NW, SEG, KV8, RB, AP>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
   }
-  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, UNI, KV8, RB, AP>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream,
+  hipLaunchKernelGGL((rpa_decode_kernel<D, NW, SEG, KV8, RB, AP>), dim3(n_items), dim3(C::NT), C::LDS_BYTES, stream,
                      a.items, a.page_table, a.q, a.k, a.v, a);
   return hipGetLastError();
 }
 
 // Appending calls (new rows given) run the AP form, with four waves.
-template <int D, int NW, bool UNI, bool KV8 = false, int RB = 1>
+template <int D, int NW, bool KV8 = false, int RB = 1>
 static hipError_t launch_decode_u(const KernelArgs& a, int n_items, hipStream_t stream) {
-  if (a.k_new != nullptr) return launch_decode_v<D, 4, UNI, KV8, RB, true>(a, n_items, stream);
-  return launch_decode_v<D, NW, UNI, KV8, RB, false>(a, n_items, stream);
+  const bool ap = a.k_new != nullptr;
+  if (a.page_size % 32 == 0)
+    return ap ? launch_decode_v<D, 4, 32, KV8, RB, true>(a, n_items, stream)
+              : launch_decode_v<D, NW, 32, KV8, RB, false>(a, n_items, stream);
+  if (a.page_size % 16 == 0)
+    return ap ? launch_decode_v<D, 4, 16, KV8, RB, true>(a, n_items, stream)
+              : launch_decode_v<D, NW, 16, KV8, RB, false>(a, n_items, stream);
+  return ap ? launch_decode_v<D, 4, 0, KV8, RB, true>(a, n_items, stream)
+            : launch_decode_v<D, NW, 0, KV8, RB, false>(a, n_items, stream);
 }
 
 // Eight-wave workgroups are not used for D = 512: two waves per SIMD cannot
@@ -1726,26 +1836,19 @@ static hipError_t launch_decode_u(const KernelArgs& a, int n_items, hipStream_t 
 template <int D>
 static hipError_t launch_decode_t(const KernelArgs& a, int n_items, int waves, bool kv8, int rows,
                                   hipStream_t stream) {
-  const bool uni = a.page_size % 32 == 0;
   if constexpr (D < 512) {
     if (rows > 16) {
-      if (kv8)
-        return uni ? launch_decode_u<D, 4, true, true, 2>(a, n_items, stream)
-                   : launch_decode_u<D, 4, false, true, 2>(a, n_items, stream);
-      return uni ? launch_decode_u<D, 4, true, false, 2>(a, n_items, stream)
-                 : launch_decode_u<D, 4, false, false, 2>(a, n_items, stream);
+      if (kv8) return launch_decode_u<D, 4, true, 2>(a, n_items, stream);
+      return launch_decode_u<D, 4, false, 2>(a, n_items, stream);
     }
   } else {
     if (rows > 16) return hipErrorInvalidValue;
   }
-  if (kv8)
-    return uni ? launch_decode_u<D, 4, true, true>(a, n_items, stream)
-               : launch_decode_u<D, 4, false, true>(a, n_items, stream);
+  if (kv8) return launch_decode_u<D, 4, true>(a, n_items, stream);
   if constexpr (D < 512) {
-    if (waves == 8) return uni ? launch_decode_u<D, 8, true>(a, n_items, stream)
-                               : launch_decode_u<D, 8, false>(a, n_items, stream);
+    if (waves == 8) return launch_decode_u<D, 8>(a, n_items, stream);
   }
-  return uni ? launch_decode_u<D, 4, true>(a, n_items, stream) : launch_decode_u<D, 4, false>(a, n_items, stream);
+  return launch_decode_u<D, 4>(a, n_items, stream);
 }
 
 template <int D>

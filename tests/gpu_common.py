@@ -49,3 +49,24 @@ def compare(got: torch.Tensor, ref: np.ndarray, rows=None, label=""):
 
 def oracle_rows(inp: wl.Inputs, rows=None) -> np.ndarray:
     return ora.forward_inputs(inp, rows)
+
+
+def bitwise_mismatch(got: torch.Tensor, want: torch.Tensor, inp: wl.Inputs, label="") -> str:
+    """'' when got equals want bit for bit; otherwise a report of the token
+    rows that differ (their sequences, how many hold NaN) and of both
+    tensors' error against the oracle on a few of them, so that a failure
+    names the wrong side."""
+    if torch.equal(got, want):
+        return ""
+    differ = (got.view(torch.int16) != want.view(torch.int16)).flatten(1).any(1).nonzero().flatten().cpu().numpy()
+    cu = inp.cu_q_lens.numpy()
+    seqs = sorted({int(np.searchsorted(cu, t, side="right") - 1) for t in differ})
+    nan_rows = int(torch.isnan(got[torch.from_numpy(differ).to(got.device)]).flatten(1).any(1).sum())
+    rows = differ[:: max(1, len(differ) // 6)][:6]
+    ref = oracle_rows(inp, rows)
+    errs = []
+    for name, t in (("got", got), ("want", want)):
+        g = t.detach().to("cpu", torch.float64).numpy()[rows]
+        errs.append(f"{name} max-abs vs oracle {float(np.nanmax(np.abs(g - ref))):.3e}")
+    return (f"{label}: {len(differ)} token rows differ (sequences {seqs[:12]}, q_lens "
+            f"{[int(cu[s + 1] - cu[s]) for s in seqs[:12]]}), {nan_rows} of them with NaN; " + ", ".join(errs))

@@ -19,7 +19,7 @@ import torch
 
 import oracle.rpa_oracle as ora
 import rpa_workloads as wl
-from gpu_common import compare, gpu_available, make_attn, oracle_rows
+from gpu_common import bitwise_mismatch, compare, gpu_available, make_attn, oracle_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -143,7 +143,8 @@ def test_replay_after_calls_with_larger_metadata_is_bitwise():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(out, eager), f"replay {rep} after a larger eager call"
+        bad = bitwise_mismatch(out, eager, host, f"replay {rep} after a larger eager call")
+        assert not bad, bad
     # twelve more keys: more than the cache keeps, so every uncaptured plan is evicted
     for i in range(12):
         kv_i = bh.kv_lens.clone()
@@ -153,14 +154,16 @@ def test_replay_after_calls_with_larger_metadata_is_bitwise():
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
-    assert torch.equal(out, eager), "replay after evictions"
+    bad = bitwise_mismatch(out, eager, host, "replay after evictions")
+    assert not bad, bad
     rows = wl.sample_rows(big.total_q, 40, 402, [0, big.total_q - 1])
     compare(big_out, oracle_rows(bh, rows), rows=rows, label="larger eager call")
     # the pinned plan is released; the context keeps working eagerly
     attn.release_captured()
     again = attn.forward(d.q, d.k_pages, d.v_pages, d.page_table, cu, kv, w.window, w.scale)
     torch.cuda.synchronize()
-    assert torch.equal(again, eager)
+    bad = bitwise_mismatch(again, eager, host, "eager call after the release")
+    assert not bad, bad
 
 
 def test_layer_stack_five_window_one_global_replays_bitwise():
@@ -172,6 +175,11 @@ def test_layer_stack_five_window_one_global_replays_bitwise():
     dev = [h.to("cuda") for h in host]
     cu, kv = host[0].cu_q_lens, host[0].kv_lens
     attn = make_attn(w)
+
+    def layer_inputs(i):
+        return wl.Inputs(w, host[i].q, host[i].k_pages, host[i].v_pages, host[i].page_table, cu, kv,
+                         host[i].trap_page, pattern[i], w.scale, True)
+
     eager = [attn.forward(dd.q, dd.k_pages, dd.v_pages, dd.page_table, cu, kv, win, w.scale).clone()
              for dd, win in zip(dev, pattern)]
     torch.cuda.synchronize()
@@ -187,11 +195,10 @@ def test_layer_stack_five_window_one_global_replays_bitwise():
         g.replay()
         torch.cuda.synchronize()
         for i, (o, e) in enumerate(zip(outs, eager)):
-            assert torch.equal(o, e), f"replay {rep} layer {i} (W {pattern[i]})"
+            bad = bitwise_mismatch(o, e, layer_inputs(i), f"replay {rep} layer {i} (W {pattern[i]})")
+            assert not bad, bad
     for i in (0, 5):
-        ref = ora.forward_inputs(wl.Inputs(w, host[i].q, host[i].k_pages, host[i].v_pages, host[i].page_table,
-                                           cu, kv, host[i].trap_page, pattern[i], w.scale, True))
-        compare(eager[i], ref, label=f"layer {i} (W {pattern[i]})")
+        compare(eager[i], ora.forward_inputs(layer_inputs(i)), label=f"layer {i} (W {pattern[i]})")
 
 
 def test_calls_on_two_streams_run_in_call_order():

@@ -40,6 +40,15 @@ CASES = {
     "with_empty_sequences": lambda: wl.custom([(0, 50), (3, 70), (0, 1), (1, 300), (0, 0), (17, 17)], 8, 2, 256, 64,
                                               0, seed=43),
     "mha_d64_window": lambda: wl.custom([(9, 200), (1, 65), (64, 64)], 4, 4, 64, 16, 33, seed=44),
+    # page sizes that are not a multiple of 16 keys (a page id per lane in the
+    # decode kernel), of 4 (a prefill wave's rows at d 256 in one page), and
+    # of 16 but not 32 (16-key decode runs, a prefill wave's rows at d 128)
+    "decode_pages8": lambda: wl.custom([(1, 64 + 37 * i) for i in range(40)], 8, 1, 256, 8, 0, seed=46),
+    "mixed_small_w1024_pages24": lambda: mixed_small(1024, page_size=24),
+    "gqa4_d128_chunks_pages48": lambda: wl.custom([(40, 100), (1, 17), (129, 129), (3, 1000)], 16, 4, 128, 48, 0,
+                                                  seed=49),
+    "gqa4_d128_chunks_pages24": lambda: wl.custom([(40, 100), (1, 17), (129, 129), (3, 1000)], 16, 4, 128, 24, 0,
+                                                  seed=50),
     "g16_d128": lambda: wl.custom([(5, 90), (1, 400)], 16, 1, 128, 64, 0, seed=45),
     "g32_d128_prefill_only": lambda: wl.custom([(5, 90), (33, 400), (1, 70)], 32, 1, 128, 64, 0, seed=47),
 }

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import rpa_workloads as wl
-from gpu_common import compare, gpu_available, make_attn, oracle_rows, run_gpu
+from gpu_common import bitwise_mismatch, compare, gpu_available, make_attn, oracle_rows, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -155,12 +155,18 @@ def test_deterministic_bitwise():
     a = run_gpu(attn, inp).clone()
     b = run_gpu(attn, inp).clone()
     c = run_gpu(make_attn(w), inp)
-    assert torch.equal(a, b) and torch.equal(a, c)
+    for label, other in (("repeated call", b), ("new context", c)):
+        bad = bitwise_mismatch(other, a, inp, label)
+        assert not bad, bad
 
 
 @pytest.mark.parametrize("hq,hkv,d,b", [
     (4, 1, 64, 16), (16, 1, 128, 32), (8, 2, 256, 64), (16, 16, 64, 8), (32, 1, 128, 16),
     (16, 2, 512, 128), (8, 8, 512, 256), (2, 1, 256, 1), (12, 4, 128, 128),
+    # every page mode at every head size: a tile in one page, a prefill
+    # wave's rows in one page, a page per lane; 32- and 16-key decode runs
+    (8, 1, 256, 8), (16, 4, 128, 48), (16, 2, 512, 12), (8, 2, 128, 24), (4, 2, 256, 6), (8, 2, 64, 40),
+    (16, 2, 512, 6), (8, 2, 64, 128),
 ])
 def test_shapes(hq, hkv, d, b):
     seqs = [(0, 5), (1, 1), (9, 9), (1, 300), (40, 170), (3, 77), (130, 130), (2, 513), (0, 0)]
