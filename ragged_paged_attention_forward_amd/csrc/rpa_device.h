@@ -1105,8 +1105,15 @@ RPA_DEV void merge_group(const KernelArgs& args, int q_start, int q_count, int k
   constexpr int C4 = D / 4;
   constexpr int NB = 8;   // splits fetched per batch: every load of a batch is in flight at once
   const int rows = q_count * args.group;
-  const float* lse = args.partial_lse + static_cast<int64_t>(partial_base) * 16;
-  const float* po = args.partial_o + static_cast<int64_t>(partial_base) * 16 * D;
+  // Device-scope loads (they miss the compute unit's vector cache and read
+  // what other compute units wrote): the fused merge runs in the launch
+  // that writes the partials, after the last split's ticket, and a cached
+  // line of the workspace may predate its other splits' stores.
+  constexpr int kDeviceScope = 16;   // the cache-policy bit of a device-scope load
+  const __amdgpu_buffer_rsrc_t lrs =
+      make_rsrc(args.partial_lse + static_cast<int64_t>(partial_base) * 16, static_cast<uint32_t>(n * rps * 4));
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(args.partial_o + static_cast<int64_t>(partial_base) * 16 * D,
+                                               static_cast<uint32_t>(n * rps * D * 4));
   for (int idx = tid; idx < rows * C4; idx += nthreads) {
     const int r = idx / C4;
     const int c = idx - r * C4;
@@ -1118,8 +1125,11 @@ RPA_DEV void merge_group(const KernelArgs& args, int q_start, int q_count, int k
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const bool ok = i0 + b < n;
-        l[b] = ok ? lse[(i0 + b) * rps + r] : kNegInf;
-        v[b] = ok ? *reinterpret_cast<const f32x4*>(po + (static_cast<int64_t>(i0 + b) * rps + r) * D + c * 4)
+        const int slot_row = (i0 + b) * rps + r;
+        l[b] = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, slot_row * 4, 0, kDeviceScope))
+                  : kNegInf;
+        v[b] = ok ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, (slot_row * D + c * 4) * 4, 0,
+                                                                                     kDeviceScope))
                   : f32x4{0.f, 0.f, 0.f, 0.f};
       }
       float bm = mx;
@@ -1644,7 +1654,11 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   // wave's vmcnt reaches zero.  The split that draws the last ticket then
   // reads all partials back (its own included) and merges them in split order
   // with the same arithmetic as the merge kernel, and resets the ticket for
-  // the next call.
+  // the next call.  Those reads are device-scope loads (merge_group), which
+  // miss this compute unit's vector cache: it may hold a line of the
+  // workspace read earlier in the launch by another group's merge on this
+  // unit (16 LSEs of a slot are 64 bytes, so two groups' slots share a
+  // 128-byte line), from before this group's splits wrote it.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0)
@@ -1652,7 +1666,6 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
                                        __HIP_MEMORY_SCOPE_AGENT) == it.num_splits - 1;
   __syncthreads();
   if (*lds_flag == 0) return;
-  asm volatile("" ::: "memory");
   merge_group<D>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, ROWS, tid, C::NT);
   if (tid == 0) __hip_atomic_store(args.merge_tickets + it.split_group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

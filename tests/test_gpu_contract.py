@@ -228,3 +228,40 @@ def test_calls_on_two_streams_run_in_call_order():
     rows_b = wl.sample_rows(b.total_q, 32, 6, [0, b.total_q - 1])
     compare(out_a, oracle_rows(ha, rows_a), rows=rows_a, label="stream 1")
     compare(out_b, oracle_rows(hb, rows_b), rows=rows_b, label="stream 2")
+
+
+def test_fused_merge_reads_the_splits_writes_not_stale_lines():
+    """The split workspace is pooled: a new context's plan takes a block that
+    still holds another call's partials.  The last split of a group reads
+    its group's partials in the launch that wrote them; a cached line of the
+    workspace read earlier in the launch (another group's merge on the same
+    compute unit: two slots' LSEs share a 128-byte line) must not stand in
+    for them.  Two mixed steps of one shape and different values (their
+    decode kernels run beside the prefill kernel, so merges of different
+    groups interleave) alternate on fresh contexts, so the one block they
+    take holds the other step's partials each time; every result must equal
+    the first bit for bit.  (The stale read itself is rare and timing
+    dependent: the merges' plain loads gave one wrong decode row in about a
+    quarter of the runs of test_replay_after_calls_with_larger_metadata_is_bitwise
+    after the append tests, and none in this test's runs.)"""
+    wa = wb = small_mixed(1024, seed=401, extra_decodes=150)
+    ha, hb = wl.make_inputs(wa, poison=True), wl.make_inputs(wa, seed=1401, poison=True)
+    da, db = ha.to("cuda"), hb.to("cuda")
+
+    def fresh_call(w, h, d):
+        attn = make_attn(w, max_num_seqs=400, max_q_tokens=4096)
+        out = attn.forward(d.q, d.k_pages, d.v_pages, d.page_table, h.cu_q_lens, h.kv_lens, w.window, w.scale)
+        torch.cuda.synchronize()
+        info, _ = attn.plan(h.cu_q_lens, h.kv_lens, w.window)
+        attn.close()
+        return out, info
+
+    first, info = fresh_call(wa, ha, da)
+    assert info["num_split_groups"] >= 100
+    rows = wl.sample_rows(wa.total_q, 48, 501, [0, wa.total_q - 1] + list(range(454, wa.total_q)))
+    compare(first, oracle_rows(ha, rows), rows=rows, label="first call")
+    for i in range(16):
+        fresh_call(wb, hb, db)
+        again, _ = fresh_call(wa, ha, da)
+        bad = bitwise_mismatch(again, first, ha, f"call {i + 2} after the other step")
+        assert not bad, bad
