@@ -44,10 +44,37 @@ def library_path() -> str:
 
 
 def _host_i32(x) -> np.ndarray:
+    if type(x) is np.ndarray and x.dtype == np.int32 and x.flags.c_contiguous:
+        return x
     if isinstance(x, torch.Tensor):
         x = x.detach().to("cpu")
         x = x.numpy()
     return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _host_addr(a: np.ndarray) -> int:
+    """Address of a contiguous host array's first element (a.ctypes.data,
+    which costs about a microsecond, only for arrays that cannot be viewed
+    through ctypes directly: empty or read-only ones)."""
+    try:
+        return ctypes.addressof(ctypes.c_char.from_buffer(a))
+    except (TypeError, ValueError, BufferError):
+        return a.ctypes.data
+
+
+# torch's current raw stream and device, without building Stream / device
+# objects (each of those costs microseconds per call); the public calls where
+# this build of torch lacks them
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_current_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
+def _stream_handle(stream, device_index: int) -> int:
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(device_index)
+    return torch.cuda.current_stream(device_index).cuda_stream
 
 
 def _i32p(a: np.ndarray):
@@ -68,8 +95,6 @@ class RaggedPagedAttention:
             raise RpaError(st, f"rpa_create failed: {self._lib.rpa_status_string(st).decode()}")
         self._ctx = ctx
         self._timing_cap = 0
-        self._stream_obj = None
-        self._stream_ptr = None
         self.num_q_heads = num_q_heads
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
@@ -178,17 +203,14 @@ class RaggedPagedAttention:
             out = torch.empty_like(q)
         elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
             raise ValueError("out must be a contiguous bf16 tensor shaped like q")
-        if stream is None:
-            stream = torch.cuda.current_stream(q.device)
-        if stream is not self._stream_obj:
-            self._stream_obj, self._stream_ptr = stream, ctypes.c_void_p(stream.cuda_stream)
-        return cu, kv, n, out
+        return cu, kv, n, out, _host_addr(cu), _host_addr(kv), _stream_handle(stream, q.get_device())
 
-    def _call(self, fn, name, device, args):
-        if device.index == torch.cuda.current_device():
+    def _call(self, fn, name, device_index: int, args):
+        cur = _current_device() if _current_device is not None else torch.cuda.current_device()
+        if device_index == cur:
             st = fn(*args)
         else:
-            with torch.cuda.device(device):
+            with torch.cuda.device(device_index):
                 st = fn(*args)
         if st != RPA_OK:
             raise self._error(st, name)
@@ -200,11 +222,11 @@ class RaggedPagedAttention:
         """Enqueue one attention call on ``stream`` (default: torch's current stream)."""
         if scale is None:
             scale = float(self.head_dim) ** -0.5
-        cu, kv, n, out = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream)
-        self._call(self._lib.rpa_forward, "rpa_forward", q.device,
+        cu, kv, n, out, cu_p, kv_p, sp = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out,
+                                                        stream)
+        self._call(self._lib.rpa_forward, "rpa_forward", q.get_device(),
                    (self._ctx, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), page_table.data_ptr(),
-                    cu.ctypes.data, kv.ctypes.data, n, int(window), float(scale), out.data_ptr(),
-                    self._stream_ptr))
+                    cu_p, kv_p, n, int(window), float(scale), out.data_ptr(), sp))
         return out
 
     def forward_noalloc(self, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
@@ -217,11 +239,11 @@ class RaggedPagedAttention:
         callers that cannot allocate."""
         if scale is None:
             scale = float(self.head_dim) ** -0.5
-        cu, kv, n, out = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream)
-        self._call(self._lib.rpa_forward_noalloc, "rpa_forward_noalloc", q.device,
+        cu, kv, n, out, cu_p, kv_p, sp = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out,
+                                                        stream)
+        self._call(self._lib.rpa_forward_noalloc, "rpa_forward_noalloc", q.get_device(),
                    (self._ctx, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), page_table.data_ptr(),
-                    cu.ctypes.data, kv.ctypes.data, n, int(window), float(scale), out.data_ptr(),
-                    self._stream_ptr))
+                    cu_p, kv_p, n, int(window), float(scale), out.data_ptr(), sp))
         return out
 
     def forward_append(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -233,15 +255,16 @@ class RaggedPagedAttention:
         into their page slots, then the attention of ``forward``, in one call."""
         if scale is None:
             scale = float(self.head_dim) ** -0.5
-        cu, kv, n, out = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream)
+        cu, kv, n, out, cu_p, kv_p, sp = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out,
+                                                        stream)
         shape = (q.shape[0], self.num_kv_heads, self.head_dim)
         for name, t in (("k_new", k_new), ("v_new", v_new)):
             if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
                 raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor of shape {list(shape)}")
-        self._call(self._lib.rpa_forward_append, "rpa_forward_append", q.device,
+        self._call(self._lib.rpa_forward_append, "rpa_forward_append", q.get_device(),
                    (self._ctx, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pages.data_ptr(),
-                    v_pages.data_ptr(), page_table.data_ptr(), cu.ctypes.data, kv.ctypes.data, n, int(window),
-                    float(scale), out.data_ptr(), self._stream_ptr))
+                    v_pages.data_ptr(), page_table.data_ptr(), cu_p, kv_p, n, int(window),
+                    float(scale), out.data_ptr(), sp))
         return out
 
     def forward_fp8(self, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
@@ -255,16 +278,16 @@ class RaggedPagedAttention:
         stand for their E4M3 value times their head's scale."""
         if scale is None:
             scale = float(self.head_dim) ** -0.5
-        cu, kv, n, out = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream,
-                                       kv_dtype=torch.uint8)
+        cu, kv, n, out, cu_p, kv_p, sp = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out,
+                                                        stream, kv_dtype=torch.uint8)
         for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
             if (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()
                     or tuple(t.shape) != (self.num_kv_heads,)):
                 raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape [{self.num_kv_heads}]")
-        self._call(self._lib.rpa_forward_fp8, "rpa_forward_fp8", q.device,
+        self._call(self._lib.rpa_forward_fp8, "rpa_forward_fp8", q.get_device(),
                    (self._ctx, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), k_scales.data_ptr(),
-                    v_scales.data_ptr(), page_table.data_ptr(), cu.ctypes.data, kv.ctypes.data, n, int(window),
-                    float(scale), out.data_ptr(), self._stream_ptr))
+                    v_scales.data_ptr(), page_table.data_ptr(), cu_p, kv_p, n, int(window),
+                    float(scale), out.data_ptr(), sp))
         return out
 
     def forward_fp8_append(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -276,8 +299,8 @@ class RaggedPagedAttention:
         slots of the fp8 pools, then the attention of ``forward_fp8``."""
         if scale is None:
             scale = float(self.head_dim) ** -0.5
-        cu, kv, n, out = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out, stream,
-                                       kv_dtype=torch.uint8)
+        cu, kv, n, out, cu_p, kv_p, sp = self._checked(q, k_pages, v_pages, page_table, cu_q_lens, kv_lens, out,
+                                                        stream, kv_dtype=torch.uint8)
         shape = (q.shape[0], self.num_kv_heads, self.head_dim)
         for name, t in (("k_new", k_new), ("v_new", v_new)):
             if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
@@ -286,10 +309,10 @@ class RaggedPagedAttention:
             if (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()
                     or tuple(t.shape) != (self.num_kv_heads,)):
                 raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape [{self.num_kv_heads}]")
-        self._call(self._lib.rpa_forward_fp8_append, "rpa_forward_fp8_append", q.device,
+        self._call(self._lib.rpa_forward_fp8_append, "rpa_forward_fp8_append", q.get_device(),
                    (self._ctx, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pages.data_ptr(),
                     v_pages.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(), page_table.data_ptr(),
-                    cu.ctypes.data, kv.ctypes.data, n, int(window), float(scale), out.data_ptr(), self._stream_ptr))
+                    cu_p, kv_p, n, int(window), float(scale), out.data_ptr(), sp))
         return out
 
     __call__ = forward
