@@ -285,6 +285,9 @@ def test_fused_merge_matches_merge_kernel_bitwise(window):
     (8, 1, 256, 128, [(700, 2100)], 1400),
     (16, 2, 512, 128, [(300, 1800), (2, 9)], 0),
     (4, 1, 64, 16, [(500, 1500), (7, 7)], 0),
+    # small pages: one buffer per prefill wave's rows (d 256: 4 rows, d 512: 4 rows)
+    (8, 1, 256, 16, [(700, 2100)], 1400),
+    (16, 2, 512, 8, [(300, 1800), (2, 9)], 0),
 ])
 def test_prefill_splits(hq, hkv, d, b, seqs, window):
     """Long prefill items cut along their key range: the partial results,
