@@ -98,8 +98,11 @@ int rpa_create(const rpa_config* cfg, rpa_ctx** out_ctx);
  * the window of a sequence's first query token, and the pool's other pages
  * may hold anything (even NaN): they are never read into the result.
  * Every argument check runs on the host before anything is enqueued: a call
- * that returns an error has enqueued nothing.  Page-table *values* are device
- * data and are not checked.  Returns RPA_OK, RPA_ERR_INVALID_ARG, RPA_ERR_OOM
+ * that returns an error has enqueued nothing.  A call without query tokens
+ * (cu_q_lens[num_seqs] == 0) enqueues nothing and returns RPA_OK once its
+ * metadata has passed; its device pointers may then be NULL (as torch gives
+ * for empty tensors).  Page-table *values* are device data and are not
+ * checked.  Returns RPA_OK, RPA_ERR_INVALID_ARG, RPA_ERR_OOM
  * or RPA_ERR_HIP; rpa_last_error() then holds a message.
  *
  * Ordering: the calls of one context run in the order they are made, also
@@ -180,8 +183,8 @@ int rpa_forward_noalloc(rpa_ctx* ctx, const void* q, const void* k_pages, const 
  * sequence are written by a copy kernel that runs before the attention
  * kernels.  Page slots of different tokens must be distinct (a page table
  * that maps two positions to one slot leaves either row there).  Errors as
- * for rpa_forward, plus RPA_ERR_INVALID_ARG for a NULL k_new / v_new or
- * k_pages == v_pages.
+ * for rpa_forward, plus RPA_ERR_INVALID_ARG for a NULL k_new / v_new (in a
+ * call with query tokens) or k_pages == v_pages.
  */
 int rpa_forward_append(rpa_ctx* ctx, const void* q, const void* k_new, const void* v_new, void* k_pages,
                        void* v_pages, const int32_t* page_table, const int32_t* cu_q_lens,

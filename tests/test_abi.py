@@ -315,3 +315,23 @@ def test_forward_fp8_append_rejects_bad_arguments_before_launch():
                                     ctypes.c_void_p(0x7000000), None)
     assert st == _lib.RPA_ERR_INVALID_ARG and "same buffer" in lib.rpa_last_error(ctx).decode()
     lib.rpa_destroy(ctx)
+
+
+def test_calls_without_query_tokens_accept_null_device_pointers():
+    """A call whose sequences have no query tokens enqueues nothing and needs
+    no device buffer (torch hands NULL for empty tensors), appending calls
+    included; metadata is still checked."""
+    lib, st, ctx = _ctx()
+    cu_a, cu_p = i32([0, 0, 0])
+    kv_a, kv_p = i32([5, 9])
+    assert lib.rpa_forward(ctx, None, None, None, None, cu_p, kv_p, 2, 0, 1.0, None, None) == _lib.RPA_OK
+    assert lib.rpa_forward_append(ctx, None, None, None, None, None, None, cu_p, kv_p, 2, 0, 1.0, None,
+                                  None) == _lib.RPA_OK
+    assert lib.rpa_forward_fp8(ctx, None, None, None, FAKE, FAKE, None, cu_p, kv_p, 2, 0, 1.0, None,
+                               None) == _lib.RPA_OK
+    assert lib.rpa_forward_fp8_append(ctx, None, None, None, None, None, FAKE, FAKE, None, cu_p, kv_p, 2, 0, 1.0,
+                                      None, None) == _lib.RPA_OK
+    bad_cu_a, bad_cu_p = i32([0, 0, -1])   # not non-decreasing
+    assert lib.rpa_forward_append(ctx, None, None, None, None, None, None, bad_cu_p, kv_p, 2, 0, 1.0, None,
+                                  None) == _lib.RPA_ERR_INVALID_ARG
+    lib.rpa_destroy(ctx)
