@@ -1666,6 +1666,7 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
                                        __HIP_MEMORY_SCOPE_AGENT) == it.num_splits - 1;
   __syncthreads();
   if (*lds_flag == 0) return;
+  asm volatile("" ::: "memory");   // no read of the workspace moves above the ticket
   merge_group<D>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, ROWS, tid, C::NT);
   if (tid == 0) __hip_atomic_store(args.merge_tickets + it.split_group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
