@@ -265,3 +265,60 @@ def test_fused_merge_reads_the_splits_writes_not_stale_lines():
         again, _ = fresh_call(wa, ha, da)
         bad = bitwise_mismatch(again, first, ha, f"call {i + 2} after the other step")
         assert not bad, bad
+
+
+@pytest.mark.parametrize("page_size", [128, 16, 8])
+@pytest.mark.parametrize("mode", ["bf16", "bf16_append", "fp8_staged", "fp8_converting"])
+def test_pages_past_4gib_give_the_same_bits(mode, page_size):
+    """Every page address is 64-bit: the same pages placed past the first
+    4 GiB of a pool of more than 4 GiB per tensor (page-table entries moved
+    up by as many pages) give bit for bit the result of a small pool, in
+    every page mode (a page per tile or chunk, per run of 16 keys or of a
+    wave's rows, per lane) and with an fp8 cache both ways; an appending
+    call writes the same bytes there."""
+    from append_common import stale_pages_and_new_rows
+    w = wl.custom([(60, 300), (1, 517), (1, 90), (200, 200), (3, 1000), (1, 33)], 8, 2, 128, page_size, 0,
+                  seed=600 + page_size)
+    fp8 = mode.startswith("fp8")
+    if fp8:
+        f = wl.make_fp8_inputs(w, poison=True)
+        inp, k_small, v_small = f.base, f.k_pages, f.v_pages
+    else:
+        inp = wl.make_inputs(w, poison=True)
+        k_small, v_small = inp.k_pages, inp.v_pages
+    if mode == "bf16_append":
+        k_new, k_small, v_new, v_small = stale_pages_and_new_rows(inp)
+    page_bytes = k_small[0].numel() * k_small.element_size()
+    base = -(-(int(4.25 * 2 ** 30)) // page_bytes)   # first page id past 4.25 GiB
+    n_pages = k_small.shape[0]
+
+    def run(k, v, table):
+        attn = make_attn(w)
+        if fp8:
+            attn.set_option(R.RPA_OPT_FP8_STAGE, 1 if mode == "fp8_staged" else 0)
+            out = attn.forward_fp8(inp.q.cuda(), k, v, f.k_scales.cuda(), f.v_scales.cuda(), table, inp.cu_q_lens,
+                                   inp.kv_lens, 0, w.scale)
+        elif mode == "bf16_append":
+            out = attn.forward_append(inp.q.cuda(), k_new.cuda(), v_new.cuda(), k, v, table, inp.cu_q_lens,
+                                      inp.kv_lens, 0, w.scale)
+        else:
+            out = attn.forward(inp.q.cuda(), k, v, table, inp.cu_q_lens, inp.kv_lens, 0, w.scale)
+        torch.cuda.synchronize()
+        attn.close()
+        return out
+
+    ks, vs = k_small.cuda(), v_small.cuda()
+    small = run(ks, vs, inp.page_table.cuda()).clone()
+    kb = torch.zeros((base + n_pages,) + tuple(k_small.shape[1:]), dtype=k_small.dtype, device="cuda")
+    vb = torch.zeros_like(kb)
+    kb[base:] = k_small.cuda()
+    vb[base:] = v_small.cuda()
+    big = run(kb, vb, (inp.page_table + base).cuda())
+    assert kb.numel() * kb.element_size() > 4 * 2 ** 30
+    bad = bitwise_mismatch(big, small, inp, f"{mode} B{page_size}: pages past 4 GiB")
+    assert not bad, bad
+    if mode == "bf16_append":
+        assert torch.equal(kb[base:].view(torch.int16), ks.view(torch.int16))
+        assert torch.equal(vb[base:].view(torch.int16), vs.view(torch.int16))
+    del kb, vb
+    torch.cuda.empty_cache()
