@@ -61,6 +61,11 @@ typedef struct rpa_config {
   int32_t max_pages_per_seq; /* row stride of page_table, >= 1                  */
   int64_t max_q_tokens;      /* most query tokens of one call                   */
 } rpa_config;
+/* Page size and speed: the kernels read a run of keys that lies in one page
+ * through one buffer (a whole prefill tile or decode chunk when B is a
+ * multiple of 32 or 64 keys, a 16-key run or one wave's rows of a prefill
+ * tile when B is a multiple of 16, or of 4 at D = 256 and 512); any other B
+ * works with a page lookup per lane, about 7-18 % slower. */
 
 /*
  * rpa_create -- validate `cfg` and allocate a context (host memory only; the
