@@ -305,9 +305,21 @@ RPA_DEV void sched_reads_ahead() {
   }
 }
 
+// Waves per SIMD a prefill shape is built for: two (fragments of up to 256
+// VGPRs per wave), or three for a shape whose fragments fit 168 VGPRs.
+template <int D, int BN, int NW, int NB, int NS, int DS>
+struct PrefillWaves {
+  static constexpr int PER_SIMD = 2;
+};
+template <>
+struct PrefillWaves<128, 32, 4, 1, 2, 1> {
+  static constexpr int PER_SIMD = 3;
+};
+
 template <int D, int BN, int NW, int NB, int NS, int DS = 1, bool KV8 = false>
 struct PrefillCfg {
   static constexpr int NT = NW * 64;
+  static constexpr int WAVES_PER_SIMD = PrefillWaves<D, BN, NW, NB, NS, DS>::PER_SIMD;
   static constexpr int DH = D / DS;                  // head columns per wave
   static constexpr int ROWS = (NW / DS) * NB * 32;   // query rows per workgroup
   static constexpr int ROW_B = D * 2;                // bytes per key row
@@ -340,8 +352,9 @@ struct PrefillCfg {
   // after the current one's products).
   static constexpr int STAGE8 = 2 * BN * D;
   static constexpr int LOADS8 = BN * D / 1024 / NW;  // 1 KB direct loads per wave per tensor
-  static constexpr int WGS = (160 * 1024) / (NS * STAGE_B) < 8 * 64 / NT ? (160 * 1024) / (NS * STAGE_B)
-                                                                           : 8 * 64 / NT;   // bf16 form, per CU
+  static constexpr int WGS = (160 * 1024) / (NS * STAGE_B) < 4 * WAVES_PER_SIMD * 64 / NT
+                                 ? (160 * 1024) / (NS * STAGE_B)
+                                 : 4 * WAVES_PER_SIMD * 64 / NT;   // bf16 form, per CU
   static constexpr int CB = 2 * STAGE_B + NS * STAGE8 <= (160 * 1024) / (WGS > 0 ? WGS : 1) ? 2 : 1;
   static constexpr int LDS_BYTES = KV8 ? CB * STAGE_B + NS * STAGE8 : NS * STAGE_B;
   static constexpr int LPT = 2 * (KV8 ? LOADS8 : LOADS);   // load instructions per wave per tile
@@ -360,7 +373,7 @@ struct PrefillCfg {
 RPA_DEV int xor_k(int s) { return s & 1; }
 
 template <int D, int BN, int NW, int NB, int NS, int DS, int SEG, bool KV8 = false>
-__global__ void __launch_bounds__(NW * 64, 1)
+__global__ void __launch_bounds__(NW * 64, (PrefillWaves<D, BN, NW, NB, NS, DS>::PER_SIMD == 3 ? 3 : 1))
 rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   using C = PrefillCfg<D, BN, NW, NB, NS, DS, KV8>;
   // SEG: keys of an aligned run that lies in one page.  BN: a whole tile
@@ -1794,7 +1807,8 @@ static hipError_t launch_prefill_u(const KernelArgs& a, int n_items, hipStream_t
   return hipGetLastError();
 }
 
-template <int D, int BN, int NW, int NB, int NS, int DS>
+// WITH_KV8 = false builds a shape for bf16 pages only (kv8 must be false).
+template <int D, int BN, int NW, int NB, int NS, int DS, bool WITH_KV8 = true>
 static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, bool kv8, hipStream_t stream) {
   // Buffer descriptors need a run of keys inside one page (the tile, else each
   // wave's rows of it) and 32-bit offsets; otherwise each lane looks up its
@@ -1803,10 +1817,14 @@ static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, bool kv8, h
   const int esz = kv8 ? 1 : 2;
   const bool fits = int64_t(a.page_size) * a.num_kv_heads * D * esz < (int64_t(1) << 31);
   const int seg = !fits ? 0 : a.page_size % BN == 0 ? BN : a.page_size % WR == 0 ? WR : 0;
-  if (kv8) {
-    if (seg == BN) return launch_prefill_u<D, BN, NW, NB, NS, DS, BN, true>(a, n_items, stream);
-    if (seg == WR) return launch_prefill_u<D, BN, NW, NB, NS, DS, WR, true>(a, n_items, stream);
-    return launch_prefill_u<D, BN, NW, NB, NS, DS, 0, true>(a, n_items, stream);
+  if constexpr (WITH_KV8) {
+    if (kv8) {
+      if (seg == BN) return launch_prefill_u<D, BN, NW, NB, NS, DS, BN, true>(a, n_items, stream);
+      if (seg == WR) return launch_prefill_u<D, BN, NW, NB, NS, DS, WR, true>(a, n_items, stream);
+      return launch_prefill_u<D, BN, NW, NB, NS, DS, 0, true>(a, n_items, stream);
+    }
+  } else {
+    if (kv8) return hipErrorInvalidValue;
   }
   if (seg == BN) return launch_prefill_u<D, BN, NW, NB, NS, DS, BN, false>(a, n_items, stream);
   if (seg == WR) return launch_prefill_u<D, BN, NW, NB, NS, DS, WR, false>(a, n_items, stream);
@@ -1899,12 +1917,12 @@ static hipError_t launch_merge_t(const KernelArgs& a, int n_groups, int max_rows
 }
 
 // Prefill workgroups one compute unit holds at once: by LDS (160 KB per
-// compute unit) and by waves (two per SIMD, the register budget the prefill
-// kernels are built for).
+// compute unit) and by waves (the waves per SIMD the shape's register budget
+// is built for).
 template <typename C>
 constexpr int prefill_wgs_per_cu() {
   const int by_lds = (160 * 1024) / C::LDS_BYTES;
-  const int by_waves = 8 * 64 / C::NT;
+  const int by_waves = 4 * C::WAVES_PER_SIMD * 64 / C::NT;
   const int n = by_lds < by_waves ? by_lds : by_waves;
   return n > 0 ? n : 1;
 }
@@ -1916,11 +1934,26 @@ constexpr int prefill_wgs_per_cu() {
 #define RPA_PREFILL_SHAPE_128 128, 64, 4, 1, 2, 1
 #define RPA_PREFILL_SHAPE_256 256, 32, 8, 1, 4, 1
 #define RPA_PREFILL_SHAPE_512 512, 32, 8, 1, 2, 2
+// Calls without decode items (the prefill launch has the compute units to
+// itself), bf16 pages only.  d = 128: 32-key tiles at three waves per SIMD,
+// up to 10 % faster than the shape above on windowed and chunked prefills
+// (a long causal one unchanged), but beside a decode launch it leaves the
+// decode workgroups fewer slots (the decode kernel 7 % slower in a mixed
+// step).
+#define RPA_PREFILL_SHAPE_64_ALONE RPA_PREFILL_SHAPE_64
+#define RPA_PREFILL_SHAPE_128_ALONE 128, 32, 4, 1, 2, 1
+#define RPA_PREFILL_SHAPE_256_ALONE RPA_PREFILL_SHAPE_256
+#define RPA_PREFILL_SHAPE_512_ALONE RPA_PREFILL_SHAPE_512
 
 // Defines the per-head-size entry points called by rpa_dispatch.cpp.
 #define RPA_DEFINE_HEAD_DIM(D)                                                              \
   hipError_t launch_prefill_d##D(const KernelArgs& a, int n, bool kv8, hipStream_t s) {     \
     return launch_prefill_t<RPA_PREFILL_SHAPE_##D>(a, n, kv8, s);                          \
+  }                                                                                         \
+  static_assert(PrefillCfg<RPA_PREFILL_SHAPE_##D##_ALONE>::ROWS == PrefillCfg<RPA_PREFILL_SHAPE_##D>::ROWS, \
+                "the prefill-only shape tiles queries like the shape of mixed steps");     \
+  hipError_t launch_prefill_alone_d##D(const KernelArgs& a, int n, hipStream_t s) {         \
+    return launch_prefill_t<RPA_PREFILL_SHAPE_##D##_ALONE, false>(a, n, false, s);         \
   }                                                                                         \
   hipError_t launch_decode_d##D(const KernelArgs& a, int n, int waves, bool kv8, int rows,    \
                                 hipStream_t s) {                                            \

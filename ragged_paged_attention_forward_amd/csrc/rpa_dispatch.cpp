@@ -10,6 +10,7 @@
 namespace rpa {
 
 hipError_t launch_prefill_d64(const KernelArgs& a, int n, bool kv8, hipStream_t s);
+hipError_t launch_prefill_alone_d64(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d64(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d64(const KernelArgs& a, int n, int rows, hipStream_t s);
 hipError_t launch_append_d64(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
@@ -19,6 +20,7 @@ int prefill_rows_d64();
 int prefill_wgs_per_cu_d64();
 int prefill_fp8_tiles_d64();
 hipError_t launch_prefill_d128(const KernelArgs& a, int n, bool kv8, hipStream_t s);
+hipError_t launch_prefill_alone_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d128(const KernelArgs& a, int n, int rows, hipStream_t s);
 hipError_t launch_append_d128(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
@@ -28,6 +30,7 @@ int prefill_rows_d128();
 int prefill_wgs_per_cu_d128();
 int prefill_fp8_tiles_d128();
 hipError_t launch_prefill_d256(const KernelArgs& a, int n, bool kv8, hipStream_t s);
+hipError_t launch_prefill_alone_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d256(const KernelArgs& a, int n, int rows, hipStream_t s);
 hipError_t launch_append_d256(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
@@ -37,6 +40,7 @@ int prefill_rows_d256();
 int prefill_wgs_per_cu_d256();
 int prefill_fp8_tiles_d256();
 hipError_t launch_prefill_d512(const KernelArgs& a, int n, bool kv8, hipStream_t s);
+hipError_t launch_prefill_alone_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
 hipError_t launch_merge_d512(const KernelArgs& a, int n, int rows, hipStream_t s);
 hipError_t launch_append_d512(const KernelArgs& a, int n, const void* kn, const void* vn, void* kd, void* vd,
@@ -106,11 +110,20 @@ static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
   return a;
 }
 
-hipError_t launch_prefill(const LaunchArgs& l, const rpa_work_item* items, int n_items) {
+hipError_t launch_prefill(const LaunchArgs& l, const rpa_work_item* items, int n_items, bool alone) {
   if (n_items <= 0) return hipSuccess;
   const KernelArgs a = make_args(l, items);
   hipStream_t s = static_cast<hipStream_t>(l.stream);
   const bool kv8 = l.kv_fp8 != 0;
+  if (alone && !kv8) {
+    switch (l.head_dim) {
+      case 64: return launch_prefill_alone_d64(a, n_items, s);
+      case 128: return launch_prefill_alone_d128(a, n_items, s);
+      case 256: return launch_prefill_alone_d256(a, n_items, s);
+      case 512: return launch_prefill_alone_d512(a, n_items, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (l.head_dim) {
     case 64: return launch_prefill_d64(a, n_items, kv8, s);
     case 128: return launch_prefill_d128(a, n_items, kv8, s);

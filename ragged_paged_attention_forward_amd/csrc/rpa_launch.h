@@ -46,7 +46,10 @@ int prefill_wgs_per_cu_for(int head_dim);
 int prefill_fp8_tiles_for(int head_dim);
 bool head_dim_supported(int head_dim);
 
-hipError_t launch_prefill(const LaunchArgs& a, const rpa_work_item* items, int n_items);
+// alone: the call has no decode items (the prefill launch has the compute
+// units to itself), which picks the head size's prefill-only tile shape for
+// a bf16 launch.
+hipError_t launch_prefill(const LaunchArgs& a, const rpa_work_item* items, int n_items, bool alone);
 // rows: 16 for the one-block decode kernel, 32 for the two-block one.
 hipError_t launch_decode(const LaunchArgs& a, const rpa_work_item* items, int n_items, int rows);
 // Merges split groups a.groups[0 .. n_groups) (max_rows: the most rows of a

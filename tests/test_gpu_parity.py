@@ -318,6 +318,35 @@ def test_prefill_splits(hq, hkv, d, b, seqs, window):
     assert (base.float() - got.float()).abs().max().item() <= 2e-2
 
 
+@pytest.mark.parametrize("b", [128, 16, 8, 24, 3])
+@pytest.mark.parametrize("window", [0, 333])
+def test_prefill_only_calls_head_size_128(b, window):
+    """A call with no decode items at head size 128 runs the prefill tile of
+    32 keys at three waves per SIMD (8 rows per wave, so page sizes 8 and 16
+    read one buffer per wave's rows, 24 and 3 read per lane): oracle parity
+    with the key range whole and cut into splits, and the same bits on a
+    repeated call.  A decode added to the same call switches back to the
+    64-key tile, which must agree with the oracle too."""
+    seqs = [(700, 1900), (130, 130), (65, 1000), (33, 97)]
+    w = wl.custom(seqs, 8, 2, 128, b, window, seed=b + window)
+    inp = wl.make_inputs(w, poison=True)
+    ref = oracle_rows(inp)
+    for split in (-1, 256):
+        attn = make_attn(w)
+        attn.set_option(R.RPA_OPT_PREFILL_SPLIT_KEYS, split)
+        info, _ = attn.plan(inp.cu_q_lens, inp.kv_lens, window)
+        assert info["num_decode_items"] == 0
+        got = run_gpu(attn, inp).clone()
+        compare(got, ref, label=f"prefill only B={b} W={window} split={split}")
+        assert torch.equal(run_gpu(attn, inp), got)
+    w2 = wl.custom(seqs + [(1, 500)], 8, 2, 128, b, window, seed=b + window + 1)
+    inp2 = wl.make_inputs(w2, poison=True)
+    attn = make_attn(w2)
+    info, _ = attn.plan(inp2.cu_q_lens, inp2.kv_lens, window)
+    assert info["num_decode_items"] > 0
+    compare(run_gpu(attn, inp2), oracle_rows(inp2), label=f"with a decode B={b} W={window}")
+
+
 @pytest.mark.parametrize("n_prefill", [300, 12])
 def test_concurrent_decode_stream(n_prefill):
     """Prefill items (more than the compute units, or a few) plus decodes: the
