@@ -1111,13 +1111,18 @@ struct MergeCfg {
 // Merges the n partials of one split group (rows q_count * G of tokens from
 // q_start, KV head kv_head) into the bf16 output; threads tid of nthreads.
 // Split i's rows start at row i * rps of the group's block (rps = 16 for
-// decode splits, the tile's row count for prefill splits).
-template <int D>
+// decode splits, the tile's row count for prefill splits).  Each thread
+// takes PER column slots per pass (tid, tid + nthreads, ...) and issues the
+// loads of all of them before it combines any, so a group of up to
+// PER * nthreads slots costs one memory round trip; the arithmetic of a
+// slot does not depend on PER.
+template <int D, int PER = 1>
 RPA_DEV void merge_group(const KernelArgs& args, int q_start, int q_count, int kv_head, int partial_base,
                          int n, int rps, int tid, int nthreads) {
   constexpr int C4 = D / 4;
   constexpr int NB = 8;   // splits fetched per batch: every load of a batch is in flight at once
   const int rows = q_count * args.group;
+  const int total = rows * C4;
   // Device-scope loads (they miss the compute unit's vector cache and read
   // what other compute units wrote): the fused merge runs in the launch
   // that writes the partials, after the last split's ticket, and a cached
@@ -1127,45 +1132,66 @@ RPA_DEV void merge_group(const KernelArgs& args, int q_start, int q_count, int k
       make_rsrc(args.partial_lse + static_cast<int64_t>(partial_base) * 16, static_cast<uint32_t>(n * rps * 4));
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(args.partial_o + static_cast<int64_t>(partial_base) * 16 * D,
                                                static_cast<uint32_t>(n * rps * D * 4));
-  for (int idx = tid; idx < rows * C4; idx += nthreads) {
-    const int r = idx / C4;
-    const int c = idx - r * C4;
-    float mx = kNegInf, wsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int i0 = 0; i0 < n; i0 += NB) {
-      float l[NB];
-      f32x4 v[NB];
+  for (int i0 = tid; i0 < total; i0 += nthreads * PER) {
+    float mx[PER], wsum[PER];
+    f32x4 acc[PER];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const bool ok = i0 + b < n;
-        const int slot_row = (i0 + b) * rps + r;
-        l[b] = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, slot_row * 4, 0, kDeviceScope))
-                  : kNegInf;
-        v[b] = ok ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, (slot_row * D + c * 4) * 4, 0,
-                                                                                     kDeviceScope))
-                  : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      float bm = mx;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) bm = fmaxf(bm, l[b]);
-      const float base = (bm == kNegInf) ? 0.f : bm;
-      const float rescale = fast_exp2(mx - base);   // running sums to the new maximum
-      wsum *= rescale;
-      acc *= rescale;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float w = fast_exp2(l[b] - base);
-        wsum += w;
-        acc += w * v[b];
-      }
-      mx = bm;
+    for (int p = 0; p < PER; ++p) {
+      mx[p] = kNegInf;
+      wsum[p] = 0.f;
+      acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    acc *= wsum > 0.f ? 1.f / wsum : 0.f;
-    const int tk = r / args.group;
-    const int hh = r - tk * args.group;
-    uint16_t* dst = args.out + (static_cast<int64_t>(q_start + tk) * args.num_q_heads +
-                                kv_head * args.group + hh) * D + c * 4;
-    *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    for (int s0 = 0; s0 < n; s0 += NB) {
+      float l[PER][NB];
+      f32x4 v[PER][NB];
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = i0 + p * nthreads;
+        const int r = idx / C4;
+        const int c = idx - r * C4;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const bool ok = s0 + b < n && idx < total;
+          const int slot_row = (s0 + b) * rps + r;
+          l[p][b] = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, slot_row * 4, 0,
+                                                                                        kDeviceScope))
+                       : kNegInf;
+          v[p][b] = ok ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       ors, (slot_row * D + c * 4) * 4, 0, kDeviceScope))
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        float bm = mx[p];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) bm = fmaxf(bm, l[p][b]);
+        const float base = (bm == kNegInf) ? 0.f : bm;
+        const float rescale = fast_exp2(mx[p] - base);   // running sums to the new maximum
+        wsum[p] *= rescale;
+        acc[p] *= rescale;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float w = fast_exp2(l[p][b] - base);
+          wsum[p] += w;
+          acc[p] += w * v[p][b];
+        }
+        mx[p] = bm;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = i0 + p * nthreads;
+      if (idx >= total) break;
+      const int r = idx / C4;
+      const int c = idx - r * C4;
+      const f32x4 o = acc[p] * (wsum[p] > 0.f ? 1.f / wsum[p] : 0.f);
+      const int tk = r / args.group;
+      const int hh = r - tk * args.group;
+      uint16_t* dst = args.out + (static_cast<int64_t>(q_start + tk) * args.num_q_heads +
+                                  kv_head * args.group + hh) * D + c * 4;
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
   }
 }
 
@@ -1680,7 +1706,9 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   __syncthreads();
   if (*lds_flag == 0) return;
   asm volatile("" ::: "memory");   // no read of the workspace moves above the ticket
-  merge_group<D>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, ROWS, tid, C::NT);
+  // column slots per thread: a group of 8 rows (16 at d <= 128) in one pass of four waves
+  constexpr int MPER = D >= 512 ? 4 : D >= 128 ? 2 : 1;
+  merge_group<D, MPER>(args, it.q_start, it.q_count, it.kv_head, it.partial_base, it.num_splits, ROWS, tid, C::NT);
   if (tid == 0) __hip_atomic_store(args.merge_tickets + it.split_group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
