@@ -184,9 +184,19 @@ int rpa_forward_noalloc(rpa_ctx* ctx, const void* q, const void* k_pages, const 
  * the call sees them.  A sequence whose new tokens all sit in one decode
  * item (rpa_work_item.self_append) has them written by the decode kernel
  * itself: the wave that reads the 32-key chunk holding a new key writes that
- * key's rows just before it reads the chunk.  The rows of every other
- * sequence are written by a copy kernel that runs before the attention
- * kernels.  Page slots of different tokens must be distinct (a page table
+ * key's rows just before it reads the chunk.  With a bf16 cache the prefill
+ * kernel takes the keys of a prefill sequence's new tokens straight from
+ * k_new / v_new (the key of position p is row cu_q_lens[s] + p - (kv_len -
+ * q_len) there) and each query tile's workgroup writes its own tokens' rows
+ * into their slots after its products, so no workgroup of the call reads
+ * those slots -- when every prefill sequence's first new position (kv_len -
+ * q_len) is a multiple of the keys the kernel loads per buffer run (a key
+ * tile, or one wave's rows of it: 4 to 64 keys by head size and page size;
+ * always for prefills without prior context) and the prefill launch holds
+ * at most two workgroups per slot of the device.  The rows of every other
+ * sequence (fp8 caches, a sequence's tokens spread over several decode
+ * items, the other prefill launches) are written by a copy kernel that runs
+ * before the attention kernels.  Page slots of different tokens must be distinct (a page table
  * that maps two positions to one slot leaves either row there).  Errors as
  * for rpa_forward, plus RPA_ERR_INVALID_ARG for a NULL k_new / v_new (in a
  * call with query tokens) or k_pages == v_pages.
@@ -414,9 +424,17 @@ typedef struct rpa_work_item {
   int32_t kind;         /* 0: prefill kernel item, 1: decode kernel item (<= 16
                            rows), 2: two-block decode kernel item (17..32 rows);
                            a split group has the kind of its splits               */
-  int32_t self_append;  /* 1: a decode item holding every new token of its
-                           sequence; in an appending call it writes their K/V
-                           rows itself (the split whose key range holds them) */
+  int32_t self_append;  /* 1: in an appending call with a bf16 cache the item
+                           writes K/V rows of new tokens itself: a decode item
+                           holding every new token of its sequence (the split
+                           whose key range holds them), or split 0 of a
+                           prefill item (its own query tokens' rows, KV head
+                           kv_head) when the call's prefill launch takes the
+                           new rows (see rpa_forward_append); 0: the copy
+                           kernel writes them                                */
+  int32_t new_pos0;     /* position of the sequence's first new token
+                           (kv_len - q_len): an appending call's prefill
+                           kernel reads keys from it on from k_new / v_new  */
 } rpa_work_item;
 
 typedef struct rpa_plan_info {

@@ -46,7 +46,7 @@ class Config(ctypes.Structure):
 class WorkItem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "seq", "kv_head", "q_start", "q_count", "q_pos0", "kv_begin", "kv_end", "split_group",
-        "split_index", "num_splits", "partial_base", "kind", "self_append")]
+        "split_index", "num_splits", "partial_base", "kind", "self_append", "new_pos0")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

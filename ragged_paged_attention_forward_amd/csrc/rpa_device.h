@@ -251,6 +251,15 @@ RPA_DEV void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, char* dst, int byte_of
                :: "v"(byte_off), "s"(base), "s"(rs) : "memory", "m0");
 }
 #pragma clang diagnostic pop
+// A wave-uniform pointer / value kept in scalar registers (buffer
+// descriptors must be built from them).
+RPA_DEV const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32)));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+RPA_DEV uint32_t uniform_u32(uint32_t v) { return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v))); }
 // 16 bytes per lane from a global address straight into LDS at dst + 16 * lane.
 RPA_DEV void global_load_lds16(const char* src, char* dst) {
   __builtin_amdgcn_global_load_lds((global_cptr)(src), (lds_ptr)(dst), 16, 0, 0);
@@ -372,10 +381,11 @@ struct PrefillCfg {
 
 RPA_DEV int xor_k(int s) { return s & 1; }
 
-template <int D, int BN, int NW, int NB, int NS, int DS, int SEG, bool KV8 = false>
+template <int D, int BN, int NW, int NB, int NS, int DS, int SEG, bool KV8 = false, bool AP = false>
 __global__ void __launch_bounds__(NW * 64, (PrefillWaves<D, BN, NW, NB, NS, DS>::PER_SIMD == 3 ? 3 : 1))
 rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   using C = PrefillCfg<D, BN, NW, NB, NS, DS, KV8>;
+  static_assert(!(AP && KV8), "new rows are taken from k_new / v_new with a bf16 cache only");
   // SEG: keys of an aligned run that lies in one page.  BN: a whole tile
   // (pages of a multiple of BN keys); BN / NW: the rows that one wave stages
   // of a tile; 0: a page id per lane.
@@ -465,6 +475,15 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   const int kv_begin = it.kv_begin;
   const int kv_end = it.kv_end;
   const int n_tiles = (kv_end - tile0 + BN - 1) / BN;
+  // AP (an appending call): keys from the sequence's first new position
+  // new0 on are this step's tokens, whose rows are k_new / v_new rows
+  // new_row + key (the same row pitch as a page).  They are read from there:
+  // their page slots are written by this launch, by the workgroup of each
+  // query tile after its products, and read by none of its workgroups.
+  // (The launcher runs this form only where new0 is a multiple of the
+  // buffer runs, SEG keys, so that no run mixes pool and new rows.)
+  [[maybe_unused]] const int new0 = AP ? it.new_pos0 : 0;
+  [[maybe_unused]] const int64_t new_row = static_cast<int64_t>(it.q_start) - it.q_pos0;
   // Tile order: step t takes tile (t + rot) mod n_tiles of the range, with rot
   // chosen so that its global index (key / BN) is congruent to t modulo
   // n_tiles.  The online softmax is indifferent to the order of the tiles,
@@ -586,7 +605,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     // boundary) and past kv_end read as zero, and are masked later.
     const int lo = k0 > kv_begin ? k0 : kv_begin;
     const int hi = k0 + BN < kv_end ? k0 + BN : kv_end;
-    if constexpr (UNI) {
+    if constexpr (UNI && !AP) {
       // The tile lies in one page.  The buffer starts at row lo and ends
       // after row hi - 1: rows below lo have negative offsets, which wrap
       // above the record count, so they read as zero like rows past hi.
@@ -600,7 +619,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
         buffer_load_lds16(krs, kdst + i * C::BLK_K, srow[i] * row_bytes + sgk[i] - rel_b);
         buffer_load_lds16(vrs, vdst + i * C::BLK_V, srow[i] * row_bytes + sgv[i] - rel_b);
       }
-    } else if constexpr (BUF) {
+    } else if constexpr (BUF && !AP) {
       // This wave's rows lie in one page: the same loads against a buffer
       // over the run's rows inside [lo, hi).
       int64_t base_off;
@@ -609,6 +628,49 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       run_rows(ts, k0, lo, hi, row_bytes, 2, base_off, nbytes, rel_b);
       const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const char*>(kbase) + base_off, nbytes);
       const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const char*>(vbase) + base_off, nbytes);
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        buffer_load_lds16(krs, kdst + i * C::BLK_K, srow[i] * row_bytes + sgk[i] - rel_b);
+        buffer_load_lds16(vrs, vdst + i * C::BLK_V, srow[i] * row_bytes + sgv[i] - rel_b);
+      }
+    } else if constexpr (UNI) {
+      // AP, the tile in one page: a tile below new0 reads the pool and one
+      // from new0 on reads k_new / v_new, both as above (the same buffer
+      // bounds).  No tile holds keys on both sides of new0: the AP form runs
+      // only where new0 sits on a tile boundary.
+      const int64_t trow = next_tile_row();   // page slot row of key k0
+      const int rel_b = (lo - k0) * row_bytes;
+      const uint32_t nbytes = uniform_u32(static_cast<uint32_t>((hi - lo - 1) * row_bytes + D * 2));
+      const bool fresh = lo >= new0;
+      const int64_t base_off = (((fresh ? new_row + lo : trow + (lo - k0))) * hkv + g) * D;
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(uniform_ptr((fresh ? args.k_new : kbase) + base_off), nbytes);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(uniform_ptr((fresh ? args.v_new : vbase) + base_off), nbytes);
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        buffer_load_lds16(krs, kdst + i * C::BLK_K, srow[i] * row_bytes + sgk[i] - rel_b);
+        buffer_load_lds16(vrs, vdst + i * C::BLK_V, srow[i] * row_bytes + sgv[i] - rel_b);
+      }
+    } else if constexpr (BUF) {
+      // AP, this wave's rows in one page: the run's rows come from the pool,
+      // or (from new0 on) from k_new / v_new.  No run holds keys on both
+      // sides of new0: the AP form runs only where new0 sits on a run
+      // boundary.
+      int64_t base_off;
+      uint32_t nbytes;
+      int rel_b;
+      run_rows(ts, k0, lo, hi, row_bytes, 2, base_off, nbytes, rel_b);
+      const int s0 = k0 + wave * SEG;
+      const int slo = s0 > lo ? s0 : lo;
+      const int shi = s0 + SEG < hi ? s0 + SEG : hi;
+      const char* kb = reinterpret_cast<const char*>(kbase) + base_off;
+      const char* vb = reinterpret_cast<const char*>(vbase) + base_off;
+      if (slo >= new0 && shi > slo) {
+        const int64_t noff = ((new_row + slo) * hkv + g) * D * 2;
+        kb = reinterpret_cast<const char*>(args.k_new) + noff;
+        vb = reinterpret_cast<const char*>(args.v_new) + noff;
+      }
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(uniform_ptr(kb), nbytes);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(uniform_ptr(vb), nbytes);
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
         buffer_load_lds16(krs, kdst + i * C::BLK_K, srow[i] * row_bytes + sgk[i] - rel_b);
@@ -623,11 +685,15 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       for (int i = 0; i < C::LOADS; ++i) {
         int key = k0 + srow[i];
         key = key < lo ? lo : (key < hi ? key : hi - 1);
+        const bool fresh = AP && key >= new0;   // (AP) a new key: its k_new / v_new row
         const int pidx = key / page_size;
-        const int64_t page = pt_row[pidx];
-        const int64_t off = ((page * page_size + (key - pidx * page_size)) * hkv + g) * D * 2;
-        global_load_lds16(reinterpret_cast<const char*>(kbase) + off + sgk[i], kdst + i * C::BLK_K);
-        global_load_lds16(reinterpret_cast<const char*>(vbase) + off + sgv[i], vdst + i * C::BLK_V);
+        const int64_t page = fresh ? 0 : pt_row[pidx];
+        const int64_t row = fresh ? new_row + key : page * page_size + (key - pidx * page_size);
+        const int64_t off = (row * hkv + g) * D * 2;
+        global_load_lds16(reinterpret_cast<const char*>(fresh ? args.k_new : kbase) + off + sgk[i],
+                          kdst + i * C::BLK_K);
+        global_load_lds16(reinterpret_cast<const char*>(fresh ? args.v_new : vbase) + off + sgv[i],
+                          vdst + i * C::BLK_V);
       }
     }
   };
@@ -974,6 +1040,43 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     }
   }
 
+  // AP: split 0 of a query tile writes its tokens' K/V rows (KV head g)
+  // into their page slots after its products (the copy kernel's work for
+  // these tokens): 16-byte pieces, U of them per thread in flight (more
+  // spill registers at d = 256 and 512).
+  auto write_new_rows = [&]() {
+    if constexpr (AP) {
+      if (it.self_append == 0) return;
+      constexpr int CH = D / 8;   // 16-byte pieces per row
+      constexpr int U = 8;
+      const int n = it.q_count * CH * 2;   // (token, K or V, piece)
+      uint16_t* kpool = const_cast<uint16_t*>(kbase);
+      uint16_t* vpool = const_cast<uint16_t*>(vbase);
+      for (int i0 = tid; i0 < n; i0 += C::NT * U) {
+        u32x4 val[U];
+        int64_t dst[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int idx = i0 + u * C::NT;
+          const bool ok = idx < n;
+          const int rr = idx / CH;
+          const int c = idx - rr * CH;
+          const int r = rr >> 1;
+          const int pos = it.q_pos0 + r;
+          const int64_t page = ok ? pt_row[pos / page_size] : 0;
+          const int64_t src = (static_cast<int64_t>(it.q_start + r) * hkv + g) * D + c * 8;
+          val[u] = ok ? load16(((rr & 1) ? args.v_new : args.k_new) + src) : u32x4{0, 0, 0, 0};
+          dst[u] = ((page * page_size + pos % page_size) * hkv + g) * D + c * 8;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int idx = i0 + u * C::NT;
+          if (idx < n) *reinterpret_cast<u32x4*>((((idx / CH) & 1) ? vpool : kpool) + dst[u]) = val[u];
+        }
+      }
+    }
+  };
+
   constexpr int OROWS = NB * 32;   // rows per wave
   if (it.split_group >= 0) {
     // ---- a split of a long item: normalised fp32 O and base-2 LSE per row ----
@@ -1048,6 +1151,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
         }
       }
     }
+    write_new_rows();
     return;
   }
 
@@ -1096,6 +1200,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       *reinterpret_cast<u32x4*>(args.out + (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D +
                                 dh * DH + cc * 8) = v;
   }
+  write_new_rows();
 }
 
 // ---------------------------------------------------------------------------
@@ -1734,8 +1839,9 @@ rpa_append_kernel(const rpa_work_item* __restrict__ items, const int32_t* __rest
                   uint16_t* __restrict__ k_dst, uint16_t* __restrict__ v_dst, KernelArgs args) {
   const rpa_work_item it = items[blockIdx.x];
   // decode items that hold all of their sequence's new tokens write them
-  // themselves (the decode kernel's fused write)
-  if (it.split_index != 0 || it.self_append != 0) return;
+  // themselves (the decode kernel's fused write), and so do prefill items
+  // when the prefill launch takes the call's new rows (prefill_writes)
+  if (it.split_index != 0 || (it.self_append != 0 && (it.kind != 0 || args.prefill_writes != 0))) return;
   constexpr int CH = D / 8;   // 16-byte chunks per row
   const int hkv = args.num_kv_heads;
   const int ps = args.page_size;
@@ -1819,32 +1925,48 @@ rpa_stage_kernel(const int32_t* __restrict__ stage, const int32_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int D, int BN, int NW, int NB, int NS, int DS, int SEG, bool KV8>
-static hipError_t launch_prefill_u(const KernelArgs& a, int n_items, hipStream_t stream) {
+template <int D, int BN, int NW, int NB, int NS, int DS, int SEG, bool KV8, bool AP>
+static hipError_t launch_prefill_v(const KernelArgs& a, int n_items, hipStream_t stream) {
   using C = PrefillCfg<D, BN, NW, NB, NS, DS, KV8>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, NS, DS, SEG, KV8>),
+        reinterpret_cast<const void*>(&rpa_prefill_kernel<D, BN, NW, NB, NS, DS, SEG, KV8, AP>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, NS, DS, SEG, KV8>), dim3(n_items), dim3(C::NT), C::LDS_BYTES,
-                     stream, a.items, a.page_table, a.q, a.k, a.v, a);
+  hipLaunchKernelGGL((rpa_prefill_kernel<D, BN, NW, NB, NS, DS, SEG, KV8, AP>), dim3(n_items), dim3(C::NT),
+                     C::LDS_BYTES, stream, a.items, a.page_table, a.q, a.k, a.v, a);
   return hipGetLastError();
+}
+
+// bf16 pages with new rows given (an appending call): the AP form, which
+// reads the new tokens' keys from them and writes their rows.
+template <int D, int BN, int NW, int NB, int NS, int DS, int SEG, bool KV8>
+static hipError_t launch_prefill_u(const KernelArgs& a, int n_items, hipStream_t stream) {
+  if constexpr (!KV8) {
+    if (a.k_new != nullptr) return launch_prefill_v<D, BN, NW, NB, NS, DS, SEG, false, true>(a, n_items, stream);
+  }
+  return launch_prefill_v<D, BN, NW, NB, NS, DS, SEG, KV8, false>(a, n_items, stream);
+}
+
+// Keys of a run that the prefill launch of this shape loads through one
+// buffer descriptor: a tile (BN) or a wave's rows of it (BN / NW) when pages
+// hold whole runs and the offsets fit 32 bits; 0: each lane looks up its
+// row's page.  esz: bytes per cache element.
+template <int D, int BN, int NW, int NB, int NS, int DS>
+static int prefill_run_keys(const KernelArgs& a, int esz) {
+  constexpr int WR = BN / NW;
+  const bool fits = int64_t(a.page_size) * a.num_kv_heads * D * esz < (int64_t(1) << 31);
+  return !fits ? 0 : a.page_size % BN == 0 ? BN : a.page_size % WR == 0 ? WR : 0;
 }
 
 // WITH_KV8 = false builds a shape for bf16 pages only (kv8 must be false).
 template <int D, int BN, int NW, int NB, int NS, int DS, bool WITH_KV8 = true>
 static hipError_t launch_prefill_t(const KernelArgs& a, int n_items, bool kv8, hipStream_t stream) {
-  // Buffer descriptors need a run of keys inside one page (the tile, else each
-  // wave's rows of it) and 32-bit offsets; otherwise each lane looks up its
-  // row's page.
   constexpr int WR = BN / NW;
-  const int esz = kv8 ? 1 : 2;
-  const bool fits = int64_t(a.page_size) * a.num_kv_heads * D * esz < (int64_t(1) << 31);
-  const int seg = !fits ? 0 : a.page_size % BN == 0 ? BN : a.page_size % WR == 0 ? WR : 0;
+  const int seg = prefill_run_keys<D, BN, NW, NB, NS, DS>(a, kv8 ? 1 : 2);
   if constexpr (WITH_KV8) {
     if (kv8) {
       if (seg == BN) return launch_prefill_u<D, BN, NW, NB, NS, DS, BN, true>(a, n_items, stream);
@@ -2000,6 +2122,10 @@ constexpr int prefill_wgs_per_cu() {
   }                                                                                         \
   int prefill_rows_d##D() { return PrefillCfg<RPA_PREFILL_SHAPE_##D>::ROWS; }              \
   int prefill_wgs_per_cu_d##D() { return prefill_wgs_per_cu<PrefillCfg<RPA_PREFILL_SHAPE_##D>>(); } \
-  int prefill_fp8_tiles_d##D() { return PrefillCfg<RPA_PREFILL_SHAPE_##D, true>::CB; }
+  int prefill_fp8_tiles_d##D() { return PrefillCfg<RPA_PREFILL_SHAPE_##D, true>::CB; }     \
+  int prefill_run_keys_d##D(const KernelArgs& a, bool alone) {                              \
+    return alone ? prefill_run_keys<RPA_PREFILL_SHAPE_##D##_ALONE>(a, 2)                    \
+                 : prefill_run_keys<RPA_PREFILL_SHAPE_##D>(a, 2);                           \
+  }
 
 }  // namespace rpa

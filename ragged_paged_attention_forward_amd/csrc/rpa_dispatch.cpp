@@ -19,6 +19,7 @@ hipError_t launch_stage_d64(const KernelArgs& a, const int32_t* st, int n, void*
 int prefill_rows_d64();
 int prefill_wgs_per_cu_d64();
 int prefill_fp8_tiles_d64();
+int prefill_run_keys_d64(const KernelArgs& a, bool alone);
 hipError_t launch_prefill_d128(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_prefill_alone_d128(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d128(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
@@ -29,6 +30,7 @@ hipError_t launch_stage_d128(const KernelArgs& a, const int32_t* st, int n, void
 int prefill_rows_d128();
 int prefill_wgs_per_cu_d128();
 int prefill_fp8_tiles_d128();
+int prefill_run_keys_d128(const KernelArgs& a, bool alone);
 hipError_t launch_prefill_d256(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_prefill_alone_d256(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d256(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
@@ -39,6 +41,7 @@ hipError_t launch_stage_d256(const KernelArgs& a, const int32_t* st, int n, void
 int prefill_rows_d256();
 int prefill_wgs_per_cu_d256();
 int prefill_fp8_tiles_d256();
+int prefill_run_keys_d256(const KernelArgs& a, bool alone);
 hipError_t launch_prefill_d512(const KernelArgs& a, int n, bool kv8, hipStream_t s);
 hipError_t launch_prefill_alone_d512(const KernelArgs& a, int n, hipStream_t s);
 hipError_t launch_decode_d512(const KernelArgs& a, int n, int waves, bool kv8, int rows, hipStream_t s);
@@ -49,6 +52,7 @@ hipError_t launch_stage_d512(const KernelArgs& a, const int32_t* st, int n, void
 int prefill_rows_d512();
 int prefill_wgs_per_cu_d512();
 int prefill_fp8_tiles_d512();
+int prefill_run_keys_d512(const KernelArgs& a, bool alone);
 
 int prefill_rows_for(int head_dim) {
   switch (head_dim) {
@@ -107,7 +111,21 @@ static KernelArgs make_args(const LaunchArgs& l, const rpa_work_item* items) {
   a.v_scales = l.v_scales;
   a.k_new = static_cast<const uint16_t*>(l.k_new);
   a.v_new = static_cast<const uint16_t*>(l.v_new);
+  a.prefill_writes = l.prefill_writes;
   return a;
+}
+
+bool prefill_takes_new_rows(const LaunchArgs& l, bool alone, int new_align) {
+  const KernelArgs a = make_args(l, nullptr);
+  int run = 0;
+  switch (l.head_dim) {
+    case 64: run = prefill_run_keys_d64(a, alone); break;
+    case 128: run = prefill_run_keys_d128(a, alone); break;
+    case 256: run = prefill_run_keys_d256(a, alone); break;
+    case 512: run = prefill_run_keys_d512(a, alone); break;
+    default: return false;
+  }
+  return run == 0 || new_align % run == 0;
 }
 
 hipError_t launch_prefill(const LaunchArgs& l, const rpa_work_item* items, int n_items, bool alone) {

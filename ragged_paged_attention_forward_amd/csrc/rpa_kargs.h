@@ -31,6 +31,8 @@ struct KernelArgs {
   const float* v_scales; // fp8 pools: V scale per KV head (else unused)
   const uint16_t* k_new; // appending calls: the step's new K rows [T, Hkv, D] bf16 (else null)
   const uint16_t* v_new; // appending calls: the step's new V rows (else null)
+  int32_t prefill_writes; // appending calls: 1 the prefill kernel writes its items' new rows (the
+                          // append kernel skips them)
 };
 
 }  // namespace rpa

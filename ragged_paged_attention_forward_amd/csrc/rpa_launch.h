@@ -33,6 +33,7 @@ struct LaunchArgs {
   const float* v_scales; // device [Hkv] (fp8 only)
   const void* k_new;     // appending calls: new K rows [T, Hkv, D] bf16 (else null)
   const void* v_new;     // appending calls: new V rows (else null)
+  int32_t prefill_writes;  // appending calls: 1 the prefill kernel writes its items' new rows
   void* stream;
 };
 
@@ -50,6 +51,12 @@ bool head_dim_supported(int head_dim);
 // units to itself), which picks the head size's prefill-only tile shape for
 // a bf16 launch.
 hipError_t launch_prefill(const LaunchArgs& a, const rpa_work_item* items, int n_items, bool alone);
+// Whether a bf16 prefill launch (shape chosen by `alone`) can take an
+// appending call's new rows itself: its K/V loads go in runs of keys that
+// lie in one page (a tile, or a wave's rows of one), and every sequence's
+// first new position (a multiple of new_align) must start a run, so that no
+// run holds both pool rows and new rows; with a page id per lane, always.
+bool prefill_takes_new_rows(const LaunchArgs& a, bool alone, int new_align);
 // rows: 16 for the one-block decode kernel, 32 for the two-block one.
 hipError_t launch_decode(const LaunchArgs& a, const rpa_work_item* items, int n_items, int rows);
 // Merges split groups a.groups[0 .. n_groups) (max_rows: the most rows of a

@@ -183,6 +183,7 @@ static void split_long_prefill_items(const PlanParams& p, Plan* out) {
       if (i + 1 < n) hi = (it.kv_begin + (keys * (i + 1)) / n + 63) / 64 * 64;
       rpa_work_item s = base;
       s.split_index = static_cast<int32_t>(i);
+      s.self_append = i == 0 ? base.self_append : 0;
       s.kv_begin = static_cast<int32_t>(lo);
       s.kv_end = static_cast<int32_t>(hi);
       items.push_back(s);
@@ -211,7 +212,8 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
 
   struct DecodeSeq {
     int32_t seq, q_start, q_count, pos0, kv_begin, kv_end;
-    bool whole;   // the item holds every token of its sequence
+    bool whole;        // the item holds every token of its sequence
+    int32_t new_pos0;  // position of the sequence's first new token
   };
   std::vector<DecodeSeq> dec;
 
@@ -225,7 +227,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
     const bool fits_decode = dec_tokens > 0 && q_len <= dec_tokens;
     const bool use_decode = p.path_mode != 1 && fits_decode;
     if (use_decode) {
-      dec.push_back({s, cu[s], q_len, pos_first, range_begin(pos_first, window), kv_len, true});
+      dec.push_back({s, cu[s], q_len, pos_first, range_begin(pos_first, window), kv_len, true, pos_first});
       continue;
     }
     if (p.path_mode == 3 && dec_tokens > 0) {
@@ -234,7 +236,8 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
       for (int32_t t = 0; t < q_len; t += dec_tokens) {
         const int32_t count = std::min(dec_tokens, q_len - t);
         const int32_t pos0 = pos_first + t;
-        dec.push_back({s, cu[s] + t, count, pos0, range_begin(pos0, window), pos0 + count, count == q_len});
+        dec.push_back({s, cu[s] + t, count, pos0, range_begin(pos0, window), pos0 + count, count == q_len,
+                       pos_first});
       }
       continue;
     }
@@ -254,6 +257,9 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
         it.num_splits = 1;
         it.partial_base = 0;
         it.kind = 0;
+        // bf16 cache: the tile's first split writes its tokens' new rows in an appending call
+        it.self_append = p.kv8 ? 0 : 1;
+        it.new_pos0 = pos_first;
         out->prefill.push_back(it);
       }
     }
@@ -350,6 +356,7 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
       base.q_pos0 = d.pos0;
       base.kind = two ? 2 : 1;
       base.self_append = d.whole ? 1 : 0;
+      base.new_pos0 = d.new_pos0;
       base.num_splits = n;
       if (n == 1) {
         base.kv_begin = d.kv_begin;
@@ -385,8 +392,14 @@ void build_plan(const PlanParams& p, const int32_t* cu, const int32_t* kv, int32
   std::stable_sort(out->decode.begin(), out->decode.end(), longest_first);
   std::stable_sort(out->decode2.begin(), out->decode2.end(), longest_first);
   out->append_items = 0;
+  out->prefill_writer_items = 0;
   for (const auto* list : {&out->prefill, &out->decode, &out->decode2})
     for (const auto& it : *list) out->append_items += (it.split_index == 0 && it.self_append == 0) ? 1 : 0;
+  out->new_align = 1 << 30;
+  for (const auto& it : out->prefill) {
+    out->prefill_writer_items += it.self_append;
+    if (it.new_pos0 > 0) out->new_align = std::min(out->new_align, it.new_pos0 & -it.new_pos0);
+  }
 }
 
 }  // namespace rpa

@@ -54,7 +54,11 @@ struct Plan {
   int64_t visible_pairs = 0;
   int64_t total_q = 0;
   int32_t append_items = 0;            // items whose new rows the append kernel writes (the others
-                                       // write their own in the decode kernel)
+                                       // write their own in the decode or prefill kernel)
+  int32_t prefill_writer_items = 0;    // prefill items that write their query tokens' rows (bf16):
+                                       // the append kernel takes them when the prefill kernel cannot
+  int32_t new_align = 0;               // largest power of two (up to 2^30) dividing the first new
+                                       // position of every sequence served by prefill items
   // Staging (stage_prefill): three ints per staged page (sequence, page of
   // the sequence, page of the bf16 pool), and the bf16 pool's page table
   // [num_seqs * max_pages_per_seq] (rows of staged sequences; 0 elsewhere).

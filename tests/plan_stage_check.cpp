@@ -4,7 +4,12 @@
 // that starts inside a tile) has a staged pool page that maps back to that
 // (sequence, page);
 // pool pages are numbered 0.. in list order; no staging without prefill
-// items.  Exit status 0 when every check holds.
+// items.  And the fields an appending call uses: every item's new_pos0 is
+// its sequence's kv_len - q_len; with a bf16 cache each (token, KV head) of
+// a sequence served by prefill items is written by exactly one of them
+// (split 0 of the query tile holding it, self_append set), with an fp8
+// cache by none (the copy kernel quantizes those rows).
+// Exit status 0 when every check holds.
 #include <algorithm>
 #include <cstdio>
 #include <random>
@@ -27,6 +32,7 @@ int main() {
     p.max_num_seqs = num_seqs;
     p.prefill_rows = 256;
     p.stage_prefill = true;
+    p.kv8 = rng() % 2 == 0;
     p.path_mode = rng() % 4;
     std::vector<int32_t> cu(num_seqs + 1, 0), kv(num_seqs);
     int max_pages = 1;
@@ -49,6 +55,41 @@ int main() {
     rpa::Plan plan;
     rpa::build_plan(p, cu.data(), kv.data(), num_seqs, window, &plan);
     ++planned;
+    // appending-call fields
+    std::vector<int> writes(static_cast<size_t>(cu[num_seqs]) * p.num_kv_heads, 0);
+    std::vector<char> prefill_seq(num_seqs, 0);
+    for (const auto* list : {&plan.prefill, &plan.decode, &plan.decode2})
+      for (const auto& it : *list) bad += it.new_pos0 != kv[it.seq] - (cu[it.seq + 1] - cu[it.seq]);
+    for (const auto& it : plan.prefill) {
+      prefill_seq[it.seq] = 1;
+      const int want = (!p.kv8 && it.split_index == 0) ? 1 : 0;
+      bad += it.self_append != want;
+      if (it.self_append)
+        for (int t = it.q_start; t < it.q_start + it.q_count; ++t)
+          ++writes[static_cast<size_t>(t) * p.num_kv_heads + it.kv_head];
+    }
+    for (int s = 0; s < num_seqs; ++s)
+      if (prefill_seq[s])
+        for (int t = cu[s]; t < cu[s + 1]; ++t)
+          for (int g = 0; g < p.num_kv_heads; ++g)
+            bad += writes[static_cast<size_t>(t) * p.num_kv_heads + g] != (p.kv8 ? 0 : 1);
+    // new_align: a power of two dividing every prefill sequence's first new
+    // position, and the largest one (up to 2^30) that does
+    {
+      int writers = 0;
+      for (const auto& it : plan.prefill) writers += it.self_append;
+      bad += plan.prefill_writer_items != writers;
+      const int a = plan.new_align;
+      bad += a <= 0 || (a & (a - 1)) != 0 || a > (1 << 30);
+      bool all_twice = a < (1 << 30);
+      for (int s = 0; s < num_seqs; ++s)
+        if (prefill_seq[s]) {
+          const int n0 = kv[s] - (cu[s + 1] - cu[s]);
+          bad += a > 0 && n0 % a != 0;
+          all_twice = all_twice && n0 % (2 * a) == 0;
+        }
+      bad += all_twice;
+    }
     if (plan.prefill.empty()) {
       bad += plan.stage_pages != 0;
       continue;

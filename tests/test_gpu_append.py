@@ -94,16 +94,33 @@ def test_append_matches_forward_on_filled_pages_bitwise():
 
 
 def test_append_kernel_is_timed():
-    """A mixed step runs the append kernel for its prefill chunks (timed as its
-    own kind); a step of decodes only writes every new row in the decode
-    kernel (the fused write) and launches no append kernel."""
+    """A step whose sequences' tokens span several decode items (every token
+    through decode items in chunks) runs the append kernel for them (timed as
+    its own kind); a bf16 step of fresh prefills and decodes writes every new
+    row in the attention kernels (the prefill kernel its chunks', the decode
+    kernel its decodes') and launches none, nor does a step of decodes only."""
     w = mixed_small(0)
     attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_PATH, 3)
     attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
-    run_append(w, attn)
+    inp, (k_new, k_stale, v_new, v_stale), kp, vp, out = run_append(w, attn)
     t = attn.kernel_times(R.RPA_KERNEL_APPEND)
     assert len(t) == 1 and t[0] > 0
+    want_k, want_v = ora.append_kv(k_stale, v_stale, inp.page_table, inp.cu_q_lens, inp.kv_lens, k_new, v_new)
+    assert torch.equal(kp.cpu().view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(vp.cpu().view(torch.int16), want_v.view(torch.int16))
+    w = wl.custom([(300, 300), (150, 150), (70, 70), (33, 33)] + [(1, 64 + 23 * i) for i in range(64)], 8, 1, 256,
+                  128, 0, seed=206)
+    attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
+    inp, (k_new, k_stale, v_new, v_stale), kp, vp, out = run_append(w, attn)
+    assert len(attn.kernel_times(R.RPA_KERNEL_APPEND)) == 0
+    assert len(attn.kernel_times(R.RPA_KERNEL_PREFILL)) == 1
     assert len(attn.kernel_times(R.RPA_KERNEL_DECODE)) == 1
+    want_k, want_v = ora.append_kv(k_stale, v_stale, inp.page_table, inp.cu_q_lens, inp.kv_lens, k_new, v_new)
+    assert torch.equal(kp.cpu().view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(vp.cpu().view(torch.int16), want_v.view(torch.int16))
+    compare(out, oracle_rows(inp), label="fresh prefills and decodes, fused writes")
     w = wl.decode()
     attn = make_attn(w)
     attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
@@ -141,8 +158,8 @@ def test_append_in_two_block_decode_items(name, seqs, hq, hkv, d, b, window):
 
 @pytest.mark.parametrize("path", [1, 2])
 def test_append_through_one_kernel_kind(path):
-    """Every sequence through the prefill kernel (path 1: the append kernel
-    writes all rows), or decodes wherever their rows fit (path 2)."""
+    """Every sequence through the prefill kernel (path 1: it writes all
+    rows), or decodes wherever their rows fit (path 2)."""
     w = mixed_small(0)
     attn = make_attn(w)
     attn.set_option(R.RPA_OPT_PATH, path)
@@ -151,6 +168,87 @@ def test_append_through_one_kernel_kind(path):
     assert torch.equal(kp.cpu().view(torch.int16), want_k.view(torch.int16))
     assert torch.equal(vp.cpu().view(torch.int16), want_v.view(torch.int16))
     compare(out, oracle_rows(inp), label=f"path {path}")
+
+
+@pytest.mark.parametrize("name, seqs, hq, hkv, d, b, window, split, fused", [
+    # d 256 (32-key tiles, 8 waves of 4 rows): whole tiles in one page (128), each wave's rows in
+    # one page (16), a page id per lane (6); chunks without prior context, or whose first new key
+    # starts a tile / a wave's run (fused), or sits inside one (the copy kernel writes them)
+    ("d256_pages128_fresh", [(150, 150), (300, 300), (70, 70), (1, 90)], 8, 1, 256, 128, 0, 0, True),
+    ("d256_pages128_on_tiles", [(150, 214), (33, 65), (300, 300), (70, 390), (1, 90)], 8, 1, 256, 128, 0, 0,
+     True),
+    ("d256_pages128_inside_tiles", [(150, 230), (33, 80), (70, 400), (1, 90)], 8, 1, 256, 128, 0, 0, False),
+    ("d256_pages16_window", [(150, 230), (33, 77), (70, 402), (1, 90)], 8, 1, 256, 16, 100, 0, True),
+    ("d256_pages16_inside_runs", [(150, 230), (33, 79), (1, 90)], 8, 1, 256, 16, 100, 0, False),
+    ("d256_pages6", [(150, 230), (33, 80), (70, 400), (1, 90)], 8, 1, 256, 6, 0, 0, True),
+    # d 128 with a decode (64-key tiles, 16 rows per wave) and without (32-key tiles, 8 rows per wave)
+    ("d128_pages48", [(40, 104), (129, 129), (3, 1000), (77, 301)], 16, 4, 128, 48, 0, 0, True),
+    ("d128_pages48_inside_runs", [(40, 100), (129, 129), (3, 1000)], 16, 4, 128, 48, 0, 0, False),
+    ("d128_pages8_prefill_only", [(40, 104), (129, 129), (77, 301), (5, 37)], 16, 4, 128, 8, 0, 0, True),
+    ("d512_pages32", [(45, 333), (16, 16), (1, 50)], 16, 2, 512, 32, 0, 0, True),
+    ("d64_pages16_window", [(100, 180), (9, 201), (64, 64)], 8, 2, 64, 16, 33, 0, True),
+    ("d64_pages16_inside_runs", [(100, 180), (9, 200), (64, 64)], 8, 2, 64, 16, 33, 0, False),
+    # key splits: the first split writes, every split reads the new keys from k_new
+    ("d256_splits", [(700, 2108), (1, 500)], 8, 1, 256, 128, 0, 256, True),
+    ("d256_splits_pages16", [(700, 2100), (1, 500)], 8, 1, 256, 16, 1400, 256, True),
+])
+def test_prefill_kernel_writes_the_new_rows(name, seqs, hq, hkv, d, b, window, split, fused):
+    """With a bf16 cache the prefill kernel reads a chunk's new keys from
+    k_new / v_new and each query tile writes its own tokens' rows, where
+    every chunk's first new key starts one of the kernel's buffer runs (a
+    tile, or a wave's rows of one; any key with a page id per lane): then no
+    append kernel runs (every decode here holds all of its sequence's
+    tokens).  Elsewhere the append kernel writes the prefill rows first.
+    Either way the pools come out byte for byte as the oracle's append
+    leaves them (their new slots start as NaN), the attention matches the
+    oracle, and it gives the same bits as rpa_forward over pages that
+    already hold the rows."""
+    w = wl.custom(seqs, hq, hkv, d, b, window, seed=d + b + window)
+    print(f"prefill append {name}", flush=True)
+
+    def configured():
+        a = make_attn(w)
+        if split:
+            a.set_option(R.RPA_OPT_PREFILL_SPLIT_KEYS, split)
+        return a
+
+    attn = configured()
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
+    inp, (k_new, k_stale, v_new, v_stale), kp, vp, out = run_append(w, attn)
+    info, items = attn.plan(inp.cu_q_lens, inp.kv_lens, window)
+    assert info["num_prefill_items"] > 0
+    if split:
+        assert any(it["kind"] == 0 and it["split_index"] > 0 for it in items)
+    assert (len(attn.kernel_times(R.RPA_KERNEL_APPEND)) == 0) == fused
+    want_k, want_v = ora.append_kv(k_stale, v_stale, inp.page_table, inp.cu_q_lens, inp.kv_lens, k_new, v_new)
+    assert torch.equal(kp.cpu().view(torch.int16), want_k.view(torch.int16)), f"{name}: K pages"
+    assert torch.equal(vp.cpu().view(torch.int16), want_v.view(torch.int16)), f"{name}: V pages"
+    compare(out, oracle_rows(inp), label=name)
+    dev = inp.to("cuda")
+    base = configured().forward(dev.q, dev.k_pages, dev.v_pages, dev.page_table, inp.cu_q_lens, inp.kv_lens,
+                                window, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, base), f"{name}: appending call against rpa_forward on filled pages"
+
+
+def test_long_prefill_launch_keeps_the_copy_kernel():
+    """A fresh prefill of more than two prefill workgroups per slot (a
+    4608-token causal prefill at d = 512: 576 query tiles) has its rows
+    written by the append kernel, which is cheaper there than each
+    workgroup's own write: pools byte for byte, sampled rows against the
+    oracle."""
+    w = wl.global_prefill(tokens=4608)
+    attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
+    info, _ = attn.plan(np.array([0, 4608], np.int32), np.array([4608], np.int32), w.window)
+    assert info["num_prefill_items"] > 2 * 256
+    inp, (k_new, k_stale, v_new, v_stale), kp, vp, out = run_append(w, attn)
+    assert len(attn.kernel_times(R.RPA_KERNEL_APPEND)) == 1
+    want_k, want_v = ora.append_kv(k_stale, v_stale, inp.page_table, inp.cu_q_lens, inp.kv_lens, k_new, v_new)
+    assert torch.equal(kp.cpu().view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(vp.cpu().view(torch.int16), want_v.view(torch.int16))
+    rows = wl.sample_rows(w.total_q, 48, 7, [0, w.total_q - 1])
+    compare(out, oracle_rows(inp, rows), rows=rows, label="long prefill, copy kernel")
 
 
 def test_append_in_a_captured_graph():
