@@ -112,6 +112,7 @@ RPA_DEV u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
 }
 
 RPA_DEV u32x2 load8(const uint8_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+RPA_DEV u32x4 load16b(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 RPA_DEV u32x2 buffer_load8(__amdgpu_buffer_rsrc_t rs, int byte_off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, byte_off, 0, 0));
 }
@@ -1348,6 +1349,12 @@ __global__ void __launch_bounds__(NW * 64, (D >= 512 || (RB == 2 && D >= 256)) ?
 rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   using C = DecodeCfg<D, NW, RB>;
   constexpr int ROWS = C::ROWS;
+  // Column chunks (8 columns) of V and O: MFMA row m of pass u holds chunk
+  // u*16 + m, or with an E4M3 cache of two or more passes (V16) chunk
+  // m*NU + u, so that a lane's chunks are contiguous bytes, loaded 16 at a time.
+  constexpr bool V16 = KV8 && C::NU >= 2;
+  static_assert(!V16 || C::NU * 16 == C::NCH, "every lane holds NU chunks");
+  auto vchunk = [](int u, int m) { return V16 ? m * C::NU + u : u * 16 + m; };
   extern __shared__ __attribute__((aligned(16))) float dsm[];
   float* lds_o = dsm;                     // [NW/2][ROWS][OSTRIDE]
   float* lds_m = dsm + C::LDS_O;          // [NW][ROWS]
@@ -1398,8 +1405,14 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     pos[rb] = it.q_pos0 + tk;
     const int64_t q_off = (static_cast<int64_t>(it.q_start + tk) * hq + g * G + hh) * D;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      qf[rb][kk] = row_ok[rb] ? load16(q + q_off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
+    for (int kk = 0; kk < D / 32; ++kk) {
+      // An E4M3 cache: lane lq reads 16 contiguous key bytes per pair of
+      // 32-column slices (columns 64p + 16lq ..), so the Q columns of slot kk
+      // are those bytes' half kk % 2 (the score sums over the columns, so one
+      // permutation applied to both operands leaves it unchanged).
+      const int dq = KV8 ? (kk >> 1) * 64 + lq * 16 + (kk & 1) * 8 : kk * 32 + lq * 8;
+      qf[rb][kk] = row_ok[rb] ? load16(q + q_off + dq) : u32x4{0, 0, 0, 0};
+    }
   }
 
   f32x4 o[RB][C::NU][8];
@@ -1523,8 +1536,12 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     // keys of this lane: K rows k0 + 16*kb + ln; V rows k0 + 4*lq + j and k0 + 16 + 4*lq + j
     u32x4 kf[2][D / 32];
     u32x4 vf[C::NU][8];
-    [[maybe_unused]] u32x2 kr[2][D / 32];   // KV8: the raw bytes of kf / vf
+    // KV8: the raw bytes of kf (16 per lane and column pair, see qf) and
+    // of vf (with V16, lane ln holds column chunks ln * NU .. ln * NU + NU - 1,
+    // two per 16-byte load; else chunk ln)
+    [[maybe_unused]] u32x4 kr[2][D / 64 > 0 ? D / 64 : 1];
     [[maybe_unused]] u32x2 vr[C::NU][8];
+    [[maybe_unused]] u32x4 vr2[C::NU / 2 > 0 ? C::NU / 2 : 1][8];
     if constexpr (SEG > 0) {
       // Buffer loads against each run's valid key rows [lo, hi); rows outside
       // read as zero (negative offsets wrap above the record count, an empty
@@ -1551,21 +1568,29 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       for (int kb = 0; kb < 2; ++kb) {
         const int sg = (kb * 16) / (SEG > 0 ? SEG : 32);
         const int off = (rel[sg] + kb * 16 - sg * SEG + ln) * row_bytes + lq * 8 * ESZ;
+        if constexpr (KV8) {
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          if constexpr (KV8) kr[kb][kk] = buffer_load8(krs[sg], off + kk * 32);
-          else kf[kb][kk] = buffer_load16(krs[sg], off + kk * 64);
+          for (int p = 0; p < D / 64; ++p) kr[kb][p] = buffer_load16(krs[sg], off + lq * 8 + p * 64);
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < D / 32; ++kk) kf[kb][kk] = buffer_load16(krs[sg], off + kk * 64);
         }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int sg = (j < 4 ? 0 : 16) / (SEG > 0 ? SEG : 32);
         const int key_rel = rel[sg] - sg * SEG + ((j < 4) ? (lq * 4 + j) : (16 + lq * 4 + j - 4));
+        if constexpr (V16) {
 #pragma unroll
-        for (int u = 0; u < C::NU; ++u) {
-          const int c = u * 16 + ln;
-          if constexpr (KV8) vr[u][j] = c < C::NCH ? buffer_load8(vrs[sg], key_rel * row_bytes + c * 8) : u32x2{0, 0};
-          else vf[u][j] = c < C::NCH ? buffer_load16(vrs[sg], key_rel * row_bytes + c * 16) : u32x4{0, 0, 0, 0};
+          for (int u2 = 0; u2 < C::NU / 2; ++u2)
+            vr2[u2][j] = buffer_load16(vrs[sg], key_rel * row_bytes + (ln * C::NU + 2 * u2) * 8);
+        } else {
+#pragma unroll
+          for (int u = 0; u < C::NU; ++u) {
+            const int c = u * 16 + ln;
+            if constexpr (KV8) vr[u][j] = c < C::NCH ? buffer_load8(vrs[sg], key_rel * row_bytes + c * 8) : u32x2{0, 0};
+            else vf[u][j] = c < C::NCH ? buffer_load16(vrs[sg], key_rel * row_bytes + c * 16) : u32x4{0, 0, 0, 0};
+          }
         }
       }
     } else {
@@ -1590,21 +1615,29 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       for (int kb = 0; kb < 2; ++kb) {
         const bool ok = kkey[kb] >= kv_begin && kkey[kb] < kv_end;
         const int64_t off = kv_row(kkey[kb], kpid[kb]);
+        if constexpr (KV8) {
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          if constexpr (KV8) kr[kb][kk] = ok ? load8(kbase + off + kk * 32 + lq * 8) : u32x2{0, 0};
-          else kf[kb][kk] = ok ? load16(kbase + off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
+          for (int p = 0; p < D / 64; ++p) kr[kb][p] = ok ? load16b(kbase + off + p * 64 + lq * 16) : u32x4{0, 0, 0, 0};
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < D / 32; ++kk) kf[kb][kk] = ok ? load16(kbase + off + kk * 32 + lq * 8) : u32x4{0, 0, 0, 0};
         }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const bool ok = vkey[j] >= kv_begin && vkey[j] < kv_end;
         const int64_t off = kv_row(vkey[j], vpid[j]);
+        if constexpr (V16) {
 #pragma unroll
-        for (int u = 0; u < C::NU; ++u) {
-          const int c = u * 16 + ln;
-          if constexpr (KV8) vr[u][j] = (ok && c < C::NCH) ? load8(vbase + off + c * 8) : u32x2{0, 0};
-          else vf[u][j] = (ok && c < C::NCH) ? load16(vbase + off + c * 8) : u32x4{0, 0, 0, 0};
+          for (int u2 = 0; u2 < C::NU / 2; ++u2)
+            vr2[u2][j] = ok ? load16b(vbase + off + (ln * C::NU + 2 * u2) * 8) : u32x4{0, 0, 0, 0};
+        } else {
+#pragma unroll
+          for (int u = 0; u < C::NU; ++u) {
+            const int c = u * 16 + ln;
+            if constexpr (KV8) vr[u][j] = (ok && c < C::NCH) ? load8(vbase + off + c * 8) : u32x2{0, 0};
+            else vf[u][j] = (ok && c < C::NCH) ? load16(vbase + off + c * 8) : u32x4{0, 0, 0, 0};
+          }
         }
       }
     }
@@ -1612,11 +1645,24 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) kf[kb][kk] = e4m3x8_to_bf16x8(kr[kb][kk]);
+        for (int p = 0; p < D / 64; ++p) {
+          kf[kb][2 * p] = e4m3x8_to_bf16x8(u32x2{kr[kb][p][0], kr[kb][p][1]});
+          kf[kb][2 * p + 1] = e4m3x8_to_bf16x8(u32x2{kr[kb][p][2], kr[kb][p][3]});
+        }
+      if constexpr (V16) {
 #pragma unroll
-      for (int u = 0; u < C::NU; ++u)
+        for (int u2 = 0; u2 < C::NU / 2; ++u2)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vf[u][j] = e4m3x8_to_bf16x8(vr[u][j]);
+          for (int j = 0; j < 8; ++j) {
+            vf[2 * u2][j] = e4m3x8_to_bf16x8(u32x2{vr2[u2][j][0], vr2[u2][j][1]});
+            vf[2 * u2 + 1][j] = e4m3x8_to_bf16x8(u32x2{vr2[u2][j][2], vr2[u2][j][3]});
+          }
+      } else {
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vf[u][j] = e4m3x8_to_bf16x8(vr[u][j]);
+      }
     }
     u32x4 pf[RB];
     float alpha[RB];
@@ -1698,9 +1744,9 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[rb][u][e] *= wscale;
   }
-  // lane (lq, ln) holds O[row rb*16 + ln][d = 8*(16u + 4lq + j) + e]; slot rows are padded by 4 floats
+  // lane (lq, ln) holds O[row rb*16 + ln][d = 8*chunk(u, 4lq + j) + e]; slot rows are padded by 4 floats
   auto slot_ptr = [&](int slot, int rb, int u, int j) {
-    return reinterpret_cast<f32x4*>(lds_o + (slot * ROWS + rb * 16 + ln) * C::OSTRIDE + (u * 16 + lq * 4 + j) * 8);
+    return reinterpret_cast<f32x4*>(lds_o + (slot * ROWS + rb * 16 + ln) * C::OSTRIDE + vchunk(u, lq * 4 + j) * 8);
   };
 #pragma unroll
   for (int half = NW / 2; half >= 1; half /= 2) {
@@ -1712,7 +1758,7 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
         for (int u = 0; u < C::NU; ++u)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (u * 16 + lq * 4 + j < C::NCH) {
+            if (vchunk(u, lq * 4 + j) < C::NCH) {
               f32x4* dst = slot_ptr(wave - half, rb, u, j);
               dst[0] = f32x4{o[rb][u][0][j], o[rb][u][1][j], o[rb][u][2][j], o[rb][u][3][j]};
               dst[1] = f32x4{o[rb][u][4][j], o[rb][u][5][j], o[rb][u][6][j], o[rb][u][7][j]};
@@ -1728,7 +1774,7 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
         for (int u = 0; u < C::NU; ++u)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (u * 16 + lq * 4 + j < C::NCH) {
+            if (vchunk(u, lq * 4 + j) < C::NCH) {
               const f32x4* src = slot_ptr(wave, rb, u, j);
               const f32x4 lo = src[0], hi = src[1];
 #pragma unroll
@@ -1754,7 +1800,7 @@ rpa_decode_kernel(RPA_HOT_POINTERS, KernelArgs args) {
       for (int u = 0; u < C::NU; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (u * 16 + lq * 4 + j < C::NCH) {
+          if (vchunk(u, lq * 4 + j) < C::NCH) {
             f32x4* dst = slot_ptr(0, rb, u, j);
             dst[0] = f32x4{o[rb][u][0][j], o[rb][u][1][j], o[rb][u][2][j], o[rb][u][3][j]};
             dst[1] = f32x4{o[rb][u][4][j], o[rb][u][5][j], o[rb][u][6][j], o[rb][u][7][j]};
