@@ -481,8 +481,9 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
   // new_row + key (the same row pitch as a page).  They are read from there:
   // their page slots are written by this launch, by the workgroup of each
   // query tile after its products, and read by none of its workgroups.
-  // (The launcher runs this form only where new0 is a multiple of the
-  // buffer runs, SEG keys, so that no run mixes pool and new rows.)
+  // (An appending call passes its new rows to this launch only where every
+  // item's new0 is a multiple of the buffer runs, SEG keys, so that no run
+  // mixes pool and new rows: prefill_takes_new_rows.)
   [[maybe_unused]] const int new0 = AP ? it.new_pos0 : 0;
   [[maybe_unused]] const int64_t new_row = static_cast<int64_t>(it.q_start) - it.q_pos0;
   // Tile order: step t takes tile (t + rot) mod n_tiles of the range, with rot
@@ -637,8 +638,8 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     } else if constexpr (UNI) {
       // AP, the tile in one page: a tile below new0 reads the pool and one
       // from new0 on reads k_new / v_new, both as above (the same buffer
-      // bounds).  No tile holds keys on both sides of new0: the AP form runs
-      // only where new0 sits on a tile boundary.
+      // bounds).  No tile holds keys on both sides of new0 (new0 sits on a
+      // tile boundary, see above).
       const int64_t trow = next_tile_row();   // page slot row of key k0
       const int rel_b = (lo - k0) * row_bytes;
       const uint32_t nbytes = uniform_u32(static_cast<uint32_t>((hi - lo - 1) * row_bytes + D * 2));
@@ -654,8 +655,7 @@ rpa_prefill_kernel(RPA_HOT_POINTERS, KernelArgs args) {
     } else if constexpr (BUF) {
       // AP, this wave's rows in one page: the run's rows come from the pool,
       // or (from new0 on) from k_new / v_new.  No run holds keys on both
-      // sides of new0: the AP form runs only where new0 sits on a run
-      // boundary.
+      // sides of new0 (new0 sits on a run boundary, see above).
       int64_t base_off;
       uint32_t nbytes;
       int rel_b;
