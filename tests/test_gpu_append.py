@@ -251,19 +251,26 @@ def test_long_prefill_launch_keeps_the_copy_kernel():
     compare(out, oracle_rows(inp, rows), rows=rows, label="long prefill, copy kernel")
 
 
-def test_append_in_a_captured_graph():
+@pytest.mark.parametrize("fresh", [False, True])
+def test_append_in_a_captured_graph(fresh):
     """rpa_forward_append captured into a HIP graph (warm work list) and
-    replayed: each replay writes the same rows and gives the eager bits."""
-    w = mixed_small(1024)
+    replayed: each replay writes the same rows and gives the eager bits --
+    with chunks on prior context (the copy kernel writes their rows) and
+    with fresh prefills (the prefill kernel writes them)."""
+    w = (wl.custom([(300, 300), (150, 150), (70, 70), (33, 33)] + [(1, 64 + 23 * i) for i in range(64)], 8, 1, 256,
+                   128, 1024, seed=207) if fresh else mixed_small(1024))
     inp = wl.make_inputs(w, poison=True)
     k_new, k_stale, v_new, v_stale = stale_pages_and_new_rows(inp)
     d = inp.to("cuda")
     kn, vn = k_new.cuda(), v_new.cuda()
     kp, vp = k_stale.cuda(), v_stale.cuda()
     attn = make_attn(w)
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 4)
     eager = attn.forward_append(d.q, kn, vn, kp, vp, d.page_table, inp.cu_q_lens, inp.kv_lens, w.window,
                                 w.scale).clone()
     torch.cuda.synchronize()
+    assert (len(attn.kernel_times(R.RPA_KERNEL_APPEND)) == 0) == fresh
+    attn.set_option(R.RPA_OPT_KERNEL_TIMING, 0)
     out = torch.empty_like(eager)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
